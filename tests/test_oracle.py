@@ -1,0 +1,299 @@
+"""Pins for the CPU oracle: hand-worked values, closed forms, invariants,
+exhaustive scans and brute force.  None of these re-types the oracle's own
+formula; each would fail on a plausible slip (a dropped term, a wrong sign or
+index, the wrong rounding mode, a transposed operand).
+
+CPU only.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synthetic
+from golden_io import read_fixture
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+# ---------------------------------------------------------------- rounding
+
+def test_fp16_rounding_is_single_step_half_even():
+    # 1 + 2^-11 + 2^-40 is just above the tie between FP16 1.0 and 1.0009765625.
+    # A detour through FP32 would drop 2^-40, land on the tie and round to 1.0.
+    v = np.float64(1.0) + np.float64(2.0) ** -11 + np.float64(2.0) ** -40
+    assert float(O.fp16_rne(v)) == 1.0009765625
+    # exact ties go to the even significand
+    assert float(O.fp16_rne(np.float64(1.0) + 2.0 ** -11)) == 1.0
+    assert float(O.fp16_rne(np.float64(1.0) + 3 * 2.0 ** -11)) == 1.001953125
+
+
+def test_rne_div_matches_exact_fractions():
+    from fractions import Fraction
+    a = np.arange(-300, 301)
+    for s in range(1, 18):
+        got = O.rne_div(a, s)
+        for ai, gi in zip(a.tolist(), got.tolist()):
+            f = Fraction(ai, s)
+            fl = f.numerator // f.denominator
+            rem = f - fl
+            if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+                fl += 1
+            assert gi == fl, (ai, s, gi, fl)
+
+
+# ------------------------------------------------------ activation quantizer
+
+def test_act_quant_hand_worked_rows():
+    fx = read_fixture("act_quant_rows.txt")
+    X = np.array([fx[f"x{i}"] for i in range(5)], dtype=np.float16)
+    x8, s = O.quant_act_per_token(X)
+    for i in range(5):
+        assert float(s[i]) == fx[f"s{i}"][0], i
+        assert x8[i].tolist() == [int(v) for v in fx[f"q{i}"]], i
+    assert int(s.view(np.uint16)[2]) == 0x260C
+
+
+def test_act_quant_invariants_on_workload_rows():
+    X = synthetic.make_x(64, 4096, "frac", seed=3)
+    x8, s = O.quant_act_per_token(X)
+    assert x8.dtype == np.int8 and s.dtype == np.float16
+    assert np.abs(x8.astype(np.int32)).max() <= 127
+    # each token reaches +-127 at its largest-magnitude entry (normal-range scale)
+    am = np.argmax(np.abs(X.astype(np.float32)), axis=1)
+    hit = x8[np.arange(64), am].astype(np.int32)
+    assert np.all(np.abs(hit) == 127)
+    assert np.all(np.sign(hit) == np.sign(X[np.arange(64), am].astype(np.float32)))
+    # every code is within half a step of x/s (no clamping away from the max)
+    err = np.abs(x8.astype(np.float64) * s.astype(np.float64)[:, None] - X.astype(np.float64))
+    assert np.all(err <= 0.5 * s.astype(np.float64)[:, None] * (1 + 2.0 ** -20))
+
+
+def test_act_quant_is_row_local_and_sign_symmetric():
+    X = synthetic.make_x(8, 512, "fixed", seed=1)
+    x8, s = O.quant_act_per_token(X)
+    x8n, sn = O.quant_act_per_token(-X)
+    assert np.array_equal(s, sn) and np.array_equal(x8n.astype(int), -x8.astype(int))
+    x8p, sp = O.quant_act_per_token(X[::-1])
+    assert np.array_equal(x8p, x8[::-1]) and np.array_equal(sp, s[::-1])
+
+
+# ------------------------------------------------------ weight level 0
+
+def test_level0_hand_worked_row():
+    fx = read_fixture("weight_level0_row.txt")
+    W = np.array([fx["w"]], dtype=np.float16)
+    q8, s0 = O.quant_weight_level0(W)
+    assert float(s0[0]) == fx["s0"][0]
+    assert q8[0].tolist() == [int(v) for v in fx["q8"]]
+
+
+def test_level0_invariants_and_error_bound():
+    W = synthetic.make_w(256, 1024, seed=5)
+    q8, s0 = O.quant_weight_level0(W)
+    assert np.abs(q8.astype(int)).max() <= 119
+    am = np.argmax(np.abs(W.astype(np.float32)), axis=1)
+    assert np.all(np.abs(q8[np.arange(256), am].astype(int)) == 119)
+    err = np.abs(q8.astype(np.float64) * s0.astype(np.float64)[:, None] - W.astype(np.float64))
+    assert np.all(err <= 0.5 * s0.astype(np.float64)[:, None])
+
+
+def test_level0_zero_row_and_nonfinite():
+    W = np.zeros((2, 128), np.float16)
+    W[1, 5] = 1.0
+    q8, s0 = O.quant_weight_level0(W)
+    assert float(s0[0]) == 0 and not q8[0].any()
+    assert q8[1, 5] == 119
+    W[0, 0] = np.inf
+    with pytest.raises(ValueError):
+        O.quant_weight_level0(W)
+
+
+# ------------------------------------------------------ weight level 1
+
+def test_level1_hand_worked_groups():
+    fx = read_fixture("level1_groups.txt")
+    for g in "ABCDEFG":
+        vals = [int(v) for v in fx[f"{g}.q8"]]
+        row = np.array(vals + [vals[0]] * (128 - len(vals)), dtype=np.int8)[None, :]
+        q4, s1, z = O.quant_weight_level1(row, 128)
+        w8 = O.dequant_level1(q4, s1, z, 128)
+        assert int(s1[0, 0]) == int(fx[f"{g}.s1"][0]), g
+        assert int(z[0, 0]) == int(fx[f"{g}.z"][0]), g
+        n = len(vals)
+        assert q4[0, :n].tolist() == [int(v) for v in fx[f"{g}.q4"]], g
+        assert w8[0, :n].tolist() == [int(v) for v in fx[f"{g}.w8"]], g
+
+
+def _scan_level1(R):
+    """Every (lo, hi, q8) with -R <= lo <= q8 <= hi <= R through the level-1 code."""
+    worst = 0
+    viol = 0
+    max_s1 = 0
+    max_zs = 0
+    max_prod = 0
+    for lo in range(-R, R + 1):
+        hi = np.arange(lo, R + 1)[:, None]
+        q8 = np.arange(-R, R + 1)[None, :]
+        mask = (q8 >= lo) & (q8 <= hi)
+        s1, z = O.group_scale_zero(np.full(hi.shape, lo), hi)
+        q4 = O.group_codes(q8, s1, z)
+        w8 = (q4 - z) * s1
+        w8 = np.where(mask, w8, 0)
+        worst = max(worst, int(np.abs(w8).max()))
+        viol += int(((w8 > 127) | (w8 < -128)).sum())
+        max_s1 = max(max_s1, int(s1.max()))
+        max_zs = max(max_zs, int((z * s1).max()))
+        max_prod = max(max_prod, int(np.where(mask, q4 * s1, 0).max()))
+        assert s1.min() >= 1 and z.min() >= 0 and z.max() <= 15
+        assert q4.min() >= 0 and q4.max() <= 15
+    return worst, viol, max_s1, max_zs, max_prod
+
+
+def test_protective_range_119_is_safe_exhaustively():
+    # The pages: shrinking the level-0 range to [-119, 119] keeps the level-1
+    # dequantized intermediates inside INT8 (no saturation needed).
+    worst, viol, max_s1, max_zs, max_prod = _scan_level1(119)
+    assert viol == 0
+    assert worst <= 127
+    assert max_s1 == 16          # an 8-bit group scale is needed, 4 bits cannot hold 16
+    # properties the packed-byte dequantization relies on:
+    assert max_zs <= 127         # z*s1 fits a byte with room for a +128 bias
+    assert max_prod <= 255       # q4*s1 never carries out of its byte
+
+
+@pytest.mark.parametrize("R", [120, 127])
+def test_wider_level0_range_overflows_int8(R):
+    worst, viol, *_ = _scan_level1(R)
+    assert viol > 0 and worst > 127
+
+
+def test_level1_error_bound_and_roundtrip_on_workload_rows():
+    W = synthetic.make_w(64, 2048, seed=7)
+    enc = O.encode_weight_g128(W)
+    q8, q4, s1, z, w8 = (enc[k].astype(np.int64) for k in ("q8", "q4", "s1", "z", "w8"))
+    s1e = np.repeat(s1, 128, axis=1)
+    ze = np.repeat(z, 128, axis=1)
+    assert np.abs(w8).max() <= 127
+    unclamped = (q4 > 0) & (q4 < 15)
+    assert np.all(np.abs(w8 - q8)[unclamped] * 2 <= s1e[unclamped])
+    # UINT4 -> INT8 in byte lanes mod 256 equals the wide-integer w8
+    byte = ((q4 * s1e - ze * s1e) % 256).astype(np.uint8).view(np.int8)
+    assert np.array_equal(byte.astype(np.int64), w8)
+
+
+# ------------------------------------------------------ per-channel W4
+
+def test_per_channel_hand_worked_row():
+    fx = read_fixture("per_channel_row.txt")
+    W = np.array([fx["w"]], dtype=np.float16)
+    q4, s_w, z = O.quant_weight_per_channel(W)
+    assert float(s_w[0]) == fx["s_w"][0] and int(s_w.view(np.uint16)[0]) == 0x3266
+    assert int(z[0]) == int(fx["z"][0])
+    assert q4[0].tolist() == [int(v) for v in fx["q4"]]
+
+
+def test_per_channel_invariants():
+    W = synthetic.make_w(128, 1024, seed=9)
+    enc = O.encode_weight_per_channel(W)
+    w8 = enc["w8"]
+    assert np.abs(w8).max() <= 15
+    q4 = enc["q4"].astype(np.int64)
+    err = np.abs((q4 - enc["z"].astype(np.int64)[:, None]) * enc["s_w"].astype(np.float64)[:, None]
+                 - W.astype(np.float64))
+    inner = (q4 > 0) & (q4 < 15)
+    assert np.all(err[inner] <= 0.5 * np.broadcast_to(enc["s_w"].astype(np.float64)[:, None], err.shape)[inner] * (1 + 2.0 ** -20))
+    # acc through (q4 - z) equals sum x8*q4 - z * sum x8 (zero applied after the contraction)
+    X = synthetic.make_x(8, 1024, "frac", seed=2)
+    x8, sx = O.quant_act_per_token(X)
+    acc = O.gemm_exact(x8, w8)
+    alt = O.gemm_int64(x8, q4) - x8.astype(np.int64).sum(1)[:, None] * enc["z"].astype(np.int64)[None, :]
+    assert np.array_equal(acc, alt)
+
+
+# ------------------------------------------------------ GEMM and epilogue
+
+def test_gemm_matches_python_int_bruteforce():
+    rng = np.random.default_rng(11)
+    x8 = rng.integers(-127, 128, size=(5, 256), dtype=np.int64).astype(np.int8)
+    w8 = rng.integers(-121, 122, size=(7, 256), dtype=np.int64)
+    assert np.array_equal(O.gemm_exact(x8, w8), O.gemm_bruteforce(x8, w8))
+    # extreme magnitudes
+    x8 = np.full((2, 384), 127, np.int8); x8[1] = -127
+    w8 = np.full((3, 384), 121); w8[1] = -121; w8[2, ::2] = -121
+    assert np.array_equal(O.gemm_exact(x8, w8), O.gemm_bruteforce(x8, w8))
+
+
+def test_gemm_tiny_workload_bruteforce():
+    X, W = synthetic.make_inputs("tiny")
+    enc = O.encode_weight_g128(W)
+    x8, _ = O.quant_act_per_token(X)
+    assert np.array_equal(O.gemm_exact(x8[:4], enc["w8"][:9]), O.gemm_bruteforce(x8[:4], enc["w8"][:9]))
+
+
+def test_gemm_fp64_form_equals_int64_at_attention_size():
+    rng = np.random.default_rng(12)
+    x8 = rng.integers(-127, 128, size=(256, 4096)).astype(np.int8)
+    w8 = rng.integers(-121, 122, size=(128, 4096))
+    assert np.array_equal(O.gemm_exact(x8, w8), O.gemm_int64(x8, w8))
+
+
+def test_gemm_orientation_and_linearity():
+    # acc[m, n] contracts row m of x8 with row n of w8 (not a transposed operand)
+    x8 = np.zeros((3, 128), np.int8)
+    w8 = np.zeros((4, 128), np.int64)
+    x8[1, 7] = 127
+    w8[2, 7] = -5
+    acc = O.gemm_exact(x8, w8)
+    assert acc[1, 2] == -635 and np.count_nonzero(acc) == 1
+    rng = np.random.default_rng(13)
+    a = rng.integers(-60, 61, size=(4, 256)).astype(np.int8)
+    b = rng.integers(-60, 61, size=(4, 256)).astype(np.int8)
+    w = rng.integers(-121, 122, size=(6, 256))
+    assert np.array_equal(O.gemm_exact((a.astype(int) + b).astype(np.int8), w),
+                          O.gemm_exact(a, w) + O.gemm_exact(b, w))
+    perm = np.concatenate([np.arange(128, 256), np.arange(0, 128)])
+    assert np.array_equal(O.gemm_exact(a[:, perm], w[:, perm]), O.gemm_exact(a, w))
+
+
+def test_epilogue_hand_worked_cases():
+    fx = read_fixture("epilogue_cases.txt")
+    for i in range(len(fx["acc"])):
+        acc = np.array([[int(fx["acc"][i])]], dtype=np.int64)
+        y = O.epilogue(acc, np.array([fx["s_x"][i]], np.float16), np.array([fx["s_w"][i]], np.float16))
+        assert float(y[0, 0]) == fx["y"][i], i
+
+
+def test_epilogue_equals_dequantize_then_matmul():
+    X, W = synthetic.make_inputs("tiny")
+    enc = O.encode_weight_g128(W)
+    x8, s_x, acc, y = O.w4a8_forward(X, enc)
+    ystar = O.dequant_matmul_fp64(x8, s_x, enc["w8"], enc["s0"])
+    exact = acc.astype(np.float64) * s_x.astype(np.float64)[:, None] * enc["s0"].astype(np.float64)[None, :]
+    assert np.array_equal(ystar, exact)
+    assert np.array_equal(y, ystar.astype(np.float16))
+    # and the per-channel variant
+    encp = O.encode_weight_per_channel(W)
+    _, _, accp, yp = O.w4a8_forward(X, encp)
+    assert np.array_equal(yp, O.dequant_matmul_fp64(x8, s_x, encp["w8"], encp["s_w"]).astype(np.float16))
+
+
+def test_quantized_gemm_tracks_fp_gemm_loosely():
+    # Information-level sanity of the whole encoding (the pages give no error
+    # bound for one GEMM; this only rules out gross slips such as a lost zero
+    # point or a wrong scale).
+    X, W = synthetic.make_inputs("tiny")
+    ref = X.astype(np.float64) @ W.astype(np.float64).T
+    for enc in (O.encode_weight_g128(W), O.encode_weight_per_channel(W)):
+        _, _, _, y = O.w4a8_forward(X, enc)
+        rel = np.linalg.norm(y.astype(np.float64) - ref) / np.linalg.norm(ref)
+        assert rel < 0.2, rel
+
+
+def test_synthetic_prefix_and_determinism():
+    a = synthetic.make_x(64, 512, "frac", 0)
+    b = synthetic.make_x(16, 512, "frac", 0)
+    assert np.array_equal(a[:16], b)
+    assert np.array_equal(synthetic.make_w(32, 256), synthetic.make_w(32, 256))
+    cols = synthetic.outlier_channels(8192, "frac")
+    assert cols.size == 41 and np.unique(cols).size == 41
