@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Benchmark of the QoQ W4A8 GEMM path on one MI355X.
+
+A step is one pass of the online hot path over one batch of synthetic input
+already resident in HBM: per-token INT8 activation quantization followed by the
+W4A8 GEMM with its fused FP16 epilogue.  The offline weight encode/pack is not
+part of a step (it runs once per weight, on the host).
+
+Default workload: the Llama-2-7B attention-projection shape (M=256 tokens,
+K=4096, N=4096, g128).  Prints ONE JSON line with the headline numbers, the
+roofline of the GEMM kernel, the CPU oracle baseline and a sweep over the
+other workload shapes (kernel-level TOPS / GB/s / roofline fraction).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-sweep]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A8 GEMM TOPS and HBM GB/s on 1 MI355X; % of INT8-MFMA / HBM roofline"
+PEAK_INT8_TOPS = 5000.0   # MI355X dense INT8 MFMA peak, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
+MALL_BYTES = 256 * 2 ** 20
+SWEEP = ["tiny", "attn_proj", "attn_qkv", "ffn_gateup_prefill", "ffn_down_prefill", "decode_m1", "decode_m16",
+         "decode_m64", "ffn_large_g128", "ffn_large_perchannel"]
+
+
+def algo_bytes(w) -> int:
+    """Bytes the method must move per GEMM: W4 codes, group metadata (8-bit
+    scale + 4-bit zero per group of 128) or per-channel zero (4 bits), FP16
+    channel scale, INT8 activations, FP16 token scales, FP16 output."""
+    wq = w.N * w.K // 2
+    meta = (w.N * (w.K // 128) * 3) // 2 if w.group_size else w.N // 2
+    return wq + meta + 2 * w.N + w.M * w.K + 2 * w.M + 2 * w.M * w.N
+
+
+def act_bytes(w) -> int:
+    return 2 * w.M * w.K + w.M * w.K + 2 * w.M
+
+
+def bound_of(w) -> str:
+    t_hbm = algo_bytes(w) / (PEAK_HBM_GBS * 1e9)
+    t_mfma = w.ops / (PEAK_INT8_TOPS * 1e12)
+    return "mfma" if t_mfma >= t_hbm else "hbm"
+
+
+def src_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "act_quant.hip"):
+        with open(os.path.join(ROOT, "w4a8_quantized_gemm_qoq_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def busy(torch, ms: float):
+    """Keep the stream busy so launches queued behind it run back to back."""
+    try:
+        torch.cuda._sleep(int(ms * 1e-3 * 2.4e9))
+    except Exception:
+        pass
+
+
+def time_kernel(torch, launch, reps: int, sleep_ms: float = 20.0) -> float:
+    """Average duration (us) of one launch, from HIP events recorded on the
+    launch stream immediately before and after each launch; the launches are
+    queued behind a busy kernel so that host submission gaps do not count."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    busy(torch, sleep_ms)
+    for i in range(reps):
+        evs[i][0].record()
+        launch(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return 1e3 * sum(a.elapsed_time(b) for a, b in evs) / reps
+
+
+def cpu_baseline(w, X, W, seconds: float):
+    """The CPU oracle's online part (per-token quantization, exact GEMM, FP64
+    epilogue) on the same workload, repeated for about `seconds`."""
+    import numpy as np  # noqa: F401
+    import oracle as O
+    enc = O.encode_weight_g128(W) if w.group_size else O.encode_weight_per_channel(W)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        O.w4a8_forward(X, enc)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or (reps >= 1 and el * (reps + 1) / reps > 3 * seconds):
+            break
+    return {"value": w.ops * reps / el / 1e12, "unit": "TOPS", "cores": int(cores), "kind": "oracle",
+            "sample": f"full {w.name} workload (M{w.M} K{w.K} N{w.N}), {reps} repetitions in {el:.1f} s",
+            "seconds_per_step": el / reps}
+
+
+def measure_gemm(torch, q, w, X, W, reps: int):
+    """Kernel-level timing of the act quantizer and the GEMM for one workload."""
+    import numpy as np
+    dev = torch.device("cuda")
+    packed_host = q.qoq_pack_weights(W, w.group_size)
+    wbytes = packed_host.qweight.nbytes + packed_host.meta.nbytes
+    copies = 1 if bound_of(w) == "mfma" and w.M >= 1024 else max(1, math.ceil(3 * MALL_BYTES / max(wbytes, 1)))
+    copies = min(copies, 16)
+    ws = [packed_host.to(dev) for _ in range(copies)]
+    x = torch.from_numpy(np.ascontiguousarray(X)).to(dev)
+    x8 = torch.empty((w.M, w.K), dtype=torch.int8, device=dev)
+    sx = torch.empty((w.M,), dtype=torch.float16, device=dev)
+    y = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+    q.qoq_quant_act_per_token(x, x8, sx)
+    for p in ws:
+        q.qoq_w4a8_gemm(x8, sx, p, y=y)
+    torch.cuda.synchronize()
+    t_q = time_kernel(torch, lambda i: q.qoq_quant_act_per_token(x, x8, sx), reps)
+    t_g = time_kernel(torch, lambda i: q.qoq_w4a8_gemm(x8, sx, ws[i % copies], y=y), reps)
+    b = algo_bytes(w)
+    bnd = bound_of(w)
+    tops = w.ops / t_g / 1e6
+    gbs = b / t_g / 1e3
+    frac = tops / PEAK_INT8_TOPS if bnd == "mfma" else gbs / PEAK_HBM_GBS
+    del ws
+    return {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "group_size": w.group_size,
+            "gemm_us": round(t_g, 3), "tops": round(tops, 2), "gbs": round(gbs, 1), "bound": bnd,
+            "frac": round(frac, 4), "weight_copies": copies, "act_quant_us": round(t_q, 3),
+            "act_quant_gbs": round(act_bytes(w) / t_q / 1e3, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="attn_proj")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--sweep", default=",".join(SWEEP), help="comma-separated workload names")
+    ap.add_argument("--sweep-reps", type=int, default=20)
+    ap.add_argument("--kernel-reps", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the W4A8 GEMM is measured on one MI355X.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synthetic
+    import w4a8_quantized_gemm_qoq_amd as q
+
+    q.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda")
+    w = synthetic.get_workload(args.workload)
+    X, W = synthetic.make_inputs(w)
+
+    # resident inputs and outputs
+    t_pack0 = time.perf_counter()
+    packed = q.qoq_pack_weights(W, w.group_size)
+    t_pack = time.perf_counter() - t_pack0
+    p = packed.to(dev)
+    x = torch.from_numpy(X).to(dev)
+    x8 = torch.empty((w.M, w.K), dtype=torch.int8, device=dev)
+    sx = torch.empty((w.M,), dtype=torch.float16, device=dev)
+    y = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+
+    def step():
+        q.qoq_quant_act_per_token(x, x8, sx)
+        q.qoq_w4a8_gemm(x8, sx, p, y=y)
+
+    # eager warmup, then capture the K timed steps in one HIP graph so that
+    # host launch overhead does not enter the measurement
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    with torch.cuda.graph(g):
+        for _ in range(args.steps):
+            step()
+    g.replay()  # warm replay (untimed)
+    torch.cuda.synchronize()
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_s = t1 - t0
+    gpu_ms = e0.elapsed_time(e1)
+    ms_per_step = 1e3 * wall_s / args.steps
+
+    # correctness of the timed output against a direct launch (same kernels)
+    y_graph = y.clone()
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(y_graph.view(torch.int16), y.view(torch.int16)), "graph replay output differs"
+
+    # dominant kernel: the GEMM; average launch duration from HIP events
+    gemm_us = time_kernel(torch, lambda i: q.qoq_w4a8_gemm(x8, sx, p, y=y), args.kernel_reps)
+    quant_us = time_kernel(torch, lambda i: q.qoq_quant_act_per_token(x, x8, sx), args.kernel_reps)
+    bnd = bound_of(w)
+    if bnd == "mfma":
+        achieved, peak, unit = w.ops / gemm_us / 1e6, PEAK_INT8_TOPS, "TFLOP/s"
+        per_unit = "2*M*N*K int8 ops per launch"
+    else:
+        achieved, peak, unit = algo_bytes(w) / gemm_us / 1e3, PEAK_HBM_GBS, "GB/s"
+        per_unit = "algorithmic bytes per launch"
+
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    if os.path.exists(tf):
+        try:
+            rec = json.load(open(tf))
+            if rec.get("src_hash") == src_hash():
+                traffic = rec.get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    out = {
+        "metric": METRIC,
+        "value": round(w.ops * args.steps / wall_s / 1e12, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "desc": w.desc, "M": w.M, "K": w.K, "N": w.N,
+                   "group_size": w.group_size, "step": "per-token INT8 quant + W4A8 GEMM (FP16 out)",
+                   "timing": "K steps captured in one HIP graph, replayed once between synchronizations"},
+        "gpu_ms_per_step": round(gpu_ms / args.steps, 5),
+        "roofline": {"bound": bnd, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel": "gemm (qoq_w4a8_gemm)", "kernel_us": round(gemm_us, 3), "per_unit": per_unit,
+                     "algorithmic_bytes": algo_bytes(w), "ops": w.ops},
+        "act_quant_us": round(quant_us, 3),
+        "gemm_gbs_algorithmic": round(algo_bytes(w) / gemm_us / 1e3, 1),
+        "host_pack_s": round(t_pack, 3),
+        "src_hash": src_hash(),
+    }
+
+    if not args.no_sweep:
+        sweep = []
+        for name in [n for n in args.sweep.split(",") if n]:
+            sw = synthetic.get_workload(name)
+            SX, SW = synthetic.make_inputs(sw)
+            try:
+                r = measure_gemm(torch, q, sw, SX, SW, args.sweep_reps)
+            except Exception as ex:  # report, do not hide
+                r = {"workload": name, "error": repr(ex)}
+            print(f"[sweep] {json.dumps(r)}", file=sys.stderr, flush=True)
+            sweep.append(r)
+            del SX, SW
+            torch.cuda.empty_cache()
+        out["sweep"] = sweep
+
+    if args.copy_calib_mb:
+        n = args.copy_calib_mb * 2 ** 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        out["copy_calib_bytes"] = n
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, X, W, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,200 @@
+/*
+ * qoq.h -- C ABI of the MI355X (gfx950) QoQ W4A8 GEMM library (libqoq.so).
+ *
+ * The library implements the W4A8 GEMM of QoQ progressive group quantization:
+ * 4-bit weights, per-token 8-bit activations, INT8 matrix-core arithmetic with
+ * INT32 accumulation and an FP16 output.  Sources, cited by tag below:
+ *
+ *   [PL]  "QServe: W4A8KV4 Quantization and System Co-design for Efficient LLM
+ *         Serving", section summary page at paperlayer.ai abs/2405.04532v3;
+ *         cited as [PL §n, bullet topic].
+ *   [SS]  study.space summary page of the same paper.
+ *
+ * Notation: X[M,K] FP16 activations (tokens x input channels), W[N,K] FP16
+ * weights (output x input channels), Y[M,N] = X W^T.  All matrices are
+ * row-major.  FP16 values travel as uint16_t bit patterns (IEEE binary16).
+ *
+ * Conventions for every entry point:
+ *   - The return value is a qoq_status.  On failure qoq_last_error() gives a
+ *     thread-local description; nothing has been written to outputs unless
+ *     stated otherwise.
+ *   - No function allocates device memory or keeps state between calls apart
+ *     from that thread-local error text.  The caller owns every buffer.
+ *   - Host functions (pack / unpack / layout) run synchronously on the calling
+ *     thread and touch host memory only.
+ *   - Device functions take device pointers and a `stream` (a hipStream_t, or
+ *     NULL for the null stream), enqueue their kernels on it and return without
+ *     synchronizing.  Launch failures are reported as QOQ_ERR_HIP; faults inside
+ *     a kernel surface at the caller's next synchronization.
+ *   - K must be a positive multiple of 128 (one 128-wide group is the unit of
+ *     the K loop, also for the per-channel variant), M >= 1, N >= 1, and
+ *     127*127*K < 2^31 so the INT32 accumulator cannot overflow.
+ */
+#ifndef QOQ_H_
+#define QOQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(QOQ_BUILD)
+#define QOQ_API __attribute__((visibility("default")))
+#else
+#define QOQ_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qoq_status {
+  QOQ_OK = 0,
+  QOQ_ERR_INVALID_ARG = 1,       /* null pointer, bad value, codes that break the INT8 bound */
+  QOQ_ERR_UNSUPPORTED_SHAPE = 2, /* K not a multiple of 128, sizes out of range */
+  QOQ_ERR_ALIGNMENT = 3,         /* a device pointer or leading dimension is misaligned */
+  QOQ_ERR_HIP = 4,               /* the HIP runtime reported an error */
+  QOQ_ERR_INTERNAL = 5
+} qoq_status;
+
+/* Version of the packed weight layout described below. */
+#define QOQ_LAYOUT_ID 1
+/* Group size of the g128 progressive variant ([PL §6, experimental setup]). */
+#define QOQ_GROUP 128
+
+/* Static description of a status code; never NULL. */
+QOQ_API const char* qoq_status_string(int status);
+/* Detail text of the last failure on this thread ("" if none); valid until the
+ * thread's next library call. */
+QOQ_API const char* qoq_last_error(void);
+
+/*
+ * Packed weight layout (QOQ_LAYOUT_ID 1).  The GEMM reads weights in the order
+ * it computes with them ([PL §5, W4A8 GEMM optimization]: compute-aware weight
+ * reordering stores weights in computation order so that each thread issues
+ * 128-bit loads without runtime reordering).  Here the order follows the INT8
+ * matrix-core operand fragments of gfx950.
+ *
+ *   N_pad   = N rounded up to a multiple of 16; padded channels are all-zero.
+ *   G       = K / 128 groups along K.  G4 = G rounded up to a multiple of 4.
+ *
+ *   qweight (N_pad*K/2 bytes): 16-channel strips, each strip a run of G
+ *     1024-byte group blocks, each block 64 slots of 16 bytes:
+ *       offset = ((strip*G + g)*64 + slot)*16,  slot = c + 16*j  (c = channel
+ *       in strip 0..15, j = 0..3).  Slot bytes form 4 little-endian dwords
+ *       v[p], p = 0..3.  Byte b of v[p] holds two UINT4 codes: the low nibble
+ *       is input channel k = 128g + 64*(p/2) + 16j + 8*(p%2) + b and the high
+ *       nibble is that k + 4.
+ *   meta, g128 ((N_pad/16)*G4*16 bytes): one byte per (channel, group),
+ *       (s1 - 1) | (z << 4), at offset ((strip*(G4/4) + g/4)*16 + c)*4 + g%4.
+ *     meta, per-channel (N_pad bytes): byte n = z[n] (0..15).
+ *   scale (N_pad FP16): the per-channel FP16 scale -- s0 (g128) or s_w
+ *     (per-channel); 0 for padded channels.
+ *
+ * Code meaning ([PL §4, progressive group quantization]; [PL §5, W4A8 GEMM
+ * optimization: subtraction after multiplication]):
+ *   g128:         w8 = (q4 - z) * s1, s1 in [1,16], q4 and z in [0,15];
+ *                 y  = fp16(sum_k x8*w8 * s_x * s0).
+ *   per-channel:  w8 = q4 - z;  y = fp16(sum_k x8*w8 * s_x * s_w).
+ */
+typedef struct qoq_weight_layout {
+  int32_t layout_id;     /* QOQ_LAYOUT_ID */
+  int32_t group_size;    /* 128 (g128 progressive) or 0 (per-channel W4) */
+  int64_t N, K;          /* logical shape of W */
+  int64_t N_pad;         /* N rounded up to 16 */
+  int64_t n_groups;      /* G = K / 128 */
+  size_t qweight_bytes;  /* N_pad * K / 2 */
+  size_t meta_bytes;     /* see above */
+  size_t scale_bytes;    /* 2 * N_pad */
+} qoq_weight_layout;
+
+/* Sizes of the packed buffers for W[N,K].  group_size is 128 or 0. */
+QOQ_API int qoq_weight_layout_query(int64_t N, int64_t K, int32_t group_size, qoq_weight_layout* out);
+
+/*
+ * Offline weight encode and pack (host).  [PL §4, progressive group
+ * quantization]; [SS] (8-bit per-channel FP16 scales first, then 4 bits).
+ *   group_size 128: level 0, per output channel n:
+ *       s0 = fp16(max_k |W| / 119)  (FP32 divide, round half to even),
+ *       q8 = clamp(round(W / s0), -119, 119)   -- the protective range;
+ *     level 1, per (n, group of 128 along K) with lo/hi = min/max of q8:
+ *       s1 = max(1, round((hi - lo) / 15)), z = clamp(round(-lo / s1), 0, 15),
+ *       q4 = clamp(round(q8 / s1) + z, 0, 15).
+ *   group_size 0 ([PL §6, experimental setup: per-channel counterpart]):
+ *       s_w = fp16((max W - min W) / 15), z = clamp(round(-min W / s_w), 0, 15),
+ *       q4 = clamp(round(W / s_w) + z, 0, 15).
+ *   Rounding is half to even throughout; a zero scale gives all-zero codes.
+ * w_fp16: host [N][K] row-major.  qweight/meta/scale_fp16: caller-owned host
+ * buffers of the sizes qoq_weight_layout_query reports (fully written,
+ * including padding).  Rejects non-finite weights (QOQ_ERR_INVALID_ARG).
+ */
+QOQ_API int qoq_pack_weights(const uint16_t* w_fp16, int64_t N, int64_t K, int32_t group_size,
+                     void* qweight, void* meta, uint16_t* scale_fp16);
+
+/*
+ * Pack already-quantized codes (host): q4 [N][K] (0..15); for g128 s1 and z
+ * are [N][K/128] (s1 1..16, z 0..15); for per-channel s1 is ignored (may be
+ * NULL) and z is [N].  scale_fp16 [N] is copied.  Rejects codes whose
+ * dequantized value (q4 - z)*s1 leaves [-128, 127] or whose z*s1 exceeds 128
+ * (the packed-byte dequantization has no saturation), QOQ_ERR_INVALID_ARG.
+ */
+QOQ_API int qoq_pack_codes(const uint8_t* q4, const uint8_t* s1, const uint8_t* z,
+                   const uint16_t* scale_fp16, int64_t N, int64_t K, int32_t group_size,
+                   void* qweight, void* meta, uint16_t* scale_out);
+
+/* Inverse of the packing (host, for tests and debugging): writes q4 [N][K],
+ * s1 [N][K/128] (g128 only; may be NULL for per-channel), z ([N][K/128] or [N])
+ * and scale_fp16 [N]. */
+QOQ_API int qoq_unpack_weights(const void* qweight, const void* meta, const uint16_t* scale_in,
+                       int64_t N, int64_t K, int32_t group_size,
+                       uint8_t* q4, uint8_t* s1, uint8_t* z, uint16_t* scale_fp16);
+
+/*
+ * Per-token symmetric INT8 activation quantization (device).
+ * [PL §6, experimental setup: per-token INT8 activations]; [PL §5, runtime
+ * and precision mapping: activations enter the W4A8 GEMM as INT8].  Per row m:
+ *   s_x[m] = fp16(max_k |X[m,k]| / 127)  (FP32 IEEE divide, round half even),
+ *   x8[m,k] = clamp(rint(X[m,k] / s_x[m]), -127, 127)  (FP32 IEEE divide);
+ *   a zero scale gives a zero row.  Non-finite X is undefined behaviour.
+ * x_fp16: device [M][ldx] FP16, ldx >= K.  x8: device [M][K] int8 (row stride
+ * K).  sx_fp16: device [M] FP16.  Here K needs only be >= 1; x_fp16 and ldx
+ * need 16-byte / 8-element alignment for the vector path (otherwise a scalar
+ * path runs).
+ */
+QOQ_API int qoq_quant_act_per_token(const void* x_fp16, int64_t M, int64_t K, int64_t ldx,
+                            int8_t* x8, void* sx_fp16, void* stream);
+
+/* Device workspace (bytes) qoq_w4a8_gemm / qoq_w4a8_gemm_i32 need for this
+ * shape; 0 means the workspace arguments may be NULL / 0. */
+QOQ_API size_t qoq_w4a8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_size);
+
+/*
+ * W4A8 GEMM with fused epilogue (device).  [PL §5, runtime and precision
+ * mapping: INT8 matrix-core GEMM with FP16 output]; [PL §3/§4: weights are
+ * dequantized UINT4 -> INT8 inside the main loop, one INT32 accumulator spans
+ * all of K]; [PL §5, W4A8 GEMM optimization: per-channel scale fused into the
+ * epilogue].
+ *   y[m,n] = fp16(float(acc[m,n]) * s_x[m] * scale[n]),
+ *   acc[m,n] = sum_k x8[m,k] * w8[n,k]  (exact INT32).
+ * x8: device [M][K] int8, 16-byte aligned.  sx_fp16: device [M].  qweight,
+ * meta, scale_fp16: device copies of the packed buffers (qweight 16-byte
+ * aligned).  y_fp16: device [M][ldy] FP16, ldy >= N.  The FP16 result is
+ * within one FP16 ulp of the correctly rounded exact product.
+ */
+QOQ_API int qoq_w4a8_gemm(const int8_t* x8, const void* sx_fp16, const void* qweight, const void* meta,
+                  const void* scale_fp16, void* y_fp16, int64_t M, int64_t N, int64_t K,
+                  int64_t ldy, int32_t group_size, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/*
+ * Debug entry: the same main loop with an INT32 epilogue (device).  Writes the
+ * exact accumulators acc[m][n] (row stride ldacc >= N) instead of y; no scales
+ * are read.  Exists so that the integer contraction can be compared bit for bit.
+ */
+QOQ_API int qoq_w4a8_gemm_i32(const int8_t* x8, const void* qweight, const void* meta, int32_t* acc,
+                      int64_t M, int64_t N, int64_t K, int64_t ldacc, int32_t group_size,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QOQ_H_ */

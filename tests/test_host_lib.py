@@ -1,0 +1,258 @@
+"""Host-side checks of libqoq.so that need no GPU: the library loads with
+torch's HIP runtime, exports every entry point of include/qoq.h, and its
+offline packer produces exactly the oracle's codes in the documented layout.
+"""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synthetic
+import w4a8_quantized_gemm_qoq_amd as q
+from w4a8_quantized_gemm_qoq_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_symbols():
+    txt = open(os.path.join(ROOT, "include", "qoq.h")).read()
+    return sorted(set(re.findall(r"QOQ_API\s+[\w\s\*]*?\b(qoq_\w+)\s*\(", txt)))
+
+
+def test_library_exports_every_header_symbol():
+    lib = q.load_library()
+    syms = header_symbols()
+    assert len(syms) == 10, syms
+    assert sorted(_native.EXPORTS) == syms
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_library_shares_torchs_hip_runtime():
+    import torch  # noqa: F401
+    q.load_library()
+    maps = open("/proc/self/maps").read()
+    hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(hip) == 1, hip  # one HIP runtime in the process: torch's
+    assert "torch" in next(iter(hip))
+
+
+def test_status_strings():
+    lib = q.load_library()
+    for s in range(6):
+        assert lib.qoq_status_string(s)
+    assert lib.qoq_status_string(99) == b"unknown status"
+
+
+def test_layout_query_sizes():
+    L = q.qoq_weight_layout_query(28672, 8192, 128)
+    assert L["layout_id"] == 1 and L["N_pad"] == 28672 and L["n_groups"] == 64
+    assert L["qweight_bytes"] == 28672 * 8192 // 2
+    assert L["meta_bytes"] == 28672 * 64          # one byte per (channel, group)
+    assert L["scale_bytes"] == 2 * 28672
+    L = q.qoq_weight_layout_query(100, 256, 128)   # N padded to 112, G = 2 padded to 4
+    assert L["N_pad"] == 112 and L["qweight_bytes"] == 112 * 128 and L["meta_bytes"] == 7 * 4 * 16
+    L = q.qoq_weight_layout_query(24576, 8192, 0)
+    assert L["meta_bytes"] == 24576 and L["group_size"] == 0
+
+
+@pytest.mark.parametrize("N,K,G,args", [
+    (16, 100, 128, "K not multiple of 128"),
+    (16, 0, 128, "K zero"),
+    (0, 128, 128, "N zero"),
+    (16, 128, 64, "group size"),
+    (16, 133248, 128, "K over the INT32 bound"),
+])
+def test_layout_query_rejects(N, K, G, args):
+    with pytest.raises(q.QoQError):
+        q.qoq_weight_layout_query(N, K, G)
+
+
+def _documented_position(n, k):
+    """Byte offset and nibble of code (n, k) per the layout text in qoq.h."""
+    strip, c = divmod(n, 16)
+    g, kl = divmod(k, 128)
+    half, r = divmod(kl, 64)
+    j, t = divmod(r, 16)
+    # low nibble of byte b of dword p: k = 64*(p//2) + 16j + 8*(p%2) + b; high = that + 4
+    sub, b = divmod(t, 4)          # t = 8*(p%2) + 4*high + b
+    p2, high = divmod(sub, 2)
+    p = 2 * half + p2
+    slot = c + 16 * j
+    return ((strip * (K_G[0]) + g) * 64 + slot) * 16 + 4 * p + b, high
+
+
+K_G = [0]
+
+
+def test_packed_layout_matches_documentation():
+    N, K = 40, 384
+    K_G[0] = K // 128
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        n, k = int(rng.integers(N)), int(rng.integers(K))
+        q4 = np.zeros((N, K), np.uint8)
+        q4[n, k] = 9
+        p = q.qoq_pack_codes(q4, np.ones((N, K // 128), np.uint8), np.zeros((N, K // 128), np.uint8),
+                             np.ones(N, np.float16), 128)
+        nz = np.flatnonzero(p.qweight)
+        assert nz.size == 1
+        off, high = _documented_position(n, k)
+        assert nz[0] == off
+        assert p.qweight[off] == (0x90 if high else 0x09)
+
+
+def test_meta_layout_matches_documentation():
+    N, K = 48, 768  # G = 6, G4 = 8
+    G, G4 = 6, 8
+    q4 = np.zeros((N, K), np.uint8)
+    s1 = np.ones((N, G), np.uint8)
+    z = np.zeros((N, G), np.uint8)
+    s1[37, 5] = 11
+    z[37, 5] = 3
+    p = q.qoq_pack_codes(q4, s1, z, np.ones(N, np.float16), 128)
+    strip, c = divmod(37, 16)
+    off = ((strip * (G4 // 4) + 5 // 4) * 16 + c) * 4 + 5 % 4
+    assert np.flatnonzero(p.meta).tolist() == [off]
+    assert p.meta[off] == (11 - 1) | (3 << 4)
+
+
+def _oracle_codes(W, group_size):
+    if group_size:
+        e = O.encode_weight_g128(W)
+        return e["q4"], e["s1"], e["z"], e["s0"]
+    e = O.encode_weight_per_channel(W)
+    return e["q4"], None, e["z"], e["s_w"]
+
+
+def _check_pack_matches_oracle(W, group_size):
+    p = q.qoq_pack_weights(W, group_size)
+    q4, s1, z, sc = q.qoq_unpack_weights(p)
+    oq4, os1, oz, osc = _oracle_codes(W, group_size)
+    assert np.array_equal(q4, oq4)
+    if group_size:
+        assert np.array_equal(s1, os1)
+    assert np.array_equal(z, oz)
+    assert np.array_equal(sc.view(np.uint16), osc.view(np.uint16))
+    # padding channels are zero codes with zero scale
+    L = q.qoq_weight_layout_query(W.shape[0], W.shape[1], group_size)
+    assert np.all(np.asarray(p.scale)[W.shape[0]:L["N_pad"]] == 0)
+    return p
+
+
+@pytest.mark.parametrize("group_size", [128, 0])
+@pytest.mark.parametrize("name", ["tiny"])
+def test_pack_weights_matches_oracle_tiny(name, group_size):
+    _, W = synthetic.make_inputs(name)
+    _check_pack_matches_oracle(W, group_size)
+
+
+@pytest.mark.parametrize("group_size", [128, 0])
+def test_pack_weights_matches_oracle_ragged(group_size):
+    W = synthetic.make_w(77, 1152, seed=4)   # N not a multiple of 16, G = 9
+    _check_pack_matches_oracle(W, group_size)
+
+
+@pytest.mark.parametrize("group_size", [128, 0])
+def test_pack_weights_matches_oracle_attention_shape(group_size):
+    W = synthetic.make_w(4096, 4096, seed=0)
+    _check_pack_matches_oracle(W, group_size)
+
+
+@pytest.mark.parametrize("group_size", [128, 0])
+def test_pack_weights_edge_rows(group_size):
+    K = 256
+    rows = [
+        np.zeros(K),                                   # zero row
+        np.full(K, 3.0),                               # constant row
+        np.r_[np.full(K - 1, 1e-7), 6e-8],             # FP16 subnormals
+        np.r_[65504.0, -65504.0, np.zeros(K - 2)],     # FP16 extremes
+        np.r_[np.full(K // 2, 0.25), np.full(K // 2, -7.0)],  # groups of one sign each
+        np.linspace(-1, 1, K),
+        np.r_[1.0, np.zeros(K - 1)],                   # single spike
+        np.r_[-0.0, np.full(K - 1, -2.5)],
+    ]
+    W = np.array(rows, dtype=np.float16)
+    _check_pack_matches_oracle(W, group_size)
+
+
+def test_pack_weights_rejects_nonfinite():
+    W = synthetic.make_w(16, 128)
+    W[3, 7] = np.float16(np.inf)
+    with pytest.raises(q.QoQError):
+        q.qoq_pack_weights(W, 128)
+    W[3, 7] = np.float16(np.nan)
+    with pytest.raises(q.QoQError):
+        q.qoq_pack_weights(W, 0)
+
+
+def test_pack_codes_roundtrip_and_validation():
+    rng = np.random.default_rng(1)
+    N, K = 35, 512
+    G = K // 128
+    s1 = rng.integers(1, 17, size=(N, G)).astype(np.uint8)
+    z = np.minimum(rng.integers(0, 16, size=(N, G)), 128 // s1).astype(np.uint8)
+    z = np.minimum(z, 15).astype(np.uint8)
+    # choose codes inside the INT8 bound for each group
+    q4 = np.zeros((N, K), np.uint8)
+    for n in range(N):
+        for g in range(G):
+            hi = min(15, int(z[n, g]) + 127 // int(s1[n, g]))
+            q4[n, g * 128:(g + 1) * 128] = rng.integers(0, hi + 1, size=128)
+    sc = rng.standard_normal(N).astype(np.float16)
+    p = q.qoq_pack_codes(q4, s1, z, sc, 128)
+    uq4, us1, uz, usc = q.qoq_unpack_weights(p)
+    assert np.array_equal(uq4, q4) and np.array_equal(us1, s1) and np.array_equal(uz, z)
+    assert np.array_equal(usc.view(np.uint16), sc.view(np.uint16))
+    bad = s1.copy(); bad[0, 0] = 0
+    with pytest.raises(q.QoQError):
+        q.qoq_pack_codes(q4, bad, z, sc, 128)
+    bad = s1.copy(); bad[0, 0] = 17
+    with pytest.raises(q.QoQError):
+        q.qoq_pack_codes(q4, bad, z, sc, 128)
+    # w8 = (15 - 0) * 16 = 240 breaks the INT8 bound
+    q4b = q4.copy(); q4b[0, 0] = 15
+    s1b = s1.copy(); s1b[0, 0] = 16
+    zb = z.copy(); zb[0, 0] = 0
+    with pytest.raises(q.QoQError):
+        q.qoq_pack_codes(q4b, s1b, zb, sc, 128)
+    # z * s1 = 9 * 16 = 144 > 128
+    zb[0, 0] = 9; q4b[0, 0] = 9
+    with pytest.raises(q.QoQError):
+        q.qoq_pack_codes(q4b, s1b, zb, sc, 128)
+    # per-channel roundtrip
+    zc = rng.integers(0, 16, size=N).astype(np.uint8)
+    p = q.qoq_pack_codes(q4, None, zc, sc, 0)
+    uq4, us1, uz, usc = q.qoq_unpack_weights(p)
+    assert us1 is None and np.array_equal(uq4, q4) and np.array_equal(uz, zc)
+
+
+def test_pack_codes_accepts_extreme_valid_bytes():
+    # w8 = -128 (z*s1 = 128, q4 = 0) and w8 = 127 are the byte extremes the
+    # packed dequantization must still represent
+    N, K = 16, 128
+    q4 = np.zeros((N, K), np.uint8)
+    s1 = np.full((N, 1), 16, np.uint8)
+    z = np.full((N, 1), 8, np.uint8)
+    q4[:, 1] = 15  # (15 - 8) * 16 = 112
+    q.qoq_pack_codes(q4, s1, z, np.ones(N, np.float16), 128)
+    s1[:] = 1; z[:] = 0; q4[:] = 15
+    q.qoq_pack_codes(q4, s1, z, np.ones(N, np.float16), 128)
+
+
+def test_device_entry_points_validate_before_launch():
+    # argument errors are reported synchronously, without touching a GPU
+    lib = q.load_library()
+    assert lib.qoq_quant_act_per_token(None, 4, 128, 128, None, None, None) == 1
+    assert lib.qoq_w4a8_gemm(None, None, None, None, None, None, 4, 16, 128, 16, 128, None, 0, None) == 1
+    # K not a multiple of 128 (non-null dummy pointers are never dereferenced)
+    d = 4096
+    assert lib.qoq_w4a8_gemm_i32(d, d, d, d, 4, 16, 100, 16, 128, None, 0, None) == 2
+    # ldacc < N
+    assert lib.qoq_w4a8_gemm_i32(d, d, d, d, 4, 16, 128, 8, 128, None, 0, None) == 1
+    # misaligned qweight
+    assert lib.qoq_w4a8_gemm_i32(d, d + 4, d, d, 4, 16, 128, 16, 128, None, 0, None) == 3
+    assert lib.qoq_w4a8_gemm_workspace_size(4, 16, 128, 128) == 0

@@ -1,0 +1,22 @@
+"""QoQ W4A8 GEMM for MI355X (gfx950): Python binding of libqoq.so.
+
+The C ABI (include/qoq.h) is the product; this package only marshals
+arguments to it.  Names mirror the C entry points.
+"""
+
+from ._native import (  # noqa: F401
+    EXPORTS,
+    GROUP,
+    LIB_PATH,
+    PackedWeight,
+    QoQError,
+    load_library,
+    qoq_pack_codes,
+    qoq_pack_weights,
+    qoq_quant_act_per_token,
+    qoq_unpack_weights,
+    qoq_w4a8_forward,
+    qoq_w4a8_gemm,
+    qoq_w4a8_gemm_i32,
+    qoq_weight_layout_query,
+)

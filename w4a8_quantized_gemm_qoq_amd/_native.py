@@ -1,0 +1,278 @@
+"""ctypes binding of libqoq.so (argument marshalling only).
+
+Every step of the W4A8 path runs inside the library: the host packer for the
+offline weight encode, the HIP kernels for activation quantization and the
+GEMM.  This module only turns NumPy arrays / torch tensors into pointers and
+sizes, passes torch's current HIP stream, and maps error codes to Python
+exceptions.  It never computes a result itself and has no fallback: if the
+library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqoq.so")
+
+EXPORTS = [
+    "qoq_status_string",
+    "qoq_last_error",
+    "qoq_weight_layout_query",
+    "qoq_pack_weights",
+    "qoq_pack_codes",
+    "qoq_unpack_weights",
+    "qoq_quant_act_per_token",
+    "qoq_w4a8_gemm_workspace_size",
+    "qoq_w4a8_gemm",
+    "qoq_w4a8_gemm_i32",
+]
+
+GROUP = 128
+
+
+class QoQError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        super().__init__(f"{fn}: status {status}: {detail}")
+        self.status = status
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [
+        ("layout_id", ctypes.c_int32),
+        ("group_size", ctypes.c_int32),
+        ("N", ctypes.c_int64),
+        ("K", ctypes.c_int64),
+        ("N_pad", ctypes.c_int64),
+        ("n_groups", ctypes.c_int64),
+        ("qweight_bytes", ctypes.c_size_t),
+        ("meta_bytes", ctypes.c_size_t),
+        ("scale_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib = None
+
+
+def load_library():
+    """Load libqoq.so (after torch, so that torch's HIP runtime is the one in use)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m w4a8_quantized_gemm_qoq_amd.build` "
+            "(there is no fallback implementation)")
+    try:
+        import torch  # noqa: F401  -- loads torch's libamdhip64 first
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "qoq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "qoq_last_error": (ctypes.c_char_p, []),
+        "qoq_weight_layout_query": (ctypes.c_int, [i64, i64, i32, ctypes.POINTER(_Layout)]),
+        "qoq_pack_weights": (ctypes.c_int, [vp, i64, i64, i32, vp, vp, vp]),
+        "qoq_pack_codes": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i32, vp, vp, vp]),
+        "qoq_unpack_weights": (ctypes.c_int, [vp, vp, vp, i64, i64, i32, vp, vp, vp, vp]),
+        "qoq_quant_act_per_token": (ctypes.c_int, [vp, i64, i64, i64, vp, vp, vp]),
+        "qoq_w4a8_gemm_workspace_size": (sz, [i64, i64, i64, i32]),
+        "qoq_w4a8_gemm": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]),
+        "qoq_w4a8_gemm_i32": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, fn: str):
+    if status != 0:
+        lib = load_library()
+        raise QoQError(status, fn, lib.qoq_last_error().decode() or lib.qoq_status_string(status).decode())
+
+
+def _np_ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "host arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _t_ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ---------------------------------------------------------------- host side
+
+def qoq_weight_layout_query(N: int, K: int, group_size: int = GROUP) -> dict:
+    lib = load_library()
+    L = _Layout()
+    _check(lib.qoq_weight_layout_query(N, K, group_size, ctypes.byref(L)), "qoq_weight_layout_query")
+    return {f: getattr(L, f) for f, _ in _Layout._fields_}
+
+
+@dataclass
+class PackedWeight:
+    """Packed W4 weights (host NumPy arrays or device torch tensors)."""
+    qweight: object
+    meta: object
+    scale: object  # FP16 bit patterns (uint16) on the host, torch.float16 on the device
+    N: int
+    K: int
+    group_size: int
+
+    def to(self, device="cuda") -> "PackedWeight":
+        import torch
+        def dev(a, dtype=None):
+            t = torch.from_numpy(np.ascontiguousarray(a))
+            if dtype is not None:
+                t = t.view(dtype)
+            return t.to(device)
+        return PackedWeight(dev(self.qweight), dev(self.meta), dev(self.scale, torch.float16),
+                            self.N, self.K, self.group_size)
+
+
+def _alloc_packed(N, K, group_size):
+    L = qoq_weight_layout_query(N, K, group_size)
+    return (L, np.empty(L["qweight_bytes"], np.uint8), np.empty(L["meta_bytes"], np.uint8),
+            np.empty(L["N_pad"], np.uint16))
+
+
+def qoq_pack_weights(W: np.ndarray, group_size: int = GROUP) -> PackedWeight:
+    """Offline progressive (g128) or per-channel W4 encode + pack, on the host."""
+    W = np.ascontiguousarray(W, dtype=np.float16)
+    N, K = W.shape
+    lib = load_library()
+    _, qw, meta, scale = _alloc_packed(N, K, group_size)
+    _check(lib.qoq_pack_weights(_np_ptr(W.view(np.uint16)), N, K, group_size, _np_ptr(qw), _np_ptr(meta),
+                                _np_ptr(scale)), "qoq_pack_weights")
+    return PackedWeight(qw, meta, scale, N, K, group_size)
+
+
+def qoq_pack_codes(q4, s1, z, scale, group_size: int = GROUP) -> PackedWeight:
+    q4 = np.ascontiguousarray(q4, dtype=np.uint8)
+    N, K = q4.shape
+    z = np.ascontiguousarray(z, dtype=np.uint8)
+    s1 = None if s1 is None else np.ascontiguousarray(s1, dtype=np.uint8)
+    scale = np.ascontiguousarray(np.asarray(scale, dtype=np.float16).view(np.uint16))
+    lib = load_library()
+    _, qw, meta, sc = _alloc_packed(N, K, group_size)
+    _check(lib.qoq_pack_codes(_np_ptr(q4), _np_ptr(s1), _np_ptr(z), _np_ptr(scale), N, K, group_size, _np_ptr(qw),
+                              _np_ptr(meta), _np_ptr(sc)), "qoq_pack_codes")
+    return PackedWeight(qw, meta, sc, N, K, group_size)
+
+
+def qoq_unpack_weights(p: PackedWeight):
+    """(q4 [N,K], s1 [N,G] or None, z [N,G] or [N], scale fp16 [N]) from host-packed buffers."""
+    lib = load_library()
+    N, K, gs = p.N, p.K, p.group_size
+    G = K // GROUP
+    q4 = np.empty((N, K), np.uint8)
+    s1 = np.empty((N, G), np.uint8) if gs else None
+    z = np.empty((N, G), np.uint8) if gs else np.empty(N, np.uint8)
+    sc = np.empty(N, np.uint16)
+    scale_in = np.ascontiguousarray(np.asarray(p.scale).view(np.uint16))
+    _check(lib.qoq_unpack_weights(_np_ptr(p.qweight), _np_ptr(p.meta), _np_ptr(scale_in), N, K, gs, _np_ptr(q4),
+                                  _np_ptr(s1), _np_ptr(z), _np_ptr(sc)), "qoq_unpack_weights")
+    return q4, s1, z, sc.view(np.float16)
+
+
+# ---------------------------------------------------------------- device side
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("device entry points take GPU tensors")
+
+
+def qoq_quant_act_per_token(x, x8=None, sx=None, stream=None):
+    """Per-token INT8 quantization of FP16 x [M, K] (row stride may exceed K) on the GPU."""
+    import torch
+    _require_cuda(x)
+    if x.dtype != torch.float16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D FP16 tensor with unit column stride")
+    M, K = x.shape
+    if x8 is None:
+        x8 = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if sx is None:
+        sx = torch.empty((M,), dtype=torch.float16, device=x.device)
+    _require_cuda(x8, sx)
+    if not (x8.is_contiguous() and x8.shape == (M, K) and x8.dtype == torch.int8):
+        raise ValueError("x8 must be a contiguous int8 [M, K] tensor")
+    if not (sx.is_contiguous() and sx.numel() == M and sx.dtype == torch.float16):
+        raise ValueError("sx must be a contiguous float16 [M] tensor")
+    lib = load_library()
+    _check(lib.qoq_quant_act_per_token(_t_ptr(x), M, K, x.stride(0), _t_ptr(x8), _t_ptr(sx), _stream(stream)),
+           "qoq_quant_act_per_token")
+    return x8, sx
+
+
+def _check_gemm_inputs(x8, w: PackedWeight):
+    import torch
+    _require_cuda(x8, w.qweight, w.meta, w.scale)
+    if x8.dtype != torch.int8 or x8.dim() != 2 or not x8.is_contiguous():
+        raise ValueError("x8 must be a contiguous int8 [M, K] tensor")
+    if x8.shape[1] != w.K:
+        raise ValueError(f"x8 has K={x8.shape[1]}, weights have K={w.K}")
+
+
+def qoq_w4a8_gemm(x8, sx, w: PackedWeight, y=None, workspace=None, stream=None):
+    """y = fp16(x8 @ w8^T * s_x * scale) on the GPU; returns y [M, N] FP16."""
+    import torch
+    _check_gemm_inputs(x8, w)
+    M = x8.shape[0]
+    if y is None:
+        y = torch.empty((M, w.N), dtype=torch.float16, device=x8.device)
+    _require_cuda(sx, y)
+    if y.dtype != torch.float16 or y.shape != (M, w.N) or y.stride(1) != 1:
+        raise ValueError("y must be float16 [M, N] with unit column stride")
+    if sx.dtype != torch.float16 or sx.numel() != M or not sx.is_contiguous():
+        raise ValueError("sx must be contiguous float16 [M]")
+    lib = load_library()
+    ws_bytes = lib.qoq_w4a8_gemm_workspace_size(M, w.N, w.K, w.group_size)
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x8.device)
+    _check(lib.qoq_w4a8_gemm(_t_ptr(x8), _t_ptr(sx), _t_ptr(w.qweight), _t_ptr(w.meta), _t_ptr(w.scale), _t_ptr(y),
+                             M, w.N, w.K, y.stride(0), w.group_size, _t_ptr(workspace) if ws_bytes else None,
+                             ws_bytes, _stream(stream)), "qoq_w4a8_gemm")
+    return y
+
+
+def qoq_w4a8_gemm_i32(x8, w: PackedWeight, acc=None, workspace=None, stream=None):
+    """Exact INT32 accumulators acc = x8 @ w8^T on the GPU (debug entry point)."""
+    import torch
+    _check_gemm_inputs(x8, w)
+    M = x8.shape[0]
+    if acc is None:
+        acc = torch.empty((M, w.N), dtype=torch.int32, device=x8.device)
+    _require_cuda(acc)
+    if acc.dtype != torch.int32 or acc.shape != (M, w.N) or acc.stride(1) != 1:
+        raise ValueError("acc must be int32 [M, N] with unit column stride")
+    lib = load_library()
+    ws_bytes = lib.qoq_w4a8_gemm_workspace_size(M, w.N, w.K, w.group_size)
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x8.device)
+    _check(lib.qoq_w4a8_gemm_i32(_t_ptr(x8), _t_ptr(w.qweight), _t_ptr(w.meta), _t_ptr(acc), M, w.N, w.K,
+                                 acc.stride(0), w.group_size, _t_ptr(workspace) if ws_bytes else None, ws_bytes,
+                                 _stream(stream)), "qoq_w4a8_gemm_i32")
+    return acc
+
+
+def qoq_w4a8_forward(x, w: PackedWeight, stream=None):
+    """One pass of the online path: per-token quantization then the W4A8 GEMM."""
+    x8, sx = qoq_quant_act_per_token(x, stream=stream)
+    return qoq_w4a8_gemm(x8, sx, w, stream=stream)

@@ -1,0 +1,187 @@
+// Per-token symmetric INT8 activation quantizer for gfx950.
+//
+// Follows "QServe: W4A8KV4 Quantization and System Co-design for Efficient
+// LLM Serving" (paperlayer.ai abs/2405.04532v3 summary): §6 (experimental
+// setup) quantizes activations per token to INT8; §5 (runtime and precision
+// mapping) feeds INT8 activations to the W4A8 GEMM.  Per row m:
+//   s_x = fp16(max_k |x| / 127)      -- FP32 IEEE divide, round half to even
+//   x8  = clamp(rint(x / s_x), -127, 127), zero row when s_x == 0.
+//
+// One 256-thread workgroup per token row.  The row is read once with 128-bit
+// loads and kept in registers (up to 16384 channels), the max |x| is reduced
+// exactly on the FP16 bit patterns (for non-negative finite halves the integer
+// order is the numeric order), then every element is divided by the stored
+// FP16 scale with a correctly rounded FP32 division and rounded half-even.
+// Build without fast-math: the division must stay IEEE.
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include "qoq_internal.h"
+
+namespace qoq {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint32_t max_abs_bits8(uint4 v) {
+  // max over 8 halves of (bits & 0x7fff), computed in two u16 lanes
+  const uint32_t a = v.x & 0x7fff7fffu, b = v.y & 0x7fff7fffu;
+  const uint32_t c = v.z & 0x7fff7fffu, d = v.w & 0x7fff7fffu;
+  auto m2 = [](uint32_t p, uint32_t q) {
+    const uint32_t lo = max(p & 0xffffu, q & 0xffffu);
+    const uint32_t hi = max(p >> 16, q >> 16);
+    return lo | (hi << 16);
+  };
+  const uint32_t r = m2(m2(a, b), m2(c, d));
+  return max(r & 0xffffu, r >> 16);
+}
+
+__device__ __forceinline__ int quant1(uint32_t hbits, float s) {
+  const float x = __half2float(__ushort_as_half(static_cast<unsigned short>(hbits)));
+  float q = rintf(x / s);
+  q = fminf(127.0f, fmaxf(-127.0f, q));
+  return static_cast<int>(q);
+}
+
+__device__ __forceinline__ uint32_t quant4(uint32_t h01, uint32_t h23, float s) {
+  const int q0 = quant1(h01 & 0xffffu, s), q1 = quant1(h01 >> 16, s);
+  const int q2 = quant1(h23 & 0xffffu, s), q3 = quant1(h23 >> 16, s);
+  return (uint32_t(q0) & 0xffu) | ((uint32_t(q1) & 0xffu) << 8) | ((uint32_t(q2) & 0xffu) << 16) |
+         ((uint32_t(q3) & 0xffu) << 24);
+}
+
+// Block-wide max of a uint32 value; every thread gets the result.
+__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, 64)));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  uint32_t r = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) r = max(r, red[w]);
+  return r;
+}
+
+__device__ __forceinline__ float scale_from_absmax(uint32_t amax_bits, unsigned short* s_bits) {
+  const float a = __half2float(__ushort_as_half(static_cast<unsigned short>(amax_bits)));
+  const __half sh = __float2half_rn(a / 127.0f);
+  *s_bits = __half_as_ushort(sh);
+  return __half2float(sh);
+}
+
+// Vector path, row held in registers: VPT vectors of 8 halves per thread.
+template <int VPT>
+__global__ __launch_bounds__(kThreads) void act_quant_reg_kernel(const uint4* __restrict__ x, int64_t ldx_vec,
+                                                                  int k_vec, uint2* __restrict__ x8,
+                                                                  unsigned short* __restrict__ sx) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int64_t m = blockIdx.x;
+  const uint4* row = x + m * ldx_vec;
+  uint4 v[VPT];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int idx = threadIdx.x + i * kThreads;
+    v[i] = idx < k_vec ? row[idx] : make_uint4(0, 0, 0, 0);
+    amax = max(amax, max_abs_bits8(v[i]));
+  }
+  amax = block_max(amax, red);
+  unsigned short s_bits;
+  const float s = scale_from_absmax(amax, &s_bits);
+  if (threadIdx.x == 0) sx[m] = s_bits;
+  uint2* out = x8 + m * k_vec;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int idx = threadIdx.x + i * kThreads;
+    if (idx < k_vec) {
+      uint2 q = make_uint2(0u, 0u);
+      if (s != 0.0f) q = make_uint2(quant4(v[i].x, v[i].y, s), quant4(v[i].z, v[i].w, s));
+      out[idx] = q;
+    }
+  }
+}
+
+// Vector path for long rows: two passes over the row (the second from cache).
+__global__ __launch_bounds__(kThreads) void act_quant_stream_kernel(const uint4* __restrict__ x, int64_t ldx_vec,
+                                                                     int k_vec, uint2* __restrict__ x8,
+                                                                     unsigned short* __restrict__ sx) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int64_t m = blockIdx.x;
+  const uint4* row = x + m * ldx_vec;
+  uint32_t amax = 0;
+  for (int idx = threadIdx.x; idx < k_vec; idx += kThreads) amax = max(amax, max_abs_bits8(row[idx]));
+  amax = block_max(amax, red);
+  unsigned short s_bits;
+  const float s = scale_from_absmax(amax, &s_bits);
+  if (threadIdx.x == 0) sx[m] = s_bits;
+  uint2* out = x8 + m * k_vec;
+  for (int idx = threadIdx.x; idx < k_vec; idx += kThreads) {
+    const uint4 v = row[idx];
+    uint2 q = make_uint2(0u, 0u);
+    if (s != 0.0f) q = make_uint2(quant4(v.x, v.y, s), quant4(v.z, v.w, s));
+    out[idx] = q;
+  }
+}
+
+// Scalar path for any K / alignment.
+__global__ __launch_bounds__(kThreads) void act_quant_scalar_kernel(const unsigned short* __restrict__ x,
+                                                                     int64_t ldx, int64_t K,
+                                                                     int8_t* __restrict__ x8,
+                                                                     unsigned short* __restrict__ sx) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int64_t m = blockIdx.x;
+  const unsigned short* row = x + m * ldx;
+  uint32_t amax = 0;
+  for (int64_t k = threadIdx.x; k < K; k += kThreads) amax = max(amax, uint32_t(row[k] & 0x7fffu));
+  amax = block_max(amax, red);
+  unsigned short s_bits;
+  const float s = scale_from_absmax(amax, &s_bits);
+  if (threadIdx.x == 0) sx[m] = s_bits;
+  for (int64_t k = threadIdx.x; k < K; k += kThreads)
+    x8[m * K + k] = s != 0.0f ? static_cast<int8_t>(quant1(row[k], s)) : int8_t(0);
+}
+
+}  // namespace
+}  // namespace qoq
+
+using namespace qoq;
+
+extern "C" int qoq_quant_act_per_token(const void* x_fp16, int64_t M, int64_t K, int64_t ldx, int8_t* x8,
+                                       void* sx_fp16, void* stream) {
+  clear_error();
+  if (!x_fp16 || !x8 || !sx_fp16) return fail(QOQ_ERR_INVALID_ARG, "qoq_quant_act_per_token: null pointer argument");
+  if (M < 1 || K < 1) return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "qoq_quant_act_per_token: M and K must be >= 1");
+  if (ldx < K) return fail(QOQ_ERR_INVALID_ARG, "qoq_quant_act_per_token: ldx < K");
+  if (M > 0x7fffffff) return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "qoq_quant_act_per_token: M too large");
+  if (reinterpret_cast<uintptr_t>(x_fp16) % 2 || reinterpret_cast<uintptr_t>(sx_fp16) % 2)
+    return fail(QOQ_ERR_ALIGNMENT, "qoq_quant_act_per_token: FP16 pointers must be 2-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>(M)), block(kThreads);
+  const bool vec = K % 8 == 0 && ldx % 8 == 0 && reinterpret_cast<uintptr_t>(x_fp16) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(x8) % 8 == 0 && K / 8 <= 0x7fffffff;
+  auto* sx = static_cast<unsigned short*>(sx_fp16);
+  if (vec) {
+    const auto* xv = static_cast<const uint4*>(x_fp16);
+    auto* qv = reinterpret_cast<uint2*>(x8);
+    const int k_vec = static_cast<int>(K / 8);
+    const int64_t ldv = ldx / 8;
+    if (k_vec <= kThreads)
+      hipLaunchKernelGGL(act_quant_reg_kernel<1>, grid, block, 0, st, xv, ldv, k_vec, qv, sx);
+    else if (k_vec <= 2 * kThreads)
+      hipLaunchKernelGGL(act_quant_reg_kernel<2>, grid, block, 0, st, xv, ldv, k_vec, qv, sx);
+    else if (k_vec <= 4 * kThreads)
+      hipLaunchKernelGGL(act_quant_reg_kernel<4>, grid, block, 0, st, xv, ldv, k_vec, qv, sx);
+    else if (k_vec <= 8 * kThreads)
+      hipLaunchKernelGGL(act_quant_reg_kernel<8>, grid, block, 0, st, xv, ldv, k_vec, qv, sx);
+    else
+      hipLaunchKernelGGL(act_quant_stream_kernel, grid, block, 0, st, xv, ldv, k_vec, qv, sx);
+  } else {
+    hipLaunchKernelGGL(act_quant_scalar_kernel, grid, block, 0, st, static_cast<const unsigned short*>(x_fp16), ldx,
+                       K, x8, sx);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(QOQ_ERR_HIP, "qoq_quant_act_per_token: launch failed: %s", hipGetErrorString(e));
+  return QOQ_OK;
+}
