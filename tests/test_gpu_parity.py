@@ -116,6 +116,10 @@ SMALL = [
     (257, 384, 300, 128),
     (5, 256, 48, 0),
     (70, 384, 100, 0),
+    (200, 2048, 96, 128),   # K split in 4 (INT32 partials + reduction)
+    (97, 1920, 40, 128),    # K split in 2 with an odd group count per split
+    (100, 1024, 50, 0),     # per-channel with a K split
+    (300, 640, 520, 128),   # several 128x128 tiles, ragged M and N
 ]
 
 

@@ -23,7 +23,8 @@
 // per-channel variant s1 = 1 and c = 128 - z.
 //
 // Two kernels share the packed layout (see qoq.h):
-//   gemm16: v_mfma_i32_16x16x64_i8, 16-row M tiles; for skinny M (decode).
+//   skinny: v_mfma_i32_16x16x64_i8, 16-row M tiles, K split across the
+//           waves of a block; for M <= 64 (decode, memory-bound).
 //   gemm32: v_mfma_i32_32x32x32_i8, 32x32 tiles; for M > 64 (prefill).
 // The activation tile of each 128-wide K group is staged in LDS (XOR-swizzled
 // 16-byte chunks, double-buffered); weights go global -> VGPR directly and are
@@ -36,11 +37,22 @@
 
 #include "qoq_internal.h"
 
+// Large-M tile: WM x WN waves, each TM x TN tiles of 32x32.
+#ifndef QOQ_LWM
+#define QOQ_LWM 2
+#define QOQ_LWN 4
+#define QOQ_LTM 4
+#define QOQ_LTN 2
+#endif
+
 namespace qoq {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+// 128-bit payloads are native vectors (HIP's u32x4 is a struct whose copies
+// lower to memcpy through scratch).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t c) {
   uint32_t d;
@@ -76,36 +88,10 @@ __device__ __forceinline__ void meta_perchannel(uint32_t z, uint32_t& S, uint32_
 // different banks.
 __device__ __forceinline__ int lds_off(int row, int kc) { return row * 128 + ((kc ^ (row & 7)) << 4); }
 
-template <int BM, int THREADS>
-struct AStage {
-  static constexpr int kChunks = BM * 8;
-  static constexpr int kPer = (kChunks + THREADS - 1) / THREADS;
-  uint4 r[kPer];
-
-  __device__ __forceinline__ void load(const int8_t* __restrict__ x8, int64_t K, int m0, int M, int g) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int ch = threadIdx.x + i * THREADS;
-      const int row = ch >> 3, kc = ch & 7;
-      r[i] = make_uint4(0, 0, 0, 0);
-      if ((kChunks % THREADS == 0 || ch < kChunks) && m0 + row < M)
-        r[i] = *reinterpret_cast<const uint4*>(x8 + int64_t(m0 + row) * K + int64_t(g) * 128 + kc * 16);
-    }
-  }
-  __device__ __forceinline__ void store(int8_t* lds) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int ch = threadIdx.x + i * THREADS;
-      if (kChunks % THREADS == 0 || ch < kChunks)
-        *reinterpret_cast<uint4*>(lds + lds_off(ch >> 3, ch & 7)) = r[i];
-    }
-  }
-};
-
 struct GemmArgs {
   const int8_t* x8;
   const unsigned short* sx;
-  const uint4* qw;
+  const u32x4* qw;
   const uint32_t* meta;  // g128: dwords; per-channel: bytes read through meta8
   const uint8_t* meta8;
   const unsigned short* scale;
@@ -113,13 +99,15 @@ struct GemmArgs {
   int M, N, G, G4q;  // G4q = G4 / 4 (meta dwords per strip per channel)
   int n_strips;
   int64_t ldo;
+  int ksplit;        // K splits (grid.z); > 1 writes INT32 partials
+  int64_t zstride;   // element offset between the partials of two splits
 };
 
 template <bool I32OUT>
 __device__ __forceinline__ void store_out(const GemmArgs& a, int row, int col, int acc, float sxr) {
   if (row < a.M && col < a.N) {
     if constexpr (I32OUT) {
-      static_cast<int*>(a.out)[int64_t(row) * a.ldo + col] = acc;
+      static_cast<int*>(a.out)[int64_t(blockIdx.z) * a.zstride + int64_t(row) * a.ldo + col] = acc;
     } else {
       const float sc = __half2float(__ushort_as_half(a.scale[col]));
       const float y = static_cast<float>(acc) * sxr * sc;
@@ -129,19 +117,23 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int row, int col, i
 }
 
 // ---------------------------------------------------------------------------
-// gemm16: block = WN waves side by side along N, each wave TN strips of 16
-// output channels; all waves share the BM = TM*16 rows of the block.
-template <int WN, int TM, int TN, bool PERCH, bool I32OUT>
-__global__ __launch_bounds__(64 * WN) void gemm16_kernel(GemmArgs a) {
-  constexpr int THREADS = 64 * WN;
-  constexpr int BM = TM * 16;
-  __shared__ __align__(16) int8_t As[2][BM * 128];
-
+// skinny: M <= 64 (decode).  A block is KS waves that split the K groups of
+// the same TN strips between them, so every wave streams different weight
+// bytes.  Each wave keeps its activation operand in registers, loaded straight
+// from L2 (the INT8 activations of a decode batch are small and shared by all
+// blocks), and streams its weights through a PF-deep register ring of 128-bit
+// loads so that enough bytes are in flight to cover HBM latency.  The KS
+// partial INT32 accumulators are summed exactly through LDS at the end.
+template <int TM, int TN, int KS, int PF, bool PERCH, bool I32OUT>
+__global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
+  static_assert(PF % 2 == 0, "PF must be even (A operand ping-pong)");
+  __shared__ int red[(KS > 1 ? KS - 1 : 1) * TM * 4 * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int m0 = blockIdx.y * BM;
-  const int sbase = (blockIdx.x * WN + wave) * TN;
-  const int64_t K = int64_t(a.G) * 128;
   const int c16 = lane & 15, j = lane >> 4;
+  const int sbase = blockIdx.x * TN;
+  const int m0 = blockIdx.y * TM * 16;
+  const int64_t K = int64_t(a.G) * 128;
+  const int g0 = (a.G * wave) / KS, g1 = (a.G * (wave + 1)) / KS;
 
   int strip[TN];
 #pragma unroll
@@ -159,57 +151,100 @@ __global__ __launch_bounds__(64 * WN) void gemm16_kernel(GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) acc[i][t] = v4i{0, 0, 0, 0};
 
-  AStage<BM, THREADS> ast;
-  uint4 bcur[TN], bnext[TN];
-  uint32_t mcur[TN], mnext[TN];
+  // activation rows of this lane: m0 + 16i + c16, K chunk 16j (+64 for h = 1)
+  const int8_t* arow[TM];
+  bool aval[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int row = m0 + i * 16 + c16;
+    aval[i] = row < a.M;
+    arow[i] = a.x8 + int64_t(aval[i] ? row : 0) * K + 16 * j;
+  }
 
-  auto load_b = [&](int g, uint4* b, uint32_t* m) {
+  u32x4 bq[PF][TN];
+  uint32_t mq[PF][TN];
+  u32x4 aq[2][TM][2];
+
+  auto load_b = [&](int g, u32x4* b, uint32_t* m) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       b[t] = a.qw[(int64_t(strip[t]) * a.G + g) * 64 + lane];
       if constexpr (!PERCH) m[t] = a.meta[(int64_t(strip[t]) * a.G4q + (g >> 2)) * 16 + c16];
     }
   };
-
-  ast.load(a.x8, K, m0, a.M, 0);
-  load_b(0, bcur, mcur);
-  ast.store(As[0]);
-  __syncthreads();
-
-  for (int g = 0; g < a.G; ++g) {
-    const bool more = g + 1 < a.G;
-    if (more) {
-      ast.load(a.x8, K, m0, a.M, g + 1);
-      load_b(g + 1, bnext, mnext);
+  auto load_a = [&](int g, u32x4 (*ar)[2]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        ar[i][h] = aval[i] ? *reinterpret_cast<const u32x4*>(arow[i] + int64_t(g) * 128 + 64 * h)
+                           : u32x4{0u, 0u, 0u, 0u};
     }
-    const int8_t* lds = As[g & 1];
-    if constexpr (!PERCH) {
+  };
+
 #pragma unroll
-      for (int t = 0; t < TN; ++t) meta_g128((mcur[t] >> (8 * (g & 3))) & 0xffu, S[t], C[t]);
-    }
+  for (int p = 0; p < PF; ++p)
+    if (g0 + p < g1) load_b(g0 + p, bq[p], mq[p]);
+  if (g0 < g1) load_a(g0, aq[0]);
+
+  for (int gb = g0; gb < g1; gb += PF) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      v4i af[TM];
+    for (int u = 0; u < PF; ++u) {
+      const int g = gb + u;
+      if (g < g1) {
+        u32x4 bc[TN];
+        uint32_t mc[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const v4i*>(lds + lds_off(i * 16 + c16, 4 * h + j));
+        for (int t = 0; t < TN; ++t) {
+          bc[t] = bq[u][t];
+          mc[t] = mq[u][t];
+        }
+        if (g + PF < g1) load_b(g + PF, bq[u], mq[u]);
+        if (g + 1 < g1) load_a(g + 1, aq[(u + 1) & 1]);
+        if constexpr (!PERCH) {
 #pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        const uint32_t v0 = h ? bcur[t].z : bcur[t].x;
-        const uint32_t v1 = h ? bcur[t].w : bcur[t].y;
-        const v4i bf = dequant16(v0, v1, S[t], C[t]);
+          for (int t = 0; t < TN; ++t) meta_g128((mc[t] >> (8 * (g & 3))) & 0xffu, S[t], C[t]);
+        }
 #pragma unroll
-        for (int i = 0; i < TM; ++i) acc[i][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf, acc[i][t], 0, 0, 0);
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int t = 0; t < TN; ++t) {
+            const v4i bf = dequant16(h ? bc[t][2] : bc[t][0], h ? bc[t][3] : bc[t][1], S[t], C[t]);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+              const u32x4 av = aq[u & 1][i][h];
+              const v4i af = v4i{int(av[0]), int(av[1]), int(av[2]), int(av[3])};
+              acc[i][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf, acc[i][t], 0, 0, 0);
+            }
+          }
+        }
       }
     }
-    if (more) ast.store(As[(g + 1) & 1]);
-    __syncthreads();
+  }
+
+  // exact cross-wave reduction of the K-split partial sums
+  if constexpr (KS > 1) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
-      bcur[t] = bnext[t];
-      mcur[t] = mnext[t];
+      if (wave > 0) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[(((wave - 1) * TM + i) * 4 + r) * 64 + lane] = acc[i][t][r];
+      }
+      __syncthreads();
+      if (wave == 0) {
+#pragma unroll
+        for (int w = 1; w < KS; ++w)
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][t][r] += red[(((w - 1) * TM + i) * 4 + r) * 64 + lane];
+      }
+      __syncthreads();
     }
   }
+  if (wave != 0) return;
 
   // epilogue: lane holds rows 4*(lane/16)+r of each 16x16 tile, column lane%16
 #pragma unroll
@@ -228,23 +263,108 @@ __global__ __launch_bounds__(64 * WN) void gemm16_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// gemm32: block = WM x WN waves; wave tile = TM*32 rows x TN*32 columns.
+// gemm_large: M > 64 (prefill, compute-bound).  Block = WM x WN waves, wave
+// tile = TM*32 rows x TN*32 columns of v_mfma_i32_32x32x32_i8.  The K loop is
+// unrolled by two with explicit ping-pong register buffers: while group g is
+// multiplied from LDS buffer g&1 and weight registers set g&1, the activation
+// chunks and packed weights of group g+1 are already in flight into the other
+// set, and are written to the other LDS buffer after the MFMAs.  There are no
+// loop-carried register copies, so every wait is for data that is actually
+// needed next.
+template <int BM, int THREADS>
+struct ATile {
+  static constexpr int kChunks = BM * 8;
+  static constexpr int kPer = kChunks / THREADS;
+  static_assert(kChunks % THREADS == 0, "A tile must split evenly over the block");
+};
+
+template <int NA, int THREADS>
+__device__ __forceinline__ void a_load(u32x4 (&r)[NA], const GemmArgs& a, int64_t K, int m0, int g) {
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int ch = threadIdx.x + i * THREADS;
+    const int row = min(m0 + (ch >> 3), a.M - 1);  // rows past M read a valid row; results are masked
+    r[i] = *reinterpret_cast<const u32x4*>(a.x8 + int64_t(row) * K + int64_t(g) * 128 + (ch & 7) * 16);
+  }
+}
+
+template <int NA, int THREADS>
+__device__ __forceinline__ void a_store(const u32x4 (&r)[NA], int8_t* lds) {
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int ch = threadIdx.x + i * THREADS;
+    *reinterpret_cast<u32x4*>(lds + lds_off(ch >> 3, ch & 7)) = r[i];
+  }
+}
+
+template <int TN, bool PERCH>
+__device__ __forceinline__ void b_load(u32x4 (&b)[TN][2], uint32_t (&m)[TN], const GemmArgs& a, const int (&strip)[TN],
+                                       int c16, int hh, int g) {
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    const u32x4* blk = a.qw + (int64_t(strip[t]) * a.G + g) * 64;
+    b[t][0] = blk[c16 + 16 * hh];
+    b[t][1] = blk[c16 + 16 * (2 + hh)];
+    if constexpr (!PERCH) m[t] = a.meta[(int64_t(strip[t]) * a.G4q + (g >> 2)) * 16 + c16];
+  }
+}
+
+// Multiply one 128-wide K group: 4 K steps of 32.  Weight slot 0 of a column
+// tile holds K steps 0 and 2 (low / high half), slot 1 holds steps 1 and 3.
+template <int TM, int TN, bool PERCH>
+__device__ __forceinline__ void large_group(v16i (&acc)[TM][TN], const int8_t* lds, const u32x4 (&b)[TN][2],
+                                            const uint32_t (&m)[TN], uint32_t (&S)[TN], uint32_t (&C)[TN], int g,
+                                            int row0, int c32, int hh) {
+  if constexpr (!PERCH) {
+#pragma unroll
+    for (int t = 0; t < TN; ++t) meta_g128((m[t] >> (8 * (g & 3))) & 0xffu, S[t], C[t]);
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    v4i af[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const v4i*>(lds + lds_off(row0 + i * 32 + c32, 2 * s + hh));
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      const u32x4& q = b[t][s & 1];
+      const v4i bf = dequant16((s >> 1) ? q[2] : q[0], (s >> 1) ? q[3] : q[1], S[t], C[t]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf, acc[i][t], 0, 0, 0);
+    }
+  }
+}
+
+#define QOQ_COMPILER_FENCE() asm volatile("" ::: "memory")
+
 template <int WM, int WN, int TM, int TN, bool PERCH, bool I32OUT>
-__global__ __launch_bounds__(64 * WM * WN) void gemm32_kernel(GemmArgs a) {
+__global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
   constexpr int THREADS = 64 * WM * WN;
   constexpr int BM = WM * TM * 32;
   constexpr int BN = WN * TN * 32;
-  __shared__ __align__(16) int8_t As[2][BM * 128];
+  constexpr int NA = ATile<BM, THREADS>::kPer;
+  __shared__ __align__(16) int8_t As0[BM * 128];
+  __shared__ __align__(16) int8_t As1[BM * 128];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN + wn * TN * 32;  // first column of this wave
+  // Tile order.  Workgroups are dispatched round-robin over the 8 XCDs, each
+  // with its own L2.  Remap so that each XCD gets a contiguous run of tiles,
+  // and walk tiles column-major so that the tiles resident on one XCD share
+  // the same packed weight columns (and neighbouring activation rows).
+  const int ny = gridDim.y;
+  const int nb = gridDim.x * ny;
+  int d = blockIdx.y * gridDim.x + blockIdx.x;
+  if (d < (nb / 8) * 8) d = (d % 8) * (nb / 8) + d / 8;
+  const int m0 = (d % ny) * BM;
+  const int n0 = (d / ny) * BN + wn * TN * 32;  // first column of this wave
   const int64_t K = int64_t(a.G) * 128;
   const int c32 = lane & 31, hh = lane >> 5;
   const int c16 = c32 & 15;
+  const int row0 = wm * TM * 32;
+  // K range of this split (every split holds at least one group)
+  const int gb = (a.G * int(blockIdx.z)) / a.ksplit;
+  const int ge = (a.G * (int(blockIdx.z) + 1)) / a.ksplit;
 
-  // column tile t, lane: channel n0 + 32t + c32 -> strip, channel-in-strip c16
   int strip[TN];
 #pragma unroll
   for (int t = 0; t < TN; ++t) strip[t] = min((n0 + 32 * t + c32) >> 4, a.n_strips - 1);
@@ -263,70 +383,42 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm32_kernel(GemmArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][t][e] = 0;
 
-  AStage<BM, THREADS> ast;
-  // per column tile two 16-byte slots: slot c16+16*hh (K steps 0, 2) and
-  // slot c16+16*(2+hh) (K steps 1, 3)
-  uint4 bcur[TN][2], bnext[TN][2];
-  uint32_t mcur[TN], mnext[TN];
+  u32x4 ra0[NA], ra1[NA];
+  u32x4 rb0[TN][2], rb1[TN][2];
+  uint32_t rm0[TN], rm1[TN];
 
-  auto load_b = [&](int g, uint4 (*b)[2], uint32_t* m) {
-#pragma unroll
-    for (int t = 0; t < TN; ++t) {
-      const uint4* blk = a.qw + (int64_t(strip[t]) * a.G + g) * 64;
-      b[t][0] = blk[c16 + 16 * hh];
-      b[t][1] = blk[c16 + 16 * (2 + hh)];
-      if constexpr (!PERCH) m[t] = a.meta[(int64_t(strip[t]) * a.G4q + (g >> 2)) * 16 + c16];
-    }
-  };
-
-  ast.load(a.x8, K, m0, a.M, 0);
-  load_b(0, bcur, mcur);
-  ast.store(As[0]);
+  a_load<NA, THREADS>(ra0, a, K, m0, gb);
+  b_load<TN, PERCH>(rb0, rm0, a, strip, c16, hh, gb);
+  a_store<NA, THREADS>(ra0, As0);
   __syncthreads();
 
-  for (int g = 0; g < a.G; ++g) {
-    const bool more = g + 1 < a.G;
-    if (more) {
-      ast.load(a.x8, K, m0, a.M, g + 1);
-      load_b(g + 1, bnext, mnext);
-    }
-    const int8_t* lds = As[g & 1];
-    if constexpr (!PERCH) {
-#pragma unroll
-      for (int t = 0; t < TN; ++t) meta_g128((mcur[t] >> (8 * (g & 3))) & 0xffu, S[t], C[t]);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      v4i af[TM];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const v4i*>(lds + lds_off(wm * TM * 32 + i * 32 + c32, 2 * s + hh));
-#pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        const uint4& q = bcur[t][s & 1];
-        const uint32_t v0 = (s >> 1) ? q.z : q.x;
-        const uint32_t v1 = (s >> 1) ? q.w : q.y;
-        const v4i bf = dequant16(v0, v1, S[t], C[t]);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf, acc[i][t], 0, 0, 0);
-      }
-    }
-    if (more) ast.store(As[(g + 1) & 1]);
+  // pairs of groups; every half issues the next group's loads before its MFMAs
+  int g = gb;
+  for (; g + 1 < ge; g += 2) {
+    a_load<NA, THREADS>(ra1, a, K, m0, g + 1);
+    b_load<TN, PERCH>(rb1, rm1, a, strip, c16, hh, g + 1);
+    QOQ_COMPILER_FENCE();
+    large_group<TM, TN, PERCH>(acc, As0, rb0, rm0, S, C, g, row0, c32, hh);
+    a_store<NA, THREADS>(ra1, As1);
     __syncthreads();
-#pragma unroll
-    for (int t = 0; t < TN; ++t) {
-      bcur[t][0] = bnext[t][0];
-      bcur[t][1] = bnext[t][1];
-      mcur[t] = mnext[t];
-    }
+
+    const int gn = min(g + 2, ge - 1);
+    a_load<NA, THREADS>(ra0, a, K, m0, gn);
+    b_load<TN, PERCH>(rb0, rm0, a, strip, c16, hh, gn);
+    QOQ_COMPILER_FENCE();
+    large_group<TM, TN, PERCH>(acc, As1, rb1, rm1, S, C, g + 1, row0, c32, hh);
+    a_store<NA, THREADS>(ra0, As0);
+    __syncthreads();
   }
+  if (g < ge)  // odd group count: the last group is already in (As0, rb0)
+    large_group<TM, TN, PERCH>(acc, As0, rb0, rm0, S, C, g, row0, c32, hh);
 
   // epilogue: lane holds column lane%32 and rows 8*(r/4) + 4*(lane/32) + r%4
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = m0 + wm * TM * 32 + i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const int row = m0 + row0 + i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
       float sxr = 0.0f;
       if constexpr (!I32OUT) sxr = row < a.M ? __half2float(__ushort_as_half(a.sx[row])) : 0.0f;
 #pragma unroll
@@ -336,35 +428,151 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm32_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Split-K reduction: sums the INT32 partials of the K splits (exact, in a
+// fixed order) and applies the epilogue.  Partials are [ksplit][M][ldw] with
+// ldw a multiple of 16; each thread handles four consecutive columns.
+template <bool I32OUT>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const int* __restrict__ ws, int ksplit, int M, int N,
+                                                            int ldw, const unsigned short* __restrict__ sx,
+                                                            const unsigned short* __restrict__ scale, void* out,
+                                                            int64_t ldo) {
+  const int per_row = ldw / 4;
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= int64_t(M) * per_row) return;
+  const int row = int(idx / per_row);
+  const int col = int(idx % per_row) * 4;
+  const int64_t zs = int64_t(M) * ldw;
+  const int* p = ws + int64_t(row) * ldw + col;
+  v4i s = *reinterpret_cast<const v4i*>(p);
+  for (int z = 1; z < ksplit; ++z) s += *reinterpret_cast<const v4i*>(p + z * zs);
+  float sxr = 0.0f;
+  if constexpr (!I32OUT) sxr = __half2float(__ushort_as_half(sx[row]));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int c = col + e;
+    if (c < N) {
+      if constexpr (I32OUT) {
+        static_cast<int*>(out)[int64_t(row) * ldo + c] = s[e];
+      } else {
+        const float y = static_cast<float>(s[e]) * sxr * __half2float(__ushort_as_half(scale[c]));
+        static_cast<__half*>(out)[int64_t(row) * ldo + c] = __float2half_rn(y);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launch helpers.
 
-template <int WN, int TM, int TN, bool PERCH, bool I32>
-hipError_t launch16(const GemmArgs& a, hipStream_t st) {
-  const int per_block = WN * TN;
-  const dim3 grid((a.n_strips + per_block - 1) / per_block, (a.M + TM * 16 - 1) / (TM * 16));
-  hipLaunchKernelGGL((gemm16_kernel<WN, TM, TN, PERCH, I32>), grid, dim3(64 * WN), 0, st, a);
+constexpr int kSkinnyKS = 4;  // waves per skinny block (K split)
+constexpr int kSkinnyPF = 4;  // weight groups in flight per wave
+
+template <int TM, int TN, bool PERCH, bool I32>
+hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
+  const dim3 grid((a.n_strips + TN - 1) / TN, (a.M + TM * 16 - 1) / (TM * 16));
+  hipLaunchKernelGGL((gemm_skinny_kernel<TM, TN, kSkinnyKS, kSkinnyPF, PERCH, I32>), grid, dim3(64 * kSkinnyKS), 0,
+                     st, a);
   return hipGetLastError();
 }
 
+// Strips per skinny block: the fewest rounds of 256 blocks (one per CU) times
+// strips per block; ties go to more strips per block (less activation traffic).
+inline int pick_skinny_tn(int n_strips) {
+  int best = 1;
+  long best_cost = -1;
+  for (int tn = 1; tn <= 8; ++tn) {
+    const long blocks = (n_strips + tn - 1) / tn;
+    const long cost = ((blocks + 255) / 256) * tn;
+    if (best_cost < 0 || cost <= best_cost) {
+      best = tn;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+template <int TM, bool PERCH, bool I32>
+hipError_t dispatch_skinny_tn(const GemmArgs& a, hipStream_t st) {
+  switch (pick_skinny_tn(a.n_strips)) {
+    case 1: return launch_skinny<TM, 1, PERCH, I32>(a, st);
+    case 2: return launch_skinny<TM, 2, PERCH, I32>(a, st);
+    case 3: return launch_skinny<TM, 3, PERCH, I32>(a, st);
+    case 4: return launch_skinny<TM, 4, PERCH, I32>(a, st);
+    case 5: return launch_skinny<TM, 5, PERCH, I32>(a, st);
+    case 6: return launch_skinny<TM, 6, PERCH, I32>(a, st);
+    case 7: return launch_skinny<TM, 7, PERCH, I32>(a, st);
+    default: return launch_skinny<TM, 8, PERCH, I32>(a, st);
+  }
+}
+
+// Large-M plans.  Tile 0: 256x256 blocks of 8 waves (each 128 x 64).
+// Tile 1: 128x128 blocks of 4 waves (each 64 x 64), for smaller problems.
+struct LargePlan {
+  int tile;    // 0 or 1
+  int ksplit;  // K splits
+};
+
+inline int64_t tiles_of(int64_t M, int64_t N_pad, int bm, int bn) { return ((M + bm - 1) / bm) * ((N_pad + bn - 1) / bn); }
+
+// Pick a tile and a K split so that a launch has roughly one workgroup per CU
+// or more; K splits keep at least 4 groups (512 channels) each.
+inline LargePlan plan_large(int64_t M, int64_t N, int64_t K) {
+  const int64_t N_pad = round_up(N, kStrip);
+  const int64_t G = K / kGroup;
+  LargePlan p{0, 1};
+  const int64_t big = tiles_of(M, N_pad, 256, 256);
+  if (big < 192) p.tile = 1;
+  const int64_t tiles = p.tile ? tiles_of(M, N_pad, 128, 128) : big;
+  while (tiles * p.ksplit < 256 && G / (2 * p.ksplit) >= 4) p.ksplit *= 2;
+  return p;
+}
+
+inline size_t workspace_bytes_of(int64_t M, int64_t N, int64_t K) {
+  if (M <= 64) return 0;
+  const LargePlan p = plan_large(M, N, K);
+  return p.ksplit > 1 ? size_t(p.ksplit) * size_t(M) * size_t(round_up(N, kStrip)) * sizeof(int) : 0;
+}
+
 template <int WM, int WN, int TM, int TN, bool PERCH, bool I32>
-hipError_t launch32(const GemmArgs& a, hipStream_t st) {
+hipError_t launch_large(const GemmArgs& a, hipStream_t st) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
-  const dim3 grid((a.n_strips * 16 + BN - 1) / BN, (a.M + BM - 1) / BM);
-  hipLaunchKernelGGL((gemm32_kernel<WM, WN, TM, TN, PERCH, I32>), grid, dim3(64 * WM * WN), 0, st, a);
+  const dim3 grid((a.n_strips * 16 + BN - 1) / BN, (a.M + BM - 1) / BM, a.ksplit);
+  hipLaunchKernelGGL((gemm_large_kernel<WM, WN, TM, TN, PERCH, I32>), grid, dim3(64 * WM * WN), 0, st, a);
   return hipGetLastError();
 }
 
 template <bool PERCH, bool I32>
-hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
-  if (a.M <= 16) return launch16<4, 1, 1, PERCH, I32>(a, st);
-  if (a.M <= 32) return launch16<4, 2, 1, PERCH, I32>(a, st);
-  if (a.M <= 64) return launch16<4, 4, 1, PERCH, I32>(a, st);
-  return launch32<2, 2, 2, 2, PERCH, I32>(a, st);
+hipError_t launch_large_tile(int tile, const GemmArgs& a, hipStream_t st) {
+  if (tile == 0) return launch_large<QOQ_LWM, QOQ_LWN, QOQ_LTM, QOQ_LTN, PERCH, I32>(a, st);
+  return launch_large<2, 2, 2, 2, PERCH, I32>(a, st);
+}
+
+template <bool PERCH, bool I32>
+hipError_t dispatch(const GemmArgs& a0, void* ws, hipStream_t st) {
+  if (a0.M <= 16) return dispatch_skinny_tn<1, PERCH, I32>(a0, st);
+  if (a0.M <= 32) return dispatch_skinny_tn<2, PERCH, I32>(a0, st);
+  if (a0.M <= 64) return dispatch_skinny_tn<4, PERCH, I32>(a0, st);
+  const LargePlan p = plan_large(a0.M, a0.N, int64_t(a0.G) * kGroup);
+  if (p.ksplit == 1) return launch_large_tile<PERCH, I32>(p.tile, a0, st);
+  // split K: INT32 partials into the workspace, then reduce + epilogue
+  GemmArgs a = a0;
+  a.ksplit = p.ksplit;
+  a.out = ws;
+  a.ldo = int64_t(a.n_strips) * kStrip;
+  a.zstride = int64_t(a.M) * a.ldo;
+  hipError_t e = launch_large_tile<PERCH, true>(p.tile, a, st);
+  if (e != hipSuccess) return e;
+  const int ldw = a.n_strips * kStrip;
+  const int64_t threads = int64_t(a.M) * (ldw / 4);
+  const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+  hipLaunchKernelGGL((splitk_reduce_kernel<I32>), grid, dim3(256), 0, st, static_cast<const int*>(ws), a.ksplit, a.M,
+                     a.N, ldw, a0.sx, a0.scale, a0.out, a0.ldo);
+  return hipGetLastError();
 }
 
 int run_gemm(const char* fn, const int8_t* x8, const void* sx, const void* qweight, const void* meta,
              const void* scale, void* out, int64_t M, int64_t N, int64_t K, int64_t ldo, int32_t group_size,
-             bool i32, hipStream_t st) {
+             void* workspace, size_t workspace_bytes, bool i32, hipStream_t st) {
   clear_error();
   if (!x8 || !qweight || !meta || !out || (!i32 && (!sx || !scale)))
     return fail(QOQ_ERR_INVALID_ARG, "%s: null pointer argument", fn);
@@ -377,7 +585,7 @@ int run_gemm(const char* fn, const int8_t* x8, const void* sx, const void* qweig
   GemmArgs a;
   a.x8 = x8;
   a.sx = static_cast<const unsigned short*>(sx);
-  a.qw = static_cast<const uint4*>(qweight);
+  a.qw = static_cast<const u32x4*>(qweight);
   a.meta = static_cast<const uint32_t*>(meta);
   a.meta8 = static_cast<const uint8_t*>(meta);
   a.scale = static_cast<const unsigned short*>(scale);
@@ -388,9 +596,17 @@ int run_gemm(const char* fn, const int8_t* x8, const void* sx, const void* qweig
   a.G4q = static_cast<int>(round_up(a.G, 4) / 4);
   a.n_strips = static_cast<int>(round_up(N, kStrip) / kStrip);
   a.ldo = ldo;
+  a.ksplit = 1;
+  a.zstride = 0;
+  const size_t need = workspace_bytes_of(M, N, K);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(QOQ_ERR_INVALID_ARG, "%s: workspace of %zu bytes required (got %zu); see qoq_w4a8_gemm_workspace_size",
+                fn, need, workspace ? workspace_bytes : size_t(0));
+  if (need && reinterpret_cast<uintptr_t>(workspace) % 16)
+    return fail(QOQ_ERR_ALIGNMENT, "%s: workspace must be 16-byte aligned", fn);
   hipError_t e;
-  if (group_size) e = i32 ? dispatch<false, true>(a, st) : dispatch<false, false>(a, st);
-  else e = i32 ? dispatch<true, true>(a, st) : dispatch<true, false>(a, st);
+  if (group_size) e = i32 ? dispatch<false, true>(a, workspace, st) : dispatch<false, false>(a, workspace, st);
+  else e = i32 ? dispatch<true, true>(a, workspace, st) : dispatch<true, false>(a, workspace, st);
   if (e != hipSuccess) return fail(QOQ_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return QOQ_OK;
 }
@@ -400,22 +616,26 @@ int run_gemm(const char* fn, const int8_t* x8, const void* sx, const void* qweig
 
 using namespace qoq;
 
-extern "C" size_t qoq_w4a8_gemm_workspace_size(int64_t, int64_t, int64_t, int32_t) { return 0; }
+extern "C" size_t qoq_w4a8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_size) {
+  if (M < 1 || check_weight_shape(N, K, group_size) != QOQ_OK) {
+    clear_error();
+    return 0;
+  }
+  return workspace_bytes_of(M, N, K);
+}
 
 extern "C" int qoq_w4a8_gemm(const int8_t* x8, const void* sx_fp16, const void* qweight, const void* meta,
                              const void* scale_fp16, void* y_fp16, int64_t M, int64_t N, int64_t K, int64_t ldy,
                              int32_t group_size, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
-  return run_gemm("qoq_w4a8_gemm", x8, sx_fp16, qweight, meta, scale_fp16, y_fp16, M, N, K, ldy, group_size, false,
+  return run_gemm("qoq_w4a8_gemm", x8, sx_fp16, qweight, meta, scale_fp16, y_fp16, M, N, K, ldy, group_size,
+                  workspace, workspace_bytes, false,
                   static_cast<hipStream_t>(stream));
 }
 
 extern "C" int qoq_w4a8_gemm_i32(const int8_t* x8, const void* qweight, const void* meta, int32_t* acc, int64_t M,
                                  int64_t N, int64_t K, int64_t ldacc, int32_t group_size, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
-  return run_gemm("qoq_w4a8_gemm_i32", x8, nullptr, qweight, meta, nullptr, acc, M, N, K, ldacc, group_size, true,
+  return run_gemm("qoq_w4a8_gemm_i32", x8, nullptr, qweight, meta, nullptr, acc, M, N, K, ldacc, group_size,
+                  workspace, workspace_bytes, true,
                   static_cast<hipStream_t>(stream));
 }
