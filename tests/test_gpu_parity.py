@@ -116,10 +116,14 @@ SMALL = [
     (257, 384, 300, 128),
     (5, 256, 48, 0),
     (70, 384, 100, 0),
-    (200, 2048, 96, 128),   # K split in 4 (INT32 partials + reduction)
+    (200, 2048, 96, 128),   # 128x128 tiles, K split in 4
     (97, 1920, 40, 128),    # K split in 2 with an odd group count per split
-    (100, 1024, 50, 0),     # per-channel with a K split
+    (256, 1024, 50, 0),     # per-channel with a K split
+    (300, 2048, 96, 128),   # large-M kernel, K split in 4 (INT32 partials + reduction)
+    (290, 1920, 40, 128),   # ... K split in 2 with an odd group count per split
+    (270, 1024, 50, 0),     # ... per-channel with a K split
     (300, 640, 520, 128),   # several 128x128 tiles, ragged M and N
+    (520, 512, 300, 128),   # 256x256 tiles (8 waves), ragged M and N
 ]
 
 

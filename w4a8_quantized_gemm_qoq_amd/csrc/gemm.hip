@@ -44,6 +44,14 @@
 #define QOQ_LTM 4
 #define QOQ_LTN 2
 #endif
+// Register-ring depth (groups of weights / activations in flight) of the big
+// and of the 128x128 large-M tile.
+#ifndef QOQ_LD
+#define QOQ_LD 2
+#endif
+#ifndef QOQ_SD
+#define QOQ_SD 4
+#endif
 
 namespace qoq {
 namespace {
@@ -84,9 +92,19 @@ __device__ __forceinline__ void meta_perchannel(uint32_t z, uint32_t& S, uint32_
 }
 
 // LDS tile of BM rows x 128 bytes; 16-byte chunk kc of row r lives at chunk
-// kc ^ (r & 7) so that 8 consecutive rows reading the same K chunk hit
-// different banks.
-__device__ __forceinline__ int lds_off(int row, int kc) { return row * 128 + ((kc ^ (row & 7)) << 4); }
+// kc ^ ((r >> 1) & 7).  A 128-byte row spans half of the 64 four-byte banks,
+// so rows of equal parity share a bank half; XOR-ing with r >> 1 spreads 16
+// consecutive rows reading the same K chunk over all 64 banks.
+__device__ __forceinline__ int lds_off(int row, int kc) { return row * 128 + ((kc ^ ((row >> 1) & 7)) << 4); }
+
+// Keeps prefetch loads where they are written: the empty asm with a memory
+// clobber stops IR passes from sinking loads toward their uses, and the
+// scheduling barrier stops the machine scheduler from doing the same.
+#define QOQ_COMPILER_FENCE()          \
+  do {                                \
+    asm volatile("" ::: "memory");    \
+    __builtin_amdgcn_sched_barrier(0); \
+  } while (0)
 
 struct GemmArgs {
   const int8_t* x8;
@@ -126,7 +144,7 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int row, int col, i
 // partial INT32 accumulators are summed exactly through LDS at the end.
 template <int TM, int TN, int KS, int PF, bool PERCH, bool I32OUT>
 __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
-  static_assert(PF % 2 == 0, "PF must be even (A operand ping-pong)");
+  static_assert(PF % 2 == 0, "PF must be even (activation ping-pong parity)");
   __shared__ int red[(KS > 1 ? KS - 1 : 1) * TM * 4 * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, j = lane >> 4;
@@ -153,71 +171,84 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
 
   // activation rows of this lane: m0 + 16i + c16, K chunk 16j (+64 for h = 1)
   const int8_t* arow[TM];
-  bool aval[TM];
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int row = m0 + i * 16 + c16;
-    aval[i] = row < a.M;
-    arow[i] = a.x8 + int64_t(aval[i] ? row : 0) * K + 16 * j;
+    arow[i] = a.x8 + int64_t(row < a.M ? row : 0) * K + 16 * j;
   }
 
   u32x4 bq[PF][TN];
   uint32_t mq[PF][TN];
   u32x4 aq[2][TM][2];
 
-  auto load_b = [&](int g, u32x4* b, uint32_t* m) {
+  auto load_b = [&](int g, u32x4 (&b)[TN], uint32_t (&m)[TN]) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
-      b[t] = a.qw[(int64_t(strip[t]) * a.G + g) * 64 + lane];
+      // weights are streamed once per call: non-temporal loads
+      b[t] = __builtin_nontemporal_load(a.qw + (int64_t(strip[t]) * a.G + g) * 64 + lane);
       if constexpr (!PERCH) m[t] = a.meta[(int64_t(strip[t]) * a.G4q + (g >> 2)) * 16 + c16];
     }
   };
-  auto load_a = [&](int g, u32x4 (*ar)[2]) {
+  // Rows past M read row 0 instead: output row m depends only on activation
+  // row m, and rows past M are never stored, so no zeroing (and no wait for
+  // a select) is needed and the loads stay branch-free.
+  auto load_a = [&](int g, u32x4 (&ar)[TM][2]) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        ar[i][h] = aval[i] ? *reinterpret_cast<const u32x4*>(arow[i] + int64_t(g) * 128 + 64 * h)
-                           : u32x4{0u, 0u, 0u, 0u};
+      for (int h = 0; h < 2; ++h) ar[i][h] = *reinterpret_cast<const u32x4*>(arow[i] + int64_t(g) * 128 + 64 * h);
     }
   };
 
+  auto compute = [&](int g, const u32x4 (&bc)[TN], const uint32_t (&mc)[TN], const u32x4 (&ac)[TM][2]) {
+    if constexpr (!PERCH) {
 #pragma unroll
-  for (int p = 0; p < PF; ++p)
-    if (g0 + p < g1) load_b(g0 + p, bq[p], mq[p]);
-  if (g0 < g1) load_a(g0, aq[0]);
+      for (int t = 0; t < TN; ++t) meta_g128((mc[t] >> (8 * (g & 3))) & 0xffu, S[t], C[t]);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const v4i bf = dequant16(h ? bc[t][2] : bc[t][0], h ? bc[t][3] : bc[t][1], S[t], C[t]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          acc[i][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, ac[i][h]), bf, acc[i][t], 0, 0, 0);
+      }
+    }
+  };
 
-  for (int gb = g0; gb < g1; gb += PF) {
+  const int ng = g1 - g0;
+  if (ng > 0) {
+    // prologue: weights of the first PF groups, activations of the first group
+#pragma unroll
+    for (int p = 0; p < PF; ++p) load_b(min(g0 + p, g1 - 1), bq[p], mq[p]);
+    load_a(g0, aq[0]);
+
+    // full rounds of PF groups.  Loads are unconditional (clamped at the last
+    // group) so a round is straight-line code.  Per group: issue the next
+    // group's activations, multiply out of ring slot u, then refill slot u
+    // with the weights PF groups ahead -- no register copies, so the only
+    // waits are for the data each MFMA consumes.
+    int it = 0;
+    for (; it + PF <= ng; it += PF) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        const int g = g0 + it + u;
+        load_a(min(g + 1, g1 - 1), aq[(u + 1) & 1]);
+        QOQ_COMPILER_FENCE();
+        compute(g, bq[u], mq[u], aq[u & 1]);
+        QOQ_COMPILER_FENCE();
+        load_b(min(g + PF, g1 - 1), bq[u], mq[u]);
+      }
+    }
+    // remaining ng % PF groups are already in flight in bq[0 .. rem)
+    const int rem = ng - it;
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
-      const int g = gb + u;
-      if (g < g1) {
-        u32x4 bc[TN];
-        uint32_t mc[TN];
-#pragma unroll
-        for (int t = 0; t < TN; ++t) {
-          bc[t] = bq[u][t];
-          mc[t] = mq[u][t];
-        }
-        if (g + PF < g1) load_b(g + PF, bq[u], mq[u]);
-        if (g + 1 < g1) load_a(g + 1, aq[(u + 1) & 1]);
-        if constexpr (!PERCH) {
-#pragma unroll
-          for (int t = 0; t < TN; ++t) meta_g128((mc[t] >> (8 * (g & 3))) & 0xffu, S[t], C[t]);
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-          for (int t = 0; t < TN; ++t) {
-            const v4i bf = dequant16(h ? bc[t][2] : bc[t][0], h ? bc[t][3] : bc[t][1], S[t], C[t]);
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-              const u32x4 av = aq[u & 1][i][h];
-              const v4i af = v4i{int(av[0]), int(av[1]), int(av[2]), int(av[3])};
-              acc[i][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf, acc[i][t], 0, 0, 0);
-            }
-          }
-        }
+      if (u < rem) {
+        const int g = g0 + it + u;
+        if (u + 1 < rem) load_a(g + 1, aq[(u + 1) & 1]);
+        compute(g, bq[u], mq[u], aq[u & 1]);
       }
     }
   }
@@ -334,10 +365,10 @@ __device__ __forceinline__ void large_group(v16i (&acc)[TM][TN], const int8_t* l
   }
 }
 
-#define QOQ_COMPILER_FENCE() asm volatile("" ::: "memory")
 
-template <int WM, int WN, int TM, int TN, bool PERCH, bool I32OUT>
+template <int WM, int WN, int TM, int TN, int D, bool PERCH, bool I32OUT>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
+  static_assert(D % 2 == 0, "ring depth must be even (LDS ping-pong parity)");
   constexpr int THREADS = 64 * WM * WN;
   constexpr int BM = WM * TM * 32;
   constexpr int BN = WN * TN * 32;
@@ -349,14 +380,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
   const int wm = wave / WN, wn = wave % WN;
   // Tile order.  Workgroups are dispatched round-robin over the 8 XCDs, each
   // with its own L2.  Remap so that each XCD gets a contiguous run of tiles,
-  // and walk tiles column-major so that the tiles resident on one XCD share
-  // the same packed weight columns (and neighbouring activation rows).
+  // and walk that run in bands of up to 8 row tiles, column by column, so the
+  // blocks resident on one XCD at a time cover a compact patch of the output
+  // and share both their activation rows and their packed weight columns.
   const int ny = gridDim.y;
   const int nb = gridDim.x * ny;
   int d = blockIdx.y * gridDim.x + blockIdx.x;
   if (d < (nb / 8) * 8) d = (d % 8) * (nb / 8) + d / 8;
-  const int m0 = (d % ny) * BM;
-  const int n0 = (d / ny) * BN + wn * TN * 32;  // first column of this wave
+  constexpr int kBand = 8;
+  const int band = d / (kBand * int(gridDim.x));
+  const int band_rows = min(kBand, ny - band * kBand);
+  const int in_band = d - band * kBand * int(gridDim.x);
+  const int m0 = (band * kBand + in_band % band_rows) * BM;
+  const int n0 = (in_band / band_rows) * BN + wn * TN * 32;  // first column of this wave
   const int64_t K = int64_t(a.G) * 128;
   const int c32 = lane & 31, hh = lane >> 5;
   const int c16 = c32 & 15;
@@ -383,35 +419,51 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][t][e] = 0;
 
-  u32x4 ra0[NA], ra1[NA];
-  u32x4 rb0[TN][2], rb1[TN][2];
-  uint32_t rm0[TN], rm1[TN];
+  // Register rings.  Weights: D slots, slot l % D holds the packed weights of
+  // group gb+l, refilled right after use, D groups ahead.  Activations: DA
+  // slots; at the start of step l the chunks of group gb+l+1 are written to
+  // the LDS buffer not being read (every wave passed the previous barrier),
+  // and the slot is refilled DA groups ahead.  LDS is double-buffered by
+  // group parity.
+  constexpr int DA = D / 2;
+  u32x4 ra[DA][NA];
+  u32x4 rb[D][TN][2];
+  uint32_t rm[D][TN];
+  const int n = ge - gb;
+  auto gcl = [&](int l) { return gb + min(l, n - 1); };
 
-  a_load<NA, THREADS>(ra0, a, K, m0, gb);
-  b_load<TN, PERCH>(rb0, rm0, a, strip, c16, hh, gb);
-  a_store<NA, THREADS>(ra0, As0);
+  a_load<NA, THREADS>(ra[0], a, K, m0, gb);
+  a_store<NA, THREADS>(ra[0], As0);
+#pragma unroll
+  for (int d = 1; d <= DA; ++d) a_load<NA, THREADS>(ra[d % DA], a, K, m0, gcl(d));
+#pragma unroll
+  for (int d = 0; d < D; ++d) b_load<TN, PERCH>(rb[d], rm[d], a, strip, c16, hh, gcl(d));
   __syncthreads();
 
-  // pairs of groups; every half issues the next group's loads before its MFMAs
-  int g = gb;
-  for (; g + 1 < ge; g += 2) {
-    a_load<NA, THREADS>(ra1, a, K, m0, g + 1);
-    b_load<TN, PERCH>(rb1, rm1, a, strip, c16, hh, g + 1);
-    QOQ_COMPILER_FENCE();
-    large_group<TM, TN, PERCH>(acc, As0, rb0, rm0, S, C, g, row0, c32, hh);
-    a_store<NA, THREADS>(ra1, As1);
-    __syncthreads();
-
-    const int gn = min(g + 2, ge - 1);
-    a_load<NA, THREADS>(ra0, a, K, m0, gn);
-    b_load<TN, PERCH>(rb0, rm0, a, strip, c16, hh, gn);
-    QOQ_COMPILER_FENCE();
-    large_group<TM, TN, PERCH>(acc, As1, rb1, rm1, S, C, g + 1, row0, c32, hh);
-    a_store<NA, THREADS>(ra0, As0);
-    __syncthreads();
+  int l0 = 0;
+  for (; l0 + D <= n; l0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int l = l0 + u;
+      a_store<NA, THREADS>(ra[(u + 1) % DA], (u & 1) ? As0 : As1);
+      a_load<NA, THREADS>(ra[(u + 1) % DA], a, K, m0, gcl(l + 1 + DA));
+      QOQ_COMPILER_FENCE();
+      large_group<TM, TN, PERCH>(acc, (u & 1) ? As1 : As0, rb[u], rm[u], S, C, gb + l, row0, c32, hh);
+      __syncthreads();
+      b_load<TN, PERCH>(rb[u], rm[u], a, strip, c16, hh, gcl(l + D));
+      QOQ_COMPILER_FENCE();
+    }
   }
-  if (g < ge)  // odd group count: the last group is already in (As0, rb0)
-    large_group<TM, TN, PERCH>(acc, As0, rb0, rm0, S, C, g, row0, c32, hh);
+  // the last n % D groups are already in the rings
+  const int rem = n - l0;
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    if (u < rem) {
+      if (u + 1 < rem) a_store<NA, THREADS>(ra[(u + 1) % DA], (u & 1) ? As0 : As1);
+      large_group<TM, TN, PERCH>(acc, (u & 1) ? As1 : As0, rb[u], rm[u], S, C, gb + l0 + u, row0, c32, hh);
+      __syncthreads();
+    }
+  }
 
   // epilogue: lane holds column lane%32 and rows 8*(r/4) + 4*(lane/32) + r%4
 #pragma unroll
@@ -464,24 +516,30 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const int* __restric
 // ---------------------------------------------------------------------------
 // Launch helpers.
 
-constexpr int kSkinnyKS = 4;  // waves per skinny block (K split)
+// Waves per skinny block (the K split): 8 for up to 16 rows (two waves per
+// SIMD keep more loads in flight), 4 for 32 or 64 rows (accumulators and
+// activation operands need the registers of a whole SIMD).
+constexpr int skinny_ks(int tm) { return tm == 1 ? 4 : 4; }
 constexpr int kSkinnyPF = 4;  // weight groups in flight per wave
 
 template <int TM, int TN, bool PERCH, bool I32>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
   const dim3 grid((a.n_strips + TN - 1) / TN, (a.M + TM * 16 - 1) / (TM * 16));
-  hipLaunchKernelGGL((gemm_skinny_kernel<TM, TN, kSkinnyKS, kSkinnyPF, PERCH, I32>), grid, dim3(64 * kSkinnyKS), 0,
-                     st, a);
+  constexpr int KS = skinny_ks(TM);
+  hipLaunchKernelGGL((gemm_skinny_kernel<TM, TN, KS, kSkinnyPF, PERCH, I32>), grid, dim3(64 * KS), 0, st, a);
   return hipGetLastError();
 }
 
 // Strips per skinny block: the fewest rounds of 256 blocks (one per CU) times
-// strips per block; ties go to more strips per block (less activation traffic).
-inline int pick_skinny_tn(int n_strips) {
-  int best = 1;
+// strips per block, for `ny` row tiles; ties go to more strips per block
+// (less activation traffic).
+inline int pick_skinny_tn(int n_strips, int ny, int tm) {
+  (void)tm;
+  const int lo = 1, hi = 8;
+  int best = lo;
   long best_cost = -1;
-  for (int tn = 1; tn <= 8; ++tn) {
-    const long blocks = (n_strips + tn - 1) / tn;
+  for (int tn = lo; tn <= hi; ++tn) {
+    const long blocks = long((n_strips + tn - 1) / tn) * ny;
     const long cost = ((blocks + 255) / 256) * tn;
     if (best_cost < 0 || cost <= best_cost) {
       best = tn;
@@ -493,7 +551,7 @@ inline int pick_skinny_tn(int n_strips) {
 
 template <int TM, bool PERCH, bool I32>
 hipError_t dispatch_skinny_tn(const GemmArgs& a, hipStream_t st) {
-  switch (pick_skinny_tn(a.n_strips)) {
+  switch (pick_skinny_tn(a.n_strips, (a.M + TM * 16 - 1) / (TM * 16), TM)) {
     case 1: return launch_skinny<TM, 1, PERCH, I32>(a, st);
     case 2: return launch_skinny<TM, 2, PERCH, I32>(a, st);
     case 3: return launch_skinny<TM, 3, PERCH, I32>(a, st);
@@ -527,31 +585,34 @@ inline LargePlan plan_large(int64_t M, int64_t N, int64_t K) {
   return p;
 }
 
+// Largest M served by the K-split skinny kernel (64-row tiles above 32 rows).
+constexpr int64_t kSkinnyMaxM = 64;
+
 inline size_t workspace_bytes_of(int64_t M, int64_t N, int64_t K) {
-  if (M <= 64) return 0;
+  if (M <= kSkinnyMaxM) return 0;
   const LargePlan p = plan_large(M, N, K);
   return p.ksplit > 1 ? size_t(p.ksplit) * size_t(M) * size_t(round_up(N, kStrip)) * sizeof(int) : 0;
 }
 
-template <int WM, int WN, int TM, int TN, bool PERCH, bool I32>
+template <int WM, int WN, int TM, int TN, int D, bool PERCH, bool I32>
 hipError_t launch_large(const GemmArgs& a, hipStream_t st) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   const dim3 grid((a.n_strips * 16 + BN - 1) / BN, (a.M + BM - 1) / BM, a.ksplit);
-  hipLaunchKernelGGL((gemm_large_kernel<WM, WN, TM, TN, PERCH, I32>), grid, dim3(64 * WM * WN), 0, st, a);
+  hipLaunchKernelGGL((gemm_large_kernel<WM, WN, TM, TN, D, PERCH, I32>), grid, dim3(64 * WM * WN), 0, st, a);
   return hipGetLastError();
 }
 
 template <bool PERCH, bool I32>
 hipError_t launch_large_tile(int tile, const GemmArgs& a, hipStream_t st) {
-  if (tile == 0) return launch_large<QOQ_LWM, QOQ_LWN, QOQ_LTM, QOQ_LTN, PERCH, I32>(a, st);
-  return launch_large<2, 2, 2, 2, PERCH, I32>(a, st);
+  if (tile == 0) return launch_large<QOQ_LWM, QOQ_LWN, QOQ_LTM, QOQ_LTN, QOQ_LD, PERCH, I32>(a, st);
+  return launch_large<2, 2, 2, 2, QOQ_SD, PERCH, I32>(a, st);
 }
 
 template <bool PERCH, bool I32>
 hipError_t dispatch(const GemmArgs& a0, void* ws, hipStream_t st) {
   if (a0.M <= 16) return dispatch_skinny_tn<1, PERCH, I32>(a0, st);
   if (a0.M <= 32) return dispatch_skinny_tn<2, PERCH, I32>(a0, st);
-  if (a0.M <= 64) return dispatch_skinny_tn<4, PERCH, I32>(a0, st);
+  if (a0.M <= kSkinnyMaxM) return dispatch_skinny_tn<4, PERCH, I32>(a0, st);
   const LargePlan p = plan_large(a0.M, a0.N, int64_t(a0.G) * kGroup);
   if (p.ksplit == 1) return launch_large_tile<PERCH, I32>(p.tile, a0, st);
   // split K: INT32 partials into the workspace, then reduce + epilogue
