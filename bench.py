@@ -71,18 +71,19 @@ def busy(torch, ms: float):
 
 
 def time_kernel(torch, launch, reps: int, sleep_ms: float = 20.0) -> float:
-    """Average duration (us) of one launch, from HIP events recorded on the
-    launch stream immediately before and after each launch; the launches are
-    queued behind a busy kernel so that host submission gaps do not count."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    """Average duration (us) of one launch: HIP events recorded on the launch
+    stream before and after `reps` back-to-back launches, all queued behind a
+    busy kernel so that host submission gaps do not count; divided by reps.
+    (Events around every single launch add about 2 us each on this stack.)"""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     busy(torch, sleep_ms)
+    e0.record()
     for i in range(reps):
-        evs[i][0].record()
         launch(i)
-        evs[i][1].record()
+    e1.record()
     torch.cuda.synchronize()
-    return 1e3 * sum(a.elapsed_time(b) for a, b in evs) / reps
+    return 1e3 * e0.elapsed_time(e1) / reps
 
 
 def cpu_baseline(w, X, W, seconds: float):
@@ -116,7 +117,7 @@ def measure_gemm(torch, q, w, X, W, reps: int):
     packed_host = q.qoq_pack_weights(W, w.group_size)
     wbytes = packed_host.qweight.nbytes + packed_host.meta.nbytes
     copies = 1 if bound_of(w) == "mfma" and w.M >= 1024 else max(1, math.ceil(3 * MALL_BYTES / max(wbytes, 1)))
-    copies = min(copies, 16)
+    copies = min(copies, 64)
     ws = [packed_host.to(dev) for _ in range(copies)]
     x = torch.from_numpy(np.ascontiguousarray(X)).to(dev)
     x8 = torch.empty((w.M, w.K), dtype=torch.int8, device=dev)
@@ -180,14 +181,20 @@ def main():
     packed = q.qoq_pack_weights(W, w.group_size)
     t_pack = time.perf_counter() - t_pack0
     p = packed.to(dev)
+    # Several copies of the packed weights, cycled from step to step, so that
+    # the weights come from HBM as they would for the distinct layers of a
+    # model (one copy would stay in the 256 MB last-level cache).
+    wbytes = packed.qweight.nbytes + packed.meta.nbytes
+    copies = max(1, min(64, math.ceil(3 * MALL_BYTES / max(1, wbytes))))
+    pw = [p] + [packed.to(dev) for _ in range(copies - 1)]
     x = torch.from_numpy(X).to(dev)
     x8 = torch.empty((w.M, w.K), dtype=torch.int8, device=dev)
     sx = torch.empty((w.M,), dtype=torch.float16, device=dev)
     y = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
 
-    def step():
+    def step(i=0):
         q.qoq_quant_act_per_token(x, x8, sx)
-        q.qoq_w4a8_gemm(x8, sx, p, y=y)
+        q.qoq_w4a8_gemm(x8, sx, pw[i % copies], y=y)
 
     # eager warmup, then capture the K timed steps in one HIP graph so that
     # host launch overhead does not enter the measurement
@@ -201,8 +208,8 @@ def main():
         step()
     torch.cuda.current_stream().wait_stream(s)
     with torch.cuda.graph(g):
-        for _ in range(args.steps):
-            step()
+        for i in range(args.steps):
+            step(i)
     g.replay()  # warm replay (untimed)
     torch.cuda.synchronize()
 
@@ -220,12 +227,14 @@ def main():
 
     # correctness of the timed output against a direct launch (same kernels)
     y_graph = y.clone()
-    step()
+    step(args.steps - 1)
     torch.cuda.synchronize()
     assert torch.equal(y_graph.view(torch.int16), y.view(torch.int16)), "graph replay output differs"
 
-    # dominant kernel: the GEMM; average launch duration from HIP events
-    gemm_us = time_kernel(torch, lambda i: q.qoq_w4a8_gemm(x8, sx, p, y=y), args.kernel_reps)
+    # dominant kernel: the GEMM; average launch duration from HIP events,
+    # with the same weight rotation as the timed steps
+    gemm_us = time_kernel(torch, lambda i: q.qoq_w4a8_gemm(x8, sx, pw[i % copies], y=y), args.kernel_reps)
+    ws_bytes = q.load_library().qoq_w4a8_gemm_workspace_size(w.M, w.N, w.K, w.group_size)
     quant_us = time_kernel(torch, lambda i: q.qoq_quant_act_per_token(x, x8, sx), args.kernel_reps)
     bnd = bound_of(w)
     if bnd == "mfma":
@@ -260,11 +269,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "desc": w.desc, "M": w.M, "K": w.K, "N": w.N,
                    "group_size": w.group_size, "step": "per-token INT8 quant + W4A8 GEMM (FP16 out)",
-                   "timing": "K steps captured in one HIP graph, replayed once between synchronizations"},
+                   "timing": "K steps captured in one HIP graph, replayed once between synchronizations",
+                   "weight_copies": copies},
         "gpu_ms_per_step": round(gpu_ms / args.steps, 5),
         "roofline": {"bound": bnd, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": "gemm (qoq_w4a8_gemm)", "kernel_us": round(gemm_us, 3), "per_unit": per_unit,
+                     "kernel": ("qoq_w4a8_gemm = gemm_large_kernel (K split) + splitk_reduce_kernel" if ws_bytes
+                                else "qoq_w4a8_gemm (one kernel)"),
+                     "kernel_us": round(gemm_us, 3), "per_unit": per_unit, "weight_copies": copies,
                      "algorithmic_bytes": algo_bytes(w), "ops": w.ops},
         "act_quant_us": round(quant_us, 3),
         "gemm_gbs_algorithmic": round(algo_bytes(w) / gemm_us / 1e3, 1),
