@@ -124,6 +124,11 @@ SMALL = [
     (270, 1024, 50, 0),     # ... per-channel with a K split
     (300, 640, 520, 128),   # several 128x128 tiles, ragged M and N
     (520, 512, 300, 128),   # 256x256 tiles (8 waves), ragged M and N
+    (16, 512, 9615, 128),   # strip kernel: 3 strips x 2 K parts per block, dead waves past N
+    (1, 256, 27990, 0),     # strip kernel: 7 strips per block, per-channel, ragged N
+    (12, 384, 200, 128),    # strip kernel: odd row count, K split in 8 with empty parts
+    (16, 10240, 40, 128),   # strip kernel: activations fill the whole 160 KB of LDS
+    (16, 10368, 40, 128),   # activations exceed LDS: K-split skinny kernel instead
 ]
 
 

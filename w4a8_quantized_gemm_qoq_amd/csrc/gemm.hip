@@ -62,6 +62,24 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 // lower to memcpy through scratch).
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
+// Raw buffer access.  A buffer descriptor bounds every load by its byte
+// count: a load whose offset lies past it returns zeros without a memory
+// access.  Prefetch rounds use that to stay straight-line at the end of a K
+// range: a load of a group past the range is issued with an offset beyond the
+// descriptor and costs no HBM traffic.
+constexpr int kBufDword3 = 0x00020000;    // raw 32-bit access, gfx9 family
+constexpr int kDeadOffset = 0x40000000;   // past any descriptor built here
+constexpr int kCacheStream = 2;           // nt: streamed once, do not keep in cache
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes, kBufDword3);
+}
+
+template <int AUX>
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+}
+
 __device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t c) {
   uint32_t d;
   asm("v_pk_mad_u16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
@@ -142,9 +160,9 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int row, int col, i
 // blocks), and streams its weights through a PF-deep register ring of 128-bit
 // loads so that enough bytes are in flight to cover HBM latency.  The KS
 // partial INT32 accumulators are summed exactly through LDS at the end.
-template <int TM, int TN, int KS, int PF, bool PERCH, bool I32OUT>
+template <int TM, int TN, int KS, int PF, int AD, bool PERCH, bool I32OUT>
 __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
-  static_assert(PF % 2 == 0, "PF must be even (activation ping-pong parity)");
+  static_assert(PF % AD == 0, "the activation ring must tile the weight ring");
   __shared__ int red[(KS > 1 ? KS - 1 : 1) * TM * 4 * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, j = lane >> 4;
@@ -179,14 +197,22 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
 
   u32x4 bq[PF][TN];
   uint32_t mq[PF][TN];
-  u32x4 aq[2][TM][2];
+  u32x4 aq[AD][TM][2];
 
+  // The block's strips are contiguous in the packed weights: one descriptor
+  // covers exactly the valid ones, so strips past N and groups past this
+  // wave's K range load zeros without touching memory.
+  const int strip_bytes = a.G * 1024;
+  const __amdgpu_buffer_rsrc_t wrs =
+      make_rsrc(a.qw + int64_t(sbase) * a.G * 64, min(TN, a.n_strips - sbase) * strip_bytes);
   auto load_b = [&](int g, u32x4 (&b)[TN], uint32_t (&m)[TN]) {
+    const int gofs = g < g1 ? g * 1024 : kDeadOffset;
+    const int gm = min(g, g1 - 1);
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       // weights are streamed once per call: non-temporal loads
-      b[t] = __builtin_nontemporal_load(a.qw + (int64_t(strip[t]) * a.G + g) * 64 + lane);
-      if constexpr (!PERCH) m[t] = a.meta[(int64_t(strip[t]) * a.G4q + (g >> 2)) * 16 + c16];
+      b[t] = buf_load16<kCacheStream>(wrs, lane * 16 + t * strip_bytes + gofs);
+      if constexpr (!PERCH) m[t] = a.meta[(int64_t(strip[t]) * a.G4q + (gm >> 2)) * 16 + c16];
     }
   };
   // Rows past M read row 0 instead: output row m depends only on activation
@@ -219,36 +245,40 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
 
   const int ng = g1 - g0;
   if (ng > 0) {
-    // prologue: weights of the first PF groups, activations of the first group
+    // prologue: weights of the first PF groups, activations of the first AD
 #pragma unroll
-    for (int p = 0; p < PF; ++p) load_b(min(g0 + p, g1 - 1), bq[p], mq[p]);
-    load_a(g0, aq[0]);
+    for (int p = 0; p < PF; ++p) load_b(g0 + p, bq[p], mq[p]);
+#pragma unroll
+    for (int p = 0; p < AD; ++p) load_a(min(g0 + p, g1 - 1), aq[p]);
 
-    // full rounds of PF groups.  Loads are unconditional (clamped at the last
-    // group) so a round is straight-line code.  Per group: issue the next
-    // group's activations, multiply out of ring slot u, then refill slot u
-    // with the weights PF groups ahead -- no register copies, so the only
-    // waits are for the data each MFMA consumes.
+    // full rounds of PF groups.  Loads are unconditional (weights past the
+    // range read zeros for free, activations clamp to the last group) so a
+    // round is straight-line code.  Per group: multiply out of ring slot u,
+    // then refill it with the weights PF groups ahead and the activations AD
+    // groups ahead -- no register copies.  Loads retire in issue order, so
+    // the activation lookahead AD also bounds how far ahead the weight loads
+    // effectively run.
     int it = 0;
     for (; it + PF <= ng; it += PF) {
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
         const int g = g0 + it + u;
-        load_a(min(g + 1, g1 - 1), aq[(u + 1) & 1]);
+        compute(g, bq[u], mq[u], aq[u % AD]);
         QOQ_COMPILER_FENCE();
-        compute(g, bq[u], mq[u], aq[u & 1]);
+        load_b(g + PF, bq[u], mq[u]);
+        load_a(min(g + AD, g1 - 1), aq[u % AD]);
         QOQ_COMPILER_FENCE();
-        load_b(min(g + PF, g1 - 1), bq[u], mq[u]);
       }
     }
-    // remaining ng % PF groups are already in flight in bq[0 .. rem)
+    // remaining ng % PF groups: weights are in bq[0 .. rem), activations of
+    // the first AD of them in the activation ring
     const int rem = ng - it;
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
       if (u < rem) {
         const int g = g0 + it + u;
-        if (u + 1 < rem) load_a(g + 1, aq[(u + 1) & 1]);
-        compute(g, bq[u], mq[u], aq[u & 1]);
+        compute(g, bq[u], mq[u], aq[u % AD]);
+        if (u + AD < rem) load_a(g + AD, aq[u % AD]);
       }
     }
   }
@@ -290,6 +320,153 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
         if (sbase + t < a.n_strips) store_out<I32OUT>(a, row, (sbase + t) * 16 + c16, acc[i][t][r], sxr);
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// strip: up to 16 rows (decode, memory-bound).  Every wave streams one
+// 16-channel strip over its K range -- the strip's packed bytes are one
+// contiguous run, and HBM serves a few long runs far better than many short
+// interleaved ones -- with PF groups of 128-bit loads in flight.  The INT8
+// activations of the block's rows (at most 16 x K bytes) are copied into LDS
+// once, with direct-to-LDS loads issued before the weight stream starts, and
+// every wave reads its MFMA A operand from there.  The weights are then the
+// only global loads of the main loop: global loads retire in issue order, so
+// any other global load would hold the weight stream back.  A block is `spb`
+// strips x `ks` K parts; the parts are summed exactly through LDS at the end.
+//
+// LDS activation layout: [group][row][128 B], 16-byte chunk q of LDS row
+// L = g*R + r stored at chunk q ^ ((L >> 1) & 7) (16 rows reading the same
+// chunk hit all 64 banks).
+__device__ __forceinline__ int round_up_lds(int bytes) { return (bytes + 1023) & ~1023; }
+__device__ __forceinline__ int strip_lds_off(int lrow, int q) { return lrow * 128 + ((q ^ ((lrow >> 1) & 7)) << 4); }
+
+// s_waitcnt immediates (gfx9 encoding): wait until at most n vector-memory
+// operations of this wave are outstanding, leaving the other counters free.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <int PF, bool PERCH, bool I32OUT>
+__global__ __launch_bounds__(512) void gemm_strip_kernel(GemmArgs a, int spb, int ks) {
+  extern __shared__ __align__(16) int8_t smem[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int nwaves = blockDim.x >> 6;
+  const int ws = wave / ks, wk = wave - ws * ks;
+  const int sb = blockIdx.x * spb;
+  const int strip = sb + ws;
+  const bool live = strip < a.n_strips;
+  const int cstrip = min(strip, a.n_strips - 1);
+  const int c16 = lane & 15, j = lane >> 4;
+  const int64_t K = int64_t(a.G) * 128;
+  const int R = min(a.M, 16);
+  const int g0 = (a.G * wk) / ks, g1 = (a.G * (wk + 1)) / ks, ng = g1 - g0;
+
+  uint32_t S = 0, C = 0;
+  if constexpr (PERCH) meta_perchannel(a.meta8[cstrip * 16 + c16], S, C);
+
+  // activations -> LDS.  Lane l of a wave-wide copy fills LDS chunk base + l;
+  // lanes past the end fetch a valid chunk into the allocation's padding.
+  const int n_chunks = a.G * R * 8;
+  for (int base = wave * 64; base < n_chunks; base += nwaves * 64) {
+    const int pc = min(base + lane, n_chunks - 1);
+    const int lrow = pc >> 3;
+    const int q = (pc & 7) ^ ((lrow >> 1) & 7);
+    const int g = lrow / R, r = lrow - g * R;
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(a.x8 + int64_t(r) * K + int64_t(g) * 128 + q * 16),
+                                     (__attribute__((address_space(3))) void*)(smem + base * 16), 16, 0, 0);
+  }
+  // group metadata of the block's strips -> LDS, after the activations (the
+  // strips' metadata is one contiguous run of G4q * 64 bytes per strip)
+  const int act_bytes = round_up_lds(n_chunks * 16);
+  if constexpr (!PERCH) {
+    const int m_chunks = min(spb, a.n_strips - sb) * a.G4q * 4;
+    const int8_t* msrc = reinterpret_cast<const int8_t*>(a.meta) + int64_t(sb) * a.G4q * 64;
+    for (int base = wave * 64; base < m_chunks; base += nwaves * 64) {
+      const int pc = min(base + lane, m_chunks - 1);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(msrc + pc * 16),
+                                       (__attribute__((address_space(3))) void*)(smem + act_bytes + base * 16), 16, 0, 0);
+    }
+  }
+  const uint32_t* lmeta = reinterpret_cast<const uint32_t*>(smem + act_bytes) + ws * a.G4q * 16 + c16;
+
+  // weights: one descriptor over this wave's strip (empty past N), PF groups
+  // in flight from here on
+  const int strip_bytes = a.G * 1024;
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(a.qw + int64_t(cstrip) * a.G * 64, live ? strip_bytes : 0);
+  u32x4 bq[PF];
+  auto load_b = [&](int g, u32x4& b) { b = buf_load16<kCacheStream>(wrs, lane * 16 + (g < g1 ? g * 1024 : kDeadOffset)); };
+  // Wait for this wave's direct-to-LDS copies only (they were issued before
+  // the weight loads, and loads retire in order), then meet the other waves.
+  // A plain __syncthreads would also wait for the PF weight loads and drain
+  // the HBM stream once before the first multiply.  The prologue is
+  // unconditional (a wave with an empty K range loads zeros for free) so the
+  // main loop is entered on a single path.
+#pragma unroll
+  for (int p = 0; p < PF; ++p) load_b(g0 + p, bq[p]);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(PF));
+  __builtin_amdgcn_s_barrier();
+  QOQ_COMPILER_FENCE();
+
+  const int ra = c16 < R ? c16 : 0;  // rows past M reuse row 0; they are never stored
+  v4i acc = {0, 0, 0, 0};
+  auto compute = [&](int g, const u32x4& bc) {
+    if constexpr (!PERCH) meta_g128((lmeta[(g >> 2) * 16] >> (8 * (g & 3))) & 0xffu, S, C);
+    const int lrow = g * R + ra;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const v4i af = *reinterpret_cast<const v4i*>(smem + strip_lds_off(lrow, j + 4 * h));
+      const v4i bf = dequant16(h ? bc[2] : bc[0], h ? bc[3] : bc[1], S, C);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf, acc, 0, 0, 0);
+    }
+  };
+  auto round = [&](int it) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int g = g0 + it + u;
+      compute(g, bq[u]);
+      QOQ_COMPILER_FENCE();
+      load_b(g + PF, bq[u]);
+      QOQ_COMPILER_FENCE();
+    }
+  };
+  // The first round is peeled: the loop is then entered in the same state as
+  // its back edge (PF weight loads in flight, nothing else), which lets the
+  // compiler wait for one group at a time instead of draining every round.
+  int it = 0;
+  if (ng >= PF) {
+    round(0);
+    for (it = PF; it + PF <= ng; it += PF) round(it);
+  }
+  const int rem = ng - it;
+#pragma unroll
+  for (int u = 0; u < PF; ++u) {
+    if (u < rem) compute(g0 + it + u, bq[u]);
+  }
+
+  // exact sum of the K parts (the activations in LDS are no longer needed)
+  if (ks > 1) {
+    __syncthreads();
+    int* red = reinterpret_cast<int*>(smem);
+    if (wk > 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[((ws * (ks - 1) + wk - 1) * 4 + r) * 64 + lane] = acc[r];
+    }
+    __syncthreads();
+    if (wk == 0) {
+      for (int w = 1; w < ks; ++w)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] += red[((ws * (ks - 1) + w - 1) * 4 + r) * 64 + lane];
+    }
+  }
+  if (wk != 0 || !live) return;
+
+  // epilogue: lane holds rows 4*(lane/16)+r, column lane%16 of the strip
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * j + r;
+    float sxr = 0.0f;
+    if constexpr (!I32OUT) sxr = row < a.M ? __half2float(__ushort_as_half(a.sx[row])) : 0.0f;
+    store_out<I32OUT>(a, row, strip * 16 + c16, acc[r], sxr);
   }
 }
 
@@ -516,25 +693,36 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const int* __restric
 // ---------------------------------------------------------------------------
 // Launch helpers.
 
-// Waves per skinny block (the K split): 8 for up to 16 rows (two waves per
-// SIMD keep more loads in flight), 4 for 32 or 64 rows (accumulators and
-// activation operands need the registers of a whole SIMD).
-constexpr int skinny_ks(int tm) { return tm == 1 ? 4 : 4; }
-constexpr int kSkinnyPF = 4;  // weight groups in flight per wave
+// Skinny launch shapes.  HBM streams best as few long contiguous runs: for
+// up to 16 rows every wave reads one 16-channel strip front to back (its
+// packed bytes are contiguous), with PF groups in flight and the activations
+// on a ring of the same depth.  K is split over the waves of a block only when
+// there are too few strips to give every CU several waves.  For 32 or 64 rows
+// the activation operand is larger than the weights it multiplies, so a wave
+// covers TN strips with one activation load and the K range is split over 4
+// waves.
+#ifndef QOQ_S1PF
+#define QOQ_S1PF 4
+#endif
+#ifndef QOQ_SKS4
+#define QOQ_SKS4 4
+#endif
+#ifndef QOQ_SPF
+#define QOQ_SPF 4
+#endif
+constexpr int kStripWavesTarget = 1024;  // 4 waves per CU
 
-template <int TM, int TN, bool PERCH, bool I32>
+template <int TM, int TN, int KS, int PF, int AD, bool PERCH, bool I32>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
   const dim3 grid((a.n_strips + TN - 1) / TN, (a.M + TM * 16 - 1) / (TM * 16));
-  constexpr int KS = skinny_ks(TM);
-  hipLaunchKernelGGL((gemm_skinny_kernel<TM, TN, KS, kSkinnyPF, PERCH, I32>), grid, dim3(64 * KS), 0, st, a);
+  hipLaunchKernelGGL((gemm_skinny_kernel<TM, TN, KS, PF, AD, PERCH, I32>), grid, dim3(64 * KS), 0, st, a);
   return hipGetLastError();
 }
 
 // Strips per skinny block: the fewest rounds of 256 blocks (one per CU) times
 // strips per block, for `ny` row tiles; ties go to more strips per block
 // (less activation traffic).
-inline int pick_skinny_tn(int n_strips, int ny, int tm) {
-  (void)tm;
+inline int pick_skinny_tn(int n_strips, int ny) {
   const int lo = 1, hi = 8;
   int best = lo;
   long best_cost = -1;
@@ -551,17 +739,57 @@ inline int pick_skinny_tn(int n_strips, int ny, int tm) {
 
 template <int TM, bool PERCH, bool I32>
 hipError_t dispatch_skinny_tn(const GemmArgs& a, hipStream_t st) {
-  switch (pick_skinny_tn(a.n_strips, (a.M + TM * 16 - 1) / (TM * 16), TM)) {
-    case 1: return launch_skinny<TM, 1, PERCH, I32>(a, st);
-    case 2: return launch_skinny<TM, 2, PERCH, I32>(a, st);
-    case 3: return launch_skinny<TM, 3, PERCH, I32>(a, st);
-    case 4: return launch_skinny<TM, 4, PERCH, I32>(a, st);
-    case 5: return launch_skinny<TM, 5, PERCH, I32>(a, st);
-    case 6: return launch_skinny<TM, 6, PERCH, I32>(a, st);
-    case 7: return launch_skinny<TM, 7, PERCH, I32>(a, st);
-    default: return launch_skinny<TM, 8, PERCH, I32>(a, st);
+  constexpr int KS = QOQ_SKS4, PF = QOQ_SPF, AD = 2;
+  switch (pick_skinny_tn(a.n_strips, (a.M + TM * 16 - 1) / (TM * 16))) {
+    case 1: return launch_skinny<TM, 1, KS, PF, AD, PERCH, I32>(a, st);
+    case 2: return launch_skinny<TM, 2, KS, PF, AD, PERCH, I32>(a, st);
+    case 3: return launch_skinny<TM, 3, KS, PF, AD, PERCH, I32>(a, st);
+    case 4: return launch_skinny<TM, 4, KS, PF, AD, PERCH, I32>(a, st);
+    case 5: return launch_skinny<TM, 5, KS, PF, AD, PERCH, I32>(a, st);
+    case 6: return launch_skinny<TM, 6, KS, PF, AD, PERCH, I32>(a, st);
+    case 7: return launch_skinny<TM, 7, KS, PF, AD, PERCH, I32>(a, st);
+    default: return launch_skinny<TM, 8, KS, PF, AD, PERCH, I32>(a, st);
   }
 }
+
+// Dynamic LDS of the strip kernel: the activations, or the K-part partial
+// sums, whichever is larger.
+inline size_t strip_lds_bytes(int G, int R, int spb, int ks, bool perch) {
+  const size_t act = size_t(round_up(int64_t(G) * R * 8 * 16, 1024));
+  const size_t meta = perch ? 0 : size_t(round_up(int64_t(spb) * round_up(G, 4) / 4 * 64, 1024));
+  const size_t red = size_t(spb) * size_t(ks - 1) * 1024;
+  return act + meta > red ? act + meta : red;
+}
+constexpr size_t kStripMaxLds = 160 * 1024;
+
+template <bool PERCH, bool I32>
+hipError_t launch_strip(const GemmArgs& a, int spb, int ks, size_t lds, hipStream_t st) {
+  constexpr int PF = QOQ_S1PF;
+  auto* fn = gemm_strip_kernel<PF, PERCH, I32>;
+  if (lds > 64 * 1024) {
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(kStripMaxLds));
+    if (attr != hipSuccess) return attr;
+  }
+  const dim3 grid((a.n_strips + spb - 1) / spb);
+  hipLaunchKernelGGL(fn, grid, dim3(64 * spb * ks), lds, st, a, spb, ks);
+  return hipGetLastError();
+}
+
+// Up to 16 rows: the strip kernel when the activations fit in LDS, else the
+// K-split skinny kernel.  Strips per block as for the skinny kernel (rounds of
+// 256 blocks); the K split fills a block up to 8 waves.
+template <bool PERCH, bool I32>
+hipError_t dispatch_skinny_strip(const GemmArgs& a, hipStream_t st) {
+  const int R = a.M < 16 ? a.M : 16;
+  const int spb = pick_skinny_tn(a.n_strips, 1);
+  int ks = 8 / spb;
+  if (ks < 1) ks = 1;
+  const size_t lds = strip_lds_bytes(a.G, R, spb, ks, PERCH);
+  if (lds <= kStripMaxLds) return launch_strip<PERCH, I32>(a, spb, ks, lds, st);
+  return dispatch_skinny_tn<1, PERCH, I32>(a, st);
+}
+
 
 // Large-M plans.  Tile 0: 256x256 blocks of 8 waves (each 128 x 64).
 // Tile 1: 128x128 blocks of 4 waves (each 64 x 64), for smaller problems.
@@ -610,7 +838,7 @@ hipError_t launch_large_tile(int tile, const GemmArgs& a, hipStream_t st) {
 
 template <bool PERCH, bool I32>
 hipError_t dispatch(const GemmArgs& a0, void* ws, hipStream_t st) {
-  if (a0.M <= 16) return dispatch_skinny_tn<1, PERCH, I32>(a0, st);
+  if (a0.M <= 16) return dispatch_skinny_strip<PERCH, I32>(a0, st);
   if (a0.M <= 32) return dispatch_skinny_tn<2, PERCH, I32>(a0, st);
   if (a0.M <= kSkinnyMaxM) return dispatch_skinny_tn<4, PERCH, I32>(a0, st);
   const LargePlan p = plan_large(a0.M, a0.N, int64_t(a0.G) * kGroup);
