@@ -129,6 +129,8 @@ SMALL = [
     (12, 384, 200, 128),    # strip kernel: odd row count, K split in 8 with empty parts
     (16, 10240, 40, 128),   # strip kernel: activations fill the whole 160 KB of LDS
     (16, 10368, 40, 128),   # activations exceed LDS: K-split skinny kernel instead
+    (16, 2048, 20000, 128), # strip kernel, 5 strips per block: second activation copy after the barrier
+    (7, 1664, 17000, 0),    # ... per-channel, odd row count, copies running into padding
 ]
 
 
