@@ -35,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
+#include <algorithm>
+
 #include "qoq_internal.h"
 
 // Large-M tile: WM x WN waves, each TM x TN tiles of 32x32.
@@ -52,6 +54,26 @@
 #ifndef QOQ_SD
 #define QOQ_SD 4
 #endif
+#ifndef QOQ_LDA
+#define QOQ_LDA 2
+#endif
+#ifndef QOQ_SDA
+#define QOQ_SDA 2
+#endif
+// 128x128 tile: WM x WN waves, each TM x TN tiles of 32x32
+#ifndef QOQ_SWM
+#define QOQ_SWM 2
+#endif
+#ifndef QOQ_SWN
+#define QOQ_SWN 4
+#endif
+#ifndef QOQ_STM
+#define QOQ_STM 2
+#endif
+#ifndef QOQ_STN
+#define QOQ_STN 1
+#endif
+static_assert(QOQ_SWM * QOQ_STM * 32 == 128 && QOQ_SWN * QOQ_STN * 32 == 128, "the small large-M tile is 128x128");
 
 namespace qoq {
 namespace {
@@ -543,9 +565,10 @@ __device__ __forceinline__ void large_group(v16i (&acc)[TM][TN], const int8_t* l
 }
 
 
-template <int WM, int WN, int TM, int TN, int D, bool PERCH, bool I32OUT>
+template <int WM, int WN, int TM, int TN, int D, int DA, bool PERCH, bool I32OUT>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
   static_assert(D % 2 == 0, "ring depth must be even (LDS ping-pong parity)");
+  static_assert(D % DA == 0, "the activation ring must tile the weight ring");
   constexpr int THREADS = 64 * WM * WN;
   constexpr int BM = WM * TM * 32;
   constexpr int BN = WN * TN * 32;
@@ -601,8 +624,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
   // slots; at the start of step l the chunks of group gb+l+1 are written to
   // the LDS buffer not being read (every wave passed the previous barrier),
   // and the slot is refilled DA groups ahead.  LDS is double-buffered by
-  // group parity.
-  constexpr int DA = D / 2;
+  // group parity.  Loads retire in issue order, so a step waits for the
+  // activations loaded DA steps earlier: DA steps of work must cover the
+  // load latency.
   u32x4 ra[DA][NA];
   u32x4 rb[D][TN][2];
   uint32_t rm[D][TN];
@@ -737,10 +761,16 @@ inline int pick_skinny_tn(int n_strips, int ny) {
   return best;
 }
 
+#ifndef QOQ_SAD
+#define QOQ_SAD 2
+#endif
+#ifndef QOQ_STN_MAX
+#define QOQ_STN_MAX 8
+#endif
 template <int TM, bool PERCH, bool I32>
 hipError_t dispatch_skinny_tn(const GemmArgs& a, hipStream_t st) {
-  constexpr int KS = QOQ_SKS4, PF = QOQ_SPF, AD = 2;
-  switch (pick_skinny_tn(a.n_strips, (a.M + TM * 16 - 1) / (TM * 16))) {
+  constexpr int KS = QOQ_SKS4, PF = QOQ_SPF, AD = QOQ_SAD;
+  switch (std::min(QOQ_STN_MAX, pick_skinny_tn(a.n_strips, (a.M + TM * 16 - 1) / (TM * 16)))) {
     case 1: return launch_skinny<TM, 1, KS, PF, AD, PERCH, I32>(a, st);
     case 2: return launch_skinny<TM, 2, KS, PF, AD, PERCH, I32>(a, st);
     case 3: return launch_skinny<TM, 3, KS, PF, AD, PERCH, I32>(a, st);
@@ -814,7 +844,10 @@ inline LargePlan plan_large(int64_t M, int64_t N, int64_t K) {
 }
 
 // Largest M served by the K-split skinny kernel (64-row tiles above 32 rows).
-constexpr int64_t kSkinnyMaxM = 64;
+#ifndef QOQ_SKINNY_MAXM
+#define QOQ_SKINNY_MAXM 64
+#endif
+constexpr int64_t kSkinnyMaxM = QOQ_SKINNY_MAXM;
 
 inline size_t workspace_bytes_of(int64_t M, int64_t N, int64_t K) {
   if (M <= kSkinnyMaxM) return 0;
@@ -822,18 +855,18 @@ inline size_t workspace_bytes_of(int64_t M, int64_t N, int64_t K) {
   return p.ksplit > 1 ? size_t(p.ksplit) * size_t(M) * size_t(round_up(N, kStrip)) * sizeof(int) : 0;
 }
 
-template <int WM, int WN, int TM, int TN, int D, bool PERCH, bool I32>
+template <int WM, int WN, int TM, int TN, int D, int DA, bool PERCH, bool I32>
 hipError_t launch_large(const GemmArgs& a, hipStream_t st) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   const dim3 grid((a.n_strips * 16 + BN - 1) / BN, (a.M + BM - 1) / BM, a.ksplit);
-  hipLaunchKernelGGL((gemm_large_kernel<WM, WN, TM, TN, D, PERCH, I32>), grid, dim3(64 * WM * WN), 0, st, a);
+  hipLaunchKernelGGL((gemm_large_kernel<WM, WN, TM, TN, D, DA, PERCH, I32>), grid, dim3(64 * WM * WN), 0, st, a);
   return hipGetLastError();
 }
 
 template <bool PERCH, bool I32>
 hipError_t launch_large_tile(int tile, const GemmArgs& a, hipStream_t st) {
-  if (tile == 0) return launch_large<QOQ_LWM, QOQ_LWN, QOQ_LTM, QOQ_LTN, QOQ_LD, PERCH, I32>(a, st);
-  return launch_large<2, 2, 2, 2, QOQ_SD, PERCH, I32>(a, st);
+  if (tile == 0) return launch_large<QOQ_LWM, QOQ_LWN, QOQ_LTM, QOQ_LTN, QOQ_LD, QOQ_LDA, PERCH, I32>(a, st);
+  return launch_large<QOQ_SWM, QOQ_SWN, QOQ_STM, QOQ_STN, QOQ_SD, QOQ_SDA, PERCH, I32>(a, st);
 }
 
 template <bool PERCH, bool I32>
