@@ -55,10 +55,15 @@ def bound_of(w) -> str:
 
 
 def src_hash() -> str:
+    """Hash of the kernel sources' code (line comments and blank lines dropped),
+    so that a stored traffic measurement goes stale only when code changes."""
     h = hashlib.sha256()
     for f in ("gemm.hip", "act_quant.hip"):
-        with open(os.path.join(ROOT, "w4a8_quantized_gemm_qoq_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "w4a8_quantized_gemm_qoq_amd", "csrc", f), encoding="utf-8") as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -22,15 +22,16 @@
 // turns the biased byte into the two's-complement INT8 w8.  For the
 // per-channel variant s1 = 1 and c = 128 - z.
 //
-// Two kernels share the packed layout (see qoq.h):
+// Three kernels share the packed layout (see qoq.h):
+//   strip:  v_mfma_i32_16x16x64_i8, up to 16 rows; one contiguous weight
+//           strip per wave, activations copied into LDS once (decode).
 //   skinny: v_mfma_i32_16x16x64_i8, 16-row M tiles, K split across the
-//           waves of a block; for M <= 64 (decode, memory-bound).
-//   gemm32: v_mfma_i32_32x32x32_i8, 32x32 tiles; for M > 64 (prefill).
-// The activation tile of each 128-wide K group is staged in LDS (XOR-swizzled
-// 16-byte chunks, double-buffered); weights go global -> VGPR directly and are
-// prefetched a group ahead.  Both MFMA operands use the same K order per
-// (lane group, byte), so the contraction is exact whatever order the matrix
-// unit walks K in.
+//           waves of a block; up to 64 rows (decode, memory-bound).
+//   large:  v_mfma_i32_32x32x32_i8, 128x128 or 256x256 block tiles, K
+//           optionally split across blocks; above 64 rows (prefill).
+// Weights always go global -> VGPR directly and are dequantized in
+// registers.  Both MFMA operands use the same K order per (lane group, byte),
+// so the contraction is exact whatever order the matrix unit walks K in.
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
@@ -56,6 +57,9 @@
 #endif
 #ifndef QOQ_LDA
 #define QOQ_LDA 2
+#endif
+#ifndef QOQ_AF_PIN
+#define QOQ_AF_PIN 0
 #endif
 #ifndef QOQ_SDA
 #define QOQ_SDA 2
@@ -549,17 +553,28 @@ __device__ __forceinline__ void large_group(v16i (&acc)[TM][TN], const int8_t* l
 #pragma unroll
     for (int t = 0; t < TN; ++t) meta_g128((m[t] >> (8 * (g & 3))) & 0xffu, S[t], C[t]);
   }
+  // A fragments are double-buffered across the 4 K steps: the reads of step
+  // s+1 are issued before the multiplies of step s, so LDS latency hides
+  // behind them.
+  v4i af[2][TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) af[0][i] = *reinterpret_cast<const v4i*>(lds + lds_off(row0 + i * 32 + c32, hh));
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    v4i af[TM];
+    if (s + 1 < 4) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const v4i*>(lds + lds_off(row0 + i * 32 + c32, 2 * s + hh));
+      for (int i = 0; i < TM; ++i)
+        af[(s + 1) & 1][i] = *reinterpret_cast<const v4i*>(lds + lds_off(row0 + i * 32 + c32, 2 * (s + 1) + hh));
+    }
+#if QOQ_AF_PIN
+    __builtin_amdgcn_sched_barrier(0);
+#endif
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       const u32x4& q = b[t][s & 1];
       const v4i bf = dequant16((s >> 1) ? q[2] : q[0], (s >> 1) ? q[3] : q[1], S[t], C[t]);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf, acc[i][t], 0, 0, 0);
+      for (int i = 0; i < TM; ++i) acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[s & 1][i], bf, acc[i][t], 0, 0, 0);
     }
   }
 }
