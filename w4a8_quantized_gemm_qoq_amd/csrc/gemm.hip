@@ -165,13 +165,22 @@ struct GemmArgs {
   int64_t zstride;   // element offset between the partials of two splits
 };
 
+// Epilogue scales.  Every scale an epilogue needs is loaded before its first
+// store: the output may alias the scale arrays as far as the compiler knows,
+// so a scale loaded between stores would wait for each of them in turn.
+__device__ __forceinline__ float col_scale(const GemmArgs& a, int col) {
+  return col < a.N ? __half2float(__ushort_as_half(a.scale[col])) : 0.0f;
+}
+__device__ __forceinline__ float row_scale(const GemmArgs& a, int row) {
+  return row < a.M ? __half2float(__ushort_as_half(a.sx[row])) : 0.0f;
+}
+
 template <bool I32OUT>
-__device__ __forceinline__ void store_out(const GemmArgs& a, int row, int col, int acc, float sxr) {
+__device__ __forceinline__ void store_out(const GemmArgs& a, int row, int col, int acc, float sxr, float sc) {
   if (row < a.M && col < a.N) {
     if constexpr (I32OUT) {
       static_cast<int*>(a.out)[int64_t(blockIdx.z) * a.zstride + int64_t(row) * a.ldo + col] = acc;
     } else {
-      const float sc = __half2float(__ushort_as_half(a.scale[col]));
       const float y = static_cast<float>(acc) * sxr * sc;
       static_cast<__half*>(a.out)[int64_t(row) * a.ldo + col] = __float2half_rn(y);
     }
@@ -334,16 +343,21 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
   if (wave != 0) return;
 
   // epilogue: lane holds rows 4*(lane/16)+r of each 16x16 tile, column lane%16
+  float sc[TN], sxv[TM][4];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) sc[t] = I32OUT ? 0.0f : col_scale(a, (sbase + t) * 16 + c16);
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sxv[i][r] = I32OUT ? 0.0f : row_scale(a, m0 + i * 16 + 4 * j + r);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = m0 + i * 16 + 4 * j + r;
-      float sxr = 0.0f;
-      if constexpr (!I32OUT) sxr = row < a.M ? __half2float(__ushort_as_half(a.sx[row])) : 0.0f;
 #pragma unroll
       for (int t = 0; t < TN; ++t) {
-        if (sbase + t < a.n_strips) store_out<I32OUT>(a, row, (sbase + t) * 16 + c16, acc[i][t][r], sxr);
+        if (sbase + t < a.n_strips) store_out<I32OUT>(a, row, (sbase + t) * 16 + c16, acc[i][t][r], sxv[i][r], sc[t]);
       }
     }
   }
@@ -487,13 +501,12 @@ __global__ __launch_bounds__(512) void gemm_strip_kernel(GemmArgs a, int spb, in
   if (wk != 0 || !live) return;
 
   // epilogue: lane holds rows 4*(lane/16)+r, column lane%16 of the strip
+  const float sc = I32OUT ? 0.0f : col_scale(a, strip * 16 + c16);
+  float sxv[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = 4 * j + r;
-    float sxr = 0.0f;
-    if constexpr (!I32OUT) sxr = row < a.M ? __half2float(__ushort_as_half(a.sx[row])) : 0.0f;
-    store_out<I32OUT>(a, row, strip * 16 + c16, acc[r], sxr);
-  }
+  for (int r = 0; r < 4; ++r) sxv[r] = I32OUT ? 0.0f : row_scale(a, 4 * j + r);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) store_out<I32OUT>(a, 4 * j + r, strip * 16 + c16, acc[r], sxv[r], sc);
 }
 
 // ---------------------------------------------------------------------------
@@ -681,16 +694,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
     }
   }
 
-  // epilogue: lane holds column lane%32 and rows 8*(r/4) + 4*(lane/32) + r%4
+  // epilogue: lane holds column lane%32 and rows 8*(r/4) + 4*(lane/32) + r%4.
+  // Every scale is fetched before the first store: stores count on the same
+  // in-order counter as global loads, so a load issued after a store waits
+  // for it.  The block's row scales go through LDS (free after the last
+  // barrier of the K loop; LDS reads have a counter of their own).
+  float sc[TN];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) sc[t] = I32OUT ? 0.0f : col_scale(a, n0 + 32 * t + c32);
+  float* sxs = reinterpret_cast<float*>(As0);
+  if constexpr (!I32OUT) {
+    for (int r = threadIdx.x; r < BM; r += THREADS) sxs[r] = row_scale(a, m0 + r);
+    __syncthreads();
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = m0 + row0 + i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      float sxr = 0.0f;
-      if constexpr (!I32OUT) sxr = row < a.M ? __half2float(__ushort_as_half(a.sx[row])) : 0.0f;
+      const int lr = row0 + i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const float sxr = I32OUT ? 0.0f : sxs[lr];
 #pragma unroll
-      for (int t = 0; t < TN; ++t) store_out<I32OUT>(a, row, n0 + 32 * t + c32, acc[i][t][r], sxr);
+      for (int t = 0; t < TN; ++t) store_out<I32OUT>(a, m0 + lr, n0 + 32 * t + c32, acc[i][t][r], sxr, sc[t]);
     }
   }
 }
@@ -713,8 +737,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const int* __restric
   const int* p = ws + int64_t(row) * ldw + col;
   v4i s = *reinterpret_cast<const v4i*>(p);
   for (int z = 1; z < ksplit; ++z) s += *reinterpret_cast<const v4i*>(p + z * zs);
-  float sxr = 0.0f;
-  if constexpr (!I32OUT) sxr = __half2float(__ushort_as_half(sx[row]));
+  // scales first: a load issued after a store waits for it
+  float sxr = 0.0f, sc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (!I32OUT) {
+    sxr = __half2float(__ushort_as_half(sx[row]));
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (col + e < N) sc[e] = __half2float(__ushort_as_half(scale[col + e]));
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int c = col + e;
@@ -722,7 +752,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const int* __restric
       if constexpr (I32OUT) {
         static_cast<int*>(out)[int64_t(row) * ldo + c] = s[e];
       } else {
-        const float y = static_cast<float>(s[e]) * sxr * __half2float(__ushort_as_half(scale[c]));
+        const float y = static_cast<float>(s[e]) * sxr * sc[e];
         static_cast<__half*>(out)[int64_t(row) * ldo + c] = __float2half_rn(y);
       }
     }
