@@ -722,39 +722,57 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------
 // Split-K reduction: sums the INT32 partials of the K splits (exact, in a
 // fixed order) and applies the epilogue.  Partials are [ksplit][M][ldw] with
-// ldw a multiple of 16; each thread handles four consecutive columns.
+// ldw a multiple of 16; each thread handles eight consecutive columns: two
+// 16-byte loads per split, and one 16-byte FP16 store (or two INT32 ones)
+// when the output rows are 16-byte aligned (`vec`).
 template <bool I32OUT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const int* __restrict__ ws, int ksplit, int M, int N,
                                                             int ldw, const unsigned short* __restrict__ sx,
                                                             const unsigned short* __restrict__ scale, void* out,
-                                                            int64_t ldo) {
-  const int per_row = ldw / 4;
+                                                            int64_t ldo, int vec) {
+  const int per_row = ldw / 8;
   const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= int64_t(M) * per_row) return;
   const int row = int(idx / per_row);
-  const int col = int(idx % per_row) * 4;
+  const int col = int(idx % per_row) * 8;
   const int64_t zs = int64_t(M) * ldw;
   const int* p = ws + int64_t(row) * ldw + col;
-  v4i s = *reinterpret_cast<const v4i*>(p);
-  for (int z = 1; z < ksplit; ++z) s += *reinterpret_cast<const v4i*>(p + z * zs);
-  // scales first: a load issued after a store waits for it
-  float sxr = 0.0f, sc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if constexpr (!I32OUT) {
-    sxr = __half2float(__ushort_as_half(sx[row]));
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (col + e < N) sc[e] = __half2float(__ushort_as_half(scale[col + e]));
+  v4i s0 = *reinterpret_cast<const v4i*>(p), s1 = *reinterpret_cast<const v4i*>(p + 4);
+  for (int z = 1; z < ksplit; ++z) {
+    s0 += *reinterpret_cast<const v4i*>(p + z * zs);
+    s1 += *reinterpret_cast<const v4i*>(p + z * zs + 4);
   }
+  int v[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  if constexpr (I32OUT) {
+    int* o = static_cast<int*>(out) + int64_t(row) * ldo + col;
+    if (vec && col + 8 <= N) {
+      *reinterpret_cast<v4i*>(o) = s0;
+      *reinterpret_cast<v4i*>(o + 4) = s1;
+    } else {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int c = col + e;
-    if (c < N) {
-      if constexpr (I32OUT) {
-        static_cast<int*>(out)[int64_t(row) * ldo + c] = s[e];
-      } else {
-        const float y = static_cast<float>(s[e]) * sxr * sc[e];
-        static_cast<__half*>(out)[int64_t(row) * ldo + c] = __float2half_rn(y);
-      }
+      for (int e = 0; e < 8; ++e)
+        if (col + e < N) o[e] = v[e];
+    }
+  } else {
+    // scales before any store: a load issued after a store waits for it
+    const float sxr = __half2float(__ushort_as_half(sx[row]));
+    float sc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sc[e] = col + e < N ? __half2float(__ushort_as_half(scale[col + e])) : 0.0f;
+    __half h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = __float2half_rn(static_cast<float>(v[e]) * sxr * sc[e]);
+    __half* o = static_cast<__half*>(out) + int64_t(row) * ldo + col;
+    if (vec && col + 8 <= N) {
+      u32x4 pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        pk[e] = uint32_t(__half_as_ushort(h[2 * e])) | (uint32_t(__half_as_ushort(h[2 * e + 1])) << 16);
+      *reinterpret_cast<u32x4*>(o) = pk;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (col + e < N) o[e] = h[e];
     }
   }
 }
@@ -930,10 +948,13 @@ hipError_t dispatch(const GemmArgs& a0, void* ws, hipStream_t st) {
   hipError_t e = launch_large_tile<PERCH, true>(p.tile, a, st);
   if (e != hipSuccess) return e;
   const int ldw = a.n_strips * kStrip;
-  const int64_t threads = int64_t(a.M) * (ldw / 4);
+  const int64_t threads = int64_t(a.M) * (ldw / 8);
   const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+  // 16-byte row segments: aligned base, and a row stride that keeps them aligned
+  const int esize = I32 ? 4 : 2;
+  const int vec = reinterpret_cast<uintptr_t>(a0.out) % 16 == 0 && (a0.ldo * esize) % 16 == 0;
   hipLaunchKernelGGL((splitk_reduce_kernel<I32>), grid, dim3(256), 0, st, static_cast<const int*>(ws), a.ksplit, a.M,
-                     a.N, ldw, a0.sx, a0.scale, a0.out, a0.ldo);
+                     a.N, ldw, a0.sx, a0.scale, a0.out, a0.ldo, vec);
   return hipGetLastError();
 }
 
