@@ -135,6 +135,8 @@ SMALL = [
     (520, 384, 24400, 0),   # ... per-channel, ragged M and N, 3 groups
     (768, 640, 16384, 128), # ... 5 groups: the three-stage ring wraps
     (512, 1024, 24576, 128),# ... K split in 2 over blocks (INT32 partials + reduction)
+    (256, 512, 4096, 128),  # up to 256 rows in one round of skinny blocks (4 strips, K split in LDS)
+    (200, 384, 4000, 0),    # ... per-channel, ragged M and N (252 blocks)
 ]
 
 

@@ -912,8 +912,22 @@ inline LargePlan plan_large(int64_t M, int64_t N, int64_t K) {
 #endif
 constexpr int64_t kSkinnyMaxM = QOQ_SKINNY_MAXM;
 
+// Up to 256 rows, the K-split skinny kernel (64-row tiles, partials summed in
+// LDS) also serves when it covers the whole problem in one round of blocks,
+// at least 4 strips each: the large kernel would split K across blocks there,
+// and its INT32 partials need a second pass through memory.
+constexpr int64_t kSkinnyMidMaxM = 256;
+inline bool skinny_mid(int64_t M, int64_t N) {
+  if (M <= kSkinnyMaxM || M > kSkinnyMidMaxM) return false;
+  const int n_strips = int(round_up(N, kStrip) / kStrip);
+  const int ny = int((M + 63) / 64);
+  const int tn = std::min(QOQ_STN_MAX, pick_skinny_tn(n_strips, ny));
+  const int64_t blocks = int64_t((n_strips + tn - 1) / tn) * ny;
+  return tn >= 4 && blocks <= 256;
+}
+
 inline size_t workspace_bytes_of(int64_t M, int64_t N, int64_t K) {
-  if (M <= kSkinnyMaxM) return 0;
+  if (M <= kSkinnyMaxM || skinny_mid(M, N)) return 0;
   const LargePlan p = plan_large(M, N, K);
   return p.ksplit > 1 ? size_t(p.ksplit) * size_t(M) * size_t(round_up(N, kStrip)) * sizeof(int) : 0;
 }
@@ -936,7 +950,7 @@ template <bool PERCH, bool I32>
 hipError_t dispatch(const GemmArgs& a0, void* ws, hipStream_t st) {
   if (a0.M <= 16) return dispatch_skinny_strip<PERCH, I32>(a0, st);
   if (a0.M <= 32) return dispatch_skinny_tn<2, PERCH, I32>(a0, st);
-  if (a0.M <= kSkinnyMaxM) return dispatch_skinny_tn<4, PERCH, I32>(a0, st);
+  if (a0.M <= kSkinnyMaxM || skinny_mid(a0.M, a0.N)) return dispatch_skinny_tn<4, PERCH, I32>(a0, st);
   const LargePlan p = plan_large(a0.M, a0.N, int64_t(a0.G) * kGroup);
   if (p.ksplit == 1) return launch_large_tile<PERCH, I32>(p.tile, a0, st);
   // split K: INT32 partials into the workspace, then reduce + epilogue
