@@ -198,7 +198,8 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int row, int col, i
 template <int TM, int TN, int KS, int PF, int AD, bool PERCH, bool I32OUT>
 __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
   static_assert(PF % AD == 0, "the activation ring must tile the weight ring");
-  __shared__ int red[(KS > 1 ? KS - 1 : 1) * TM * 4 * 64];
+  // partial sums of every wave: [KS][TN][TM][4][64 lanes]
+  __shared__ int red[KS > 1 ? KS * TN * TM * 4 * 64 : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, j = lane >> 4;
   const int sbase = blockIdx.x * TN;
@@ -318,48 +319,55 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
     }
   }
 
-  // exact cross-wave reduction of the K-split partial sums
-  if constexpr (KS > 1) {
-#pragma unroll
-    for (int t = 0; t < TN; ++t) {
-      if (wave > 0) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) red[(((wave - 1) * TM + i) * 4 + r) * 64 + lane] = acc[i][t][r];
-      }
-      __syncthreads();
-      if (wave == 0) {
-#pragma unroll
-        for (int w = 1; w < KS; ++w)
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][t][r] += red[(((w - 1) * TM + i) * 4 + r) * 64 + lane];
-      }
-      __syncthreads();
-    }
-  }
-  if (wave != 0) return;
-
-  // epilogue: lane holds rows 4*(lane/16)+r of each 16x16 tile, column lane%16
-  float sc[TN], sxv[TM][4];
-#pragma unroll
-  for (int t = 0; t < TN; ++t) sc[t] = I32OUT ? 0.0f : col_scale(a, (sbase + t) * 16 + c16);
+  // Exact cross-wave reduction of the K-split partial sums, and the epilogue.
+  // Every wave parks its partials in LDS; after one barrier wave w sums and
+  // stores strips w, w+KS, ... (lane holds rows 4*(lane/16)+r of each 16x16
+  // tile, column lane%16).  Scales are loaded before any store.
+  float sxv[TM][4];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) sxv[i][r] = I32OUT ? 0.0f : row_scale(a, m0 + i * 16 + 4 * j + r);
+  if constexpr (KS > 1) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+    for (int t = 0; t < TN; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = m0 + i * 16 + 4 * j + r;
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        if (sbase + t < a.n_strips) store_out<I32OUT>(a, row, (sbase + t) * 16 + c16, acc[i][t][r], sxv[i][r], sc[t]);
+        for (int r = 0; r < 4; ++r) red[(((wave * TN + t) * TM + i) * 4 + r) * 64 + lane] = acc[i][t][r];
+    __syncthreads();
+    float sc[(TN + KS - 1) / KS];
+#pragma unroll
+    for (int u = 0; u < (TN + KS - 1) / KS; ++u) {
+      const int t = wave + u * KS;
+      sc[u] = (I32OUT || t >= TN) ? 0.0f : col_scale(a, (sbase + t) * 16 + c16);
+    }
+#pragma unroll
+    for (int u = 0; u < (TN + KS - 1) / KS; ++u) {
+      const int t = wave + u * KS;
+      if (t < TN && sbase + t < a.n_strips) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            int v = 0;
+#pragma unroll
+            for (int w = 0; w < KS; ++w) v += red[(((w * TN + t) * TM + i) * 4 + r) * 64 + lane];
+            store_out<I32OUT>(a, m0 + i * 16 + 4 * j + r, (sbase + t) * 16 + c16, v, sxv[i][r], sc[u]);
+          }
       }
     }
+  } else {
+    float sc[TN];
+#pragma unroll
+    for (int t = 0; t < TN; ++t) sc[t] = I32OUT ? 0.0f : col_scale(a, (sbase + t) * 16 + c16);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+          if (sbase + t < a.n_strips) store_out<I32OUT>(a, m0 + i * 16 + 4 * j + r, (sbase + t) * 16 + c16, acc[i][t][r], sxv[i][r], sc[t]);
   }
 }
 
