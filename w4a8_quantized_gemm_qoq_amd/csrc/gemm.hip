@@ -281,11 +281,13 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
 
   const int ng = g1 - g0;
   if (ng > 0) {
-    // prologue: weights of the first PF groups, activations of the first AD
-#pragma unroll
-    for (int p = 0; p < PF; ++p) load_b(g0 + p, bq[p], mq[p]);
+    // prologue: activations of the first AD groups, then weights of the first
+    // PF (loads retire in order: the first multiply waits only for what was
+    // issued before its operands)
 #pragma unroll
     for (int p = 0; p < AD; ++p) load_a(min(g0 + p, g1 - 1), aq[p]);
+#pragma unroll
+    for (int p = 0; p < PF; ++p) load_b(g0 + p, bq[p], mq[p]);
 
     // full rounds of PF groups.  Loads are unconditional (weights past the
     // range read zeros for free, activations clamp to the last group) so a
