@@ -131,10 +131,12 @@ SMALL = [
     (16, 10368, 40, 128),   # activations exceed LDS: K-split skinny kernel instead
     (16, 2048, 20000, 128), # strip kernel, 5 strips per block: second activation copy after the barrier
     (7, 1664, 17000, 0),    # ... per-channel, odd row count, copies running into padding
-    (512, 256, 24576, 128), # 256x256 tiles (192 of them): direct-to-LDS operand pipeline, 2 groups
+    (512, 256, 24576, 128), # 256x256 tiles (192 of them), 2 groups
     (520, 384, 24400, 0),   # ... per-channel, ragged M and N, 3 groups
     (768, 640, 16384, 128), # ... 5 groups: the three-stage ring wraps
-    (512, 1024, 24576, 128),# ... K split in 2 over blocks (INT32 partials + reduction)
+    (512, 1024, 24576, 128),# ... 8 groups: 192 tiles fill one round, so no K split
+    (256, 1024, 12288, 128),# 128x128 tiles, 192 of them: no K split (a split would need 2 rounds)
+    (640, 1024, 4096, 0),   # ... per-channel, 160 tiles, ragged last row tile
     (256, 512, 4096, 128),  # up to 256 rows in one round of skinny blocks (4 strips, K split in LDS)
     (200, 384, 4000, 0),    # ... per-channel, ragged M and N (252 blocks)
 ]

@@ -903,8 +903,12 @@ struct LargePlan {
 
 inline int64_t tiles_of(int64_t M, int64_t N_pad, int bm, int bn) { return ((M + bm - 1) / bm) * ((N_pad + bn - 1) / bn); }
 
-// Pick a tile and a K split so that a launch has roughly one workgroup per CU
-// or more; K splits keep at least 4 groups (512 channels) each.
+// Pick a tile, then the K split with the least estimated time: ceil(blocks /
+// 256) rounds of blocks, each G / ksplit groups long, plus, for a split, the
+// INT32 partials written and read again by the reduction (about 5 TB/s)
+// and its launch.  Per-group block times are the ones measured with every CU
+// busy: about 0.8 us for a 128x128 tile and 2.2 us for a 256x256 one.  Every
+// split keeps at least 4 groups (512 channels).
 inline LargePlan plan_large(int64_t M, int64_t N, int64_t K) {
   const int64_t N_pad = round_up(N, kStrip);
   const int64_t G = K / kGroup;
@@ -912,7 +916,13 @@ inline LargePlan plan_large(int64_t M, int64_t N, int64_t K) {
   const int64_t big = tiles_of(M, N_pad, 256, 256);
   if (big < 192) p.tile = 1;
   const int64_t tiles = p.tile ? tiles_of(M, N_pad, 128, 128) : big;
-  while (tiles * p.ksplit < 256 && G / (2 * p.ksplit) >= 4) p.ksplit *= 2;
+  const int64_t group_ns = p.tile ? 800 : 2200;
+  auto cost_ns = [&](int64_t ks) {
+    const int64_t run = ((tiles * ks + 255) / 256) * ((G + ks - 1) / ks) * group_ns;
+    return ks > 1 ? run + ks * M * N_pad * 8 / 5000 + 2000 : run;
+  };
+  for (int64_t ks = 2; G / ks >= 4; ks *= 2)
+    if (cost_ns(ks) < cost_ns(p.ksplit)) p.ksplit = int(ks);
   return p;
 }
 
