@@ -139,6 +139,8 @@ SMALL = [
     (640, 1024, 4096, 0),   # ... per-channel, 160 tiles, ragged last row tile
     (256, 512, 4096, 128),  # up to 256 rows in one round of skinny blocks (4 strips, K split in LDS)
     (200, 384, 4000, 0),    # ... per-channel, ragged M and N (252 blocks)
+    (40, 256, 32768, 128),  # skinny 64-row tiles at most 7 strips per block; rows past M read as zeros
+    (50, 384, 30000, 0),    # ... per-channel, ragged N
 ]
 
 

@@ -197,10 +197,17 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int row, int col, i
 // partial INT32 accumulators are summed exactly through LDS at the end.
 template <int TM, int TN, int KS, int PF, int AD, bool PERCH, bool I32OUT>
 __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
-  static_assert(PF % AD == 0, "the activation ring must tile the weight ring");
-  // partial sums of every wave: [KS][TN][TM][4][64 lanes]
-  __shared__ int red[KS > 1 ? KS * TN * TM * 4 * 64 : 1];
+  static_assert(PF % AD == 0 && PF % 2 == 0, "the activation ring and the LDS ping-pong must tile the weight ring");
+  // LDS: while multiplying, each wave stages its own activations in two
+  // buffers of TM*16 rows x 128 B; afterwards the same memory holds the
+  // partial sums of every wave, [KS][TN][TM][4][64 lanes].
+  constexpr int kStageBytes = 2 * TM * 16 * 128;
+  constexpr int kRedBytes = KS > 1 ? KS * TN * TM * 4 * 64 * 4 : 0;
+  constexpr int kSmemBytes = KS * kStageBytes > kRedBytes ? KS * kStageBytes : kRedBytes;
+  __shared__ __align__(16) int8_t smem[kSmemBytes];
+  int* red = reinterpret_cast<int*>(smem);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int8_t* stage = smem + wave * kStageBytes;
   const int c16 = lane & 15, j = lane >> 4;
   const int sbase = blockIdx.x * TN;
   const int m0 = blockIdx.y * TM * 16;
@@ -223,14 +230,6 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) acc[i][t] = v4i{0, 0, 0, 0};
 
-  // activation rows of this lane: m0 + 16i + c16, K chunk 16j (+64 for h = 1)
-  const int8_t* arow[TM];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int row = m0 + i * 16 + c16;
-    arow[i] = a.x8 + int64_t(row < a.M ? row : 0) * K + 16 * j;
-  }
-
   u32x4 bq[PF][TN];
   uint32_t mq[PF][TN];
   u32x4 aq[AD][TM][2];
@@ -251,18 +250,49 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
       if constexpr (!PERCH) m[t] = a.meta[(int64_t(strip[t]) * a.G4q + (gm >> 2)) * 16 + c16];
     }
   };
-  // Rows past M read row 0 instead: output row m depends only on activation
-  // row m, and rows past M are never stored, so no zeroing (and no wait for
-  // a select) is needed and the loads stay branch-free.
+  // Activations are read in whole 128-byte rows: one load covers 8 rows x one
+  // group (lane l: row l/8, chunk l%8), so every cache line it touches is
+  // used in full (loads in the MFMA operand layout would touch 16 half-used
+  // lines each).  The descriptor covers the block's valid rows; rows past M
+  // and groups past this wave's range read zeros without touching memory.
+  const int ar8 = lane >> 3, aq8 = lane & 7;
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x8 + int64_t(m0) * K, int(min(TM * 16, a.M - m0) * K));
+  int arow[TM][2];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int rl = 16 * i + 8 * hh + ar8;
+      arow[i][hh] = m0 + rl < a.M ? int(rl * K) + 16 * aq8 : kDeadOffset;
+    }
   auto load_a = [&](int g, u32x4 (&ar)[TM][2]) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) ar[i][h] = *reinterpret_cast<const u32x4*>(arow[i] + int64_t(g) * 128 + 64 * h);
-    }
+      for (int hh = 0; hh < 2; ++hh) ar[i][hh] = buf_load16<0>(xrs, g < g1 ? arow[i][hh] + g * 128 : kDeadOffset);
+  };
+  // Into this wave's LDS buffer (chunk-XOR swizzled, conflict-free both
+  // ways), to be read back in the MFMA A layout: lane (c16, j) takes row c16
+  // of tile i, K chunk j (+4 for the second 64-wide step).  A wave reads only
+  // what it wrote, and LDS operations of one wave complete in order, so no
+  // barrier is involved.
+  auto stage_a = [&](const u32x4 (&ar)[TM][2], int buf) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        *reinterpret_cast<u32x4*>(stage + buf * (TM * 16 * 128) + lds_off(16 * i + 8 * hh + ar8, aq8)) = ar[i][hh];
   };
 
-  auto compute = [&](int g, const u32x4 (&bc)[TN], const uint32_t (&mc)[TN], const u32x4 (&ac)[TM][2]) {
+  // Multiply group g: its activations come out of LDS buffer (g - g0) % 2,
+  // read here so that the fragments are live only while they are used.
+  auto compute = [&](int g, const u32x4 (&bc)[TN], const uint32_t (&mc)[TN]) {
+    v4i af[TM][2];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        af[i][h] = *reinterpret_cast<const v4i*>(stage + ((g - g0) & 1) * (TM * 16 * 128) + lds_off(16 * i + c16, j + 4 * h));
     if constexpr (!PERCH) {
 #pragma unroll
       for (int t = 0; t < TN; ++t) meta_g128((mc[t] >> (8 * (g & 3))) & 0xffu, S[t], C[t]);
@@ -273,8 +303,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
       for (int t = 0; t < TN; ++t) {
         const v4i bf = dequant16(h ? bc[t][2] : bc[t][0], h ? bc[t][3] : bc[t][1], S[t], C[t]);
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-          acc[i][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, ac[i][h]), bf, acc[i][t], 0, 0, 0);
+        for (int i = 0; i < TM; ++i) acc[i][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i][h], bf, acc[i][t], 0, 0, 0);
       }
     }
   };
@@ -283,47 +312,56 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
   if (ng > 0) {
     // prologue: activations of the first AD groups, then weights of the first
     // PF (loads retire in order: the first multiply waits only for what was
-    // issued before its operands)
+    // issued before its operands); group g0 goes into LDS right away.
 #pragma unroll
-    for (int p = 0; p < AD; ++p) load_a(min(g0 + p, g1 - 1), aq[p]);
+    for (int p = 0; p < AD; ++p) load_a(g0 + p, aq[p]);
 #pragma unroll
     for (int p = 0; p < PF; ++p) load_b(g0 + p, bq[p], mq[p]);
+    stage_a(aq[0], 0);
+    load_a(g0 + AD, aq[0]);
+    QOQ_COMPILER_FENCE();
 
-    // full rounds of PF groups.  Loads are unconditional (weights past the
-    // range read zeros for free, activations clamp to the last group) so a
-    // round is straight-line code.  Per group: multiply out of ring slot u,
-    // then refill it with the weights PF groups ahead and the activations AD
-    // groups ahead -- no register copies.  Loads retire in issue order, so
-    // the activation lookahead AD also bounds how far ahead the weight loads
-    // effectively run.
+    // full rounds of PF groups.  Loads are unconditional (past the range they
+    // read zeros for free) so a round is straight-line code.  Step l: multiply
+    // group g0+l (weights from ring slot l % PF, activations already in
+    // registers from LDS buffer l % 2); then pass group l+1 through the other
+    // LDS buffer and refill both rings, the weights PF groups ahead and the
+    // activations AD + 1 ahead.  Loads retire in issue order, so the
+    // activation lookahead also bounds how far ahead the weights effectively
+    // run.
     int it = 0;
     for (; it + PF <= ng; it += PF) {
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
         const int g = g0 + it + u;
-        compute(g, bq[u], mq[u], aq[u % AD]);
+        compute(g, bq[u], mq[u]);
         QOQ_COMPILER_FENCE();
+        stage_a(aq[(u + 1) % AD], (u + 1) & 1);
         load_b(g + PF, bq[u], mq[u]);
-        load_a(min(g + AD, g1 - 1), aq[u % AD]);
+        load_a(g + 1 + AD, aq[(u + 1) % AD]);
         QOQ_COMPILER_FENCE();
       }
     }
-    // remaining ng % PF groups: weights are in bq[0 .. rem), activations of
-    // the first AD of them in the activation ring
+    // remaining ng % PF groups: weights are in bq[0 .. rem), the activations
+    // of the next ones in the activation ring
     const int rem = ng - it;
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
       if (u < rem) {
         const int g = g0 + it + u;
-        compute(g, bq[u], mq[u], aq[u % AD]);
-        if (u + AD < rem) load_a(g + AD, aq[u % AD]);
+        compute(g, bq[u], mq[u]);
+        if (u + 1 < rem) {
+          stage_a(aq[(u + 1) % AD], (u + 1) & 1);
+          if (u + 1 + AD < rem) load_a(g + 1 + AD, aq[(u + 1) % AD]);
+        }
       }
     }
   }
 
   // Exact cross-wave reduction of the K-split partial sums, and the epilogue.
-  // Every wave parks its partials in LDS; after one barrier wave w sums and
-  // stores strips w, w+KS, ... (lane holds rows 4*(lane/16)+r of each 16x16
+  // Once every wave is done with its activation buffers, every wave parks its
+  // partials in the same LDS; after a second barrier wave w sums and stores
+  // strips w, w+KS, ... (lane holds rows 4*(lane/16)+r of each 16x16
   // tile, column lane%16).  Scales are loaded before any store.
   float sxv[TM][4];
 #pragma unroll
@@ -331,6 +369,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) sxv[i][r] = I32OUT ? 0.0f : row_scale(a, m0 + i * 16 + 4 * j + r);
   if constexpr (KS > 1) {
+    __syncthreads();  // every wave is done with its activation buffers
 #pragma unroll
     for (int t = 0; t < TN; ++t)
 #pragma unroll
@@ -817,13 +856,12 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
 }
 
 // Strips per skinny block: the fewest rounds of 256 blocks (one per CU) times
-// strips per block, for `ny` row tiles; ties go to more strips per block
-// (less activation traffic).
-inline int pick_skinny_tn(int n_strips, int ny) {
-  const int lo = 1, hi = 8;
-  int best = lo;
+// strips per block, for `ny` row tiles and at most `hi` strips; ties go to more
+// strips per block (less activation traffic).
+inline int pick_skinny_tn(int n_strips, int ny, int hi) {
+  int best = 1;
   long best_cost = -1;
-  for (int tn = lo; tn <= hi; ++tn) {
+  for (int tn = 1; tn <= hi; ++tn) {
     const long blocks = long((n_strips + tn - 1) / tn) * ny;
     const long cost = ((blocks + 255) / 256) * tn;
     if (best_cost < 0 || cost <= best_cost) {
@@ -837,13 +875,15 @@ inline int pick_skinny_tn(int n_strips, int ny) {
 #ifndef QOQ_SAD
 #define QOQ_SAD 2
 #endif
-#ifndef QOQ_STN_MAX
-#define QOQ_STN_MAX 8
-#endif
+// Most strips per skinny block: 8, or 7 with 64-row tiles (eight would not
+// fit the register file beside four row tiles of accumulators).
+constexpr int skinny_tn_max(int tm) { return tm >= 4 ? 7 : 8; }
+
 template <int TM, bool PERCH, bool I32>
 hipError_t dispatch_skinny_tn(const GemmArgs& a, hipStream_t st) {
   constexpr int KS = QOQ_SKS4, PF = QOQ_SPF, AD = QOQ_SAD;
-  switch (std::min(QOQ_STN_MAX, pick_skinny_tn(a.n_strips, (a.M + TM * 16 - 1) / (TM * 16)))) {
+  constexpr int kHi = skinny_tn_max(TM);
+  switch (pick_skinny_tn(a.n_strips, (a.M + TM * 16 - 1) / (TM * 16), kHi)) {
     case 1: return launch_skinny<TM, 1, KS, PF, AD, PERCH, I32>(a, st);
     case 2: return launch_skinny<TM, 2, KS, PF, AD, PERCH, I32>(a, st);
     case 3: return launch_skinny<TM, 3, KS, PF, AD, PERCH, I32>(a, st);
@@ -851,7 +891,7 @@ hipError_t dispatch_skinny_tn(const GemmArgs& a, hipStream_t st) {
     case 5: return launch_skinny<TM, 5, KS, PF, AD, PERCH, I32>(a, st);
     case 6: return launch_skinny<TM, 6, KS, PF, AD, PERCH, I32>(a, st);
     case 7: return launch_skinny<TM, 7, KS, PF, AD, PERCH, I32>(a, st);
-    default: return launch_skinny<TM, 8, KS, PF, AD, PERCH, I32>(a, st);
+    default: return launch_skinny<TM, kHi, KS, PF, AD, PERCH, I32>(a, st);
   }
 }
 
@@ -885,7 +925,7 @@ hipError_t launch_strip(const GemmArgs& a, int spb, int ks, size_t lds, hipStrea
 template <bool PERCH, bool I32>
 hipError_t dispatch_skinny_strip(const GemmArgs& a, hipStream_t st) {
   const int R = a.M < 16 ? a.M : 16;
-  const int spb = pick_skinny_tn(a.n_strips, 1);
+  const int spb = pick_skinny_tn(a.n_strips, 1, 8);
   int ks = 8 / spb;
   if (ks < 1) ks = 1;
   const size_t lds = strip_lds_bytes(a.G, R, spb, ks, PERCH);
@@ -941,7 +981,7 @@ inline bool skinny_mid(int64_t M, int64_t N) {
   if (M <= kSkinnyMaxM || M > kSkinnyMidMaxM) return false;
   const int n_strips = int(round_up(N, kStrip) / kStrip);
   const int ny = int((M + 63) / 64);
-  const int tn = std::min(QOQ_STN_MAX, pick_skinny_tn(n_strips, ny));
+  const int tn = pick_skinny_tn(n_strips, ny, skinny_tn_max(4));
   const int64_t blocks = int64_t((n_strips + tn - 1) / tn) * ny;
   return tn >= 4 && blocks <= 256;
 }
