@@ -60,12 +60,17 @@ __all__ = [
     "epilogue",
     "dequant_matmul_fp64",
     "w4a8_forward",
+    "W8_QMAX",
+    "quant_weight_w8",
+    "encode_weight_w8",
+    "dequant_level1_saturating",
 ]
 
 ACT_QMAX = 127   # symmetric INT8 activation range [-127, 127]
 W8_PROTECT = 119  # protective INT8 range for the level-0 weight codes
 U4_MAX = 15       # UINT4 code range [0, 15]
 GROUP = 128       # group size along K of the level-1 (g128) quantization
+W8_QMAX = 127     # symmetric INT8 range of the W8A8 comparator's weights
 
 
 def fp16_rne(a) -> np.ndarray:
@@ -112,6 +117,23 @@ def quant_act_per_token(X):
     return q.astype(np.int8), s_x
 
 
+def _per_channel_symmetric(W, qmax):
+    """Per-output-channel symmetric INT8: s = fp16(max|W| / qmax),
+    q = clamp(round(W / s), -qmax, qmax); a zero scale gives a zero row.
+    The division and the rounding are taken in FP32 (the precision that
+    decides the codes on the device too)."""
+    W32 = np.asarray(W, dtype=np.float16).astype(np.float32)
+    if not np.all(np.isfinite(W32)):
+        raise ValueError("non-finite weight")
+    b = np.max(np.abs(W32), axis=1)
+    s = fp16_rne(b / np.float32(qmax))
+    s32 = s.astype(np.float32)
+    safe = np.where(s32 == 0, np.float32(1), s32)
+    q = np.clip(np.rint(W32 / safe[:, None]), -qmax, qmax)
+    q[s32 == 0, :] = 0
+    return q.astype(np.int8), s
+
+
 def quant_weight_level0(W):
     """Progressive quantization, level 0: per-output-channel symmetric INT8.
 
@@ -124,16 +146,7 @@ def quant_weight_level0(W):
 
     Returns (q8 int8 [N,K], s0 float16 [N]).
     """
-    W32 = np.asarray(W, dtype=np.float16).astype(np.float32)
-    if not np.all(np.isfinite(W32)):
-        raise ValueError("non-finite weight")
-    b = np.max(np.abs(W32), axis=1)
-    s0 = fp16_rne(b / np.float32(W8_PROTECT))
-    s32 = s0.astype(np.float32)
-    safe = np.where(s32 == 0, np.float32(1), s32)
-    q = np.clip(np.rint(W32 / safe[:, None]), -W8_PROTECT, W8_PROTECT)
-    q[s32 == 0, :] = 0
-    return q.astype(np.int8), s0
+    return _per_channel_symmetric(W, W8_PROTECT)
 
 
 def group_scale_zero(lo, hi):
@@ -322,3 +335,38 @@ def w4a8_forward(X, enc):
     acc = gemm_exact(x8, enc["w8"])
     y = epilogue(acc, s_x, enc["scale"])
     return x8, s_x, acc, y
+
+
+# ------------------------------------------------------------------ comparators
+
+def quant_weight_w8(W):
+    """Per-channel symmetric INT8 weights of the W8A8 comparator GEMM.
+
+    [SS]: the W4A8 GEMM is compared with an INT8 (W8A8) library GEMM;
+    [PL §6, accuracy evaluation]: W8A8 SmoothQuant is the 8-bit baseline;
+    [PL §2, integer quantization]: symmetric quantization with one scale per
+    output channel.  The full INT8 range is used (there is no second level to
+    protect).  Per row n:  s_w = fp16(max_k |W[n,k]| / 127),
+    w8 = clamp(round(W / s_w), -127, 127); a zero scale gives a zero row.
+
+    Returns (w8 int8 [N,K], s_w float16 [N]).
+    """
+    return _per_channel_symmetric(W, W8_QMAX)
+
+
+def encode_weight_w8(W):
+    """W8A8 comparator weights in the form ``w4a8_forward`` takes."""
+    w8, s_w = quant_weight_w8(W)
+    return {"w8": w8.astype(np.int64), "scale": s_w, "group_size": None}
+
+
+def dequant_level1_saturating(q4, s1, z, group=GROUP):
+    """Level-1 dequantization clamped to INT8: clip((q4 - z) * s1, -128, 127).
+
+    [PL §4, progressive group quantization]: without the protective level-0
+    range the dequantized intermediates can leave INT8 and the GEMM would have
+    to saturate them, which the pages report as costly.  This is that
+    saturating form; on codes from ``encode_weight_g128`` it equals
+    ``dequant_level1`` (their values stay within [-121, 121]).
+    """
+    return np.clip(dequant_level1(q4, s1, z, group), -128, 127)

@@ -297,3 +297,65 @@ def test_synthetic_prefix_and_determinism():
     assert np.array_equal(synthetic.make_w(32, 256), synthetic.make_w(32, 256))
     cols = synthetic.outlier_channels(8192, "frac")
     assert cols.size == 41 and np.unique(cols).size == 41
+
+
+# ------------------------------------------------------------ comparators (f1)
+
+def test_w8_hand_worked_row():
+    fx = read_fixture("weight_w8_row.txt")
+    W = np.array([fx["w"]], dtype=np.float16)
+    w8, s = O.quant_weight_w8(W)
+    assert float(s[0]) == fx["s"][0]
+    assert w8[0].tolist() == [int(v) for v in fx["w8"]]
+
+
+def test_w8_invariants_and_error_bound():
+    W = synthetic.make_w(256, 1024, seed=6)
+    w8, s = O.quant_weight_w8(W)
+    assert np.abs(w8.astype(int)).max() <= 127
+    # each row's largest magnitude lands on the range end
+    am = np.argmax(np.abs(W.astype(np.float32)), axis=1)
+    assert np.all(np.abs(w8[np.arange(256), am].astype(int)) == 127)
+    s64 = s.astype(np.float64)[:, None]
+    err = np.abs(w8.astype(np.float64) * s64 - W.astype(np.float64))
+    inside = np.abs(W.astype(np.float64)) <= 126.5 * s64
+    assert np.all(err[inside] <= 0.5 * s64.repeat(W.shape[1], 1)[inside])
+    # a finer grid than the protective level-0 one on the same rows
+    _, s0 = O.quant_weight_level0(W)
+    assert np.all(s.astype(np.float64) <= s0.astype(np.float64))
+
+
+def test_w8_zero_row_and_nonfinite():
+    W = np.zeros((2, 128), np.float16)
+    W[1, 5] = 3.0
+    w8, s = O.quant_weight_w8(W)
+    assert float(s[0]) == 0 and not w8[0].any()
+    assert w8[1, 5] == 127 and int(np.count_nonzero(w8[1])) == 1
+    W[1, 7] = np.float16(np.inf)
+    with pytest.raises(ValueError):
+        O.quant_weight_w8(W)
+
+
+def test_w8a8_forward_matches_bruteforce():
+    X, W = synthetic.make_inputs("tiny")
+    enc = O.encode_weight_w8(W)
+    x8, s_x, acc, y = O.w4a8_forward(X, enc)
+    assert np.array_equal(acc, O.gemm_bruteforce(x8, enc["w8"]))
+    yd = O.dequant_matmul_fp64(x8, s_x, enc["w8"], enc["scale"])
+    assert np.array_equal(y, O.fp16_rne(yd))
+
+
+def test_saturating_dequant_hand_cases():
+    fx = read_fixture("saturating_dequant.txt")
+    q4 = np.array([fx["q4"]], np.uint8)
+    s1 = np.array([fx["s1"]], np.uint8)
+    z = np.array([fx["z"]], np.uint8)
+    assert O.dequant_level1(q4, s1, z, group=1)[0].tolist() == [int(v) for v in fx["plain"]]
+    assert O.dequant_level1_saturating(q4, s1, z, group=1)[0].tolist() == [int(v) for v in fx["sat"]]
+
+
+def test_saturating_dequant_is_exact_inside_the_protective_range():
+    W = synthetic.make_w(128, 2048, seed=8)
+    enc = O.encode_weight_g128(W)
+    sat = O.dequant_level1_saturating(enc["q4"], enc["s1"], enc["z"])
+    assert np.array_equal(sat, enc["w8"])
