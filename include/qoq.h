@@ -193,6 +193,64 @@ QOQ_API int qoq_w4a8_gemm_i32(const int8_t* x8, const void* qweight, const void*
                       int64_t M, int64_t N, int64_t K, int64_t ldacc, int32_t group_size,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Comparators of the W4A8 GEMM.  They run the same kernels, launch plans and
+ * epilogue, so that the cost of the weight format is measured on its own.
+ */
+
+/*
+ * W8A8 weights (host): per output channel n, symmetric INT8,
+ *   s_w = fp16(max_k |W[n,k]| / 127)  (FP32 IEEE divide, round half to even),
+ *   w8  = clamp(round(W / s_w), -127, 127); a zero scale gives a zero row.
+ * This is the INT8-weight GEMM the pages compare the W4A8 GEMM with ([SS]:
+ * the W4A8 GEMM against the W8A8 library GEMM; [PL §3, roofline analysis:
+ * W4A16 against W8A8]; [PL §6, accuracy evaluation: W8A8 SmoothQuant]).
+ * Layout: qweight8 (N_pad*K bytes) is 16-channel strips, each a run of G
+ * 2048-byte group blocks of 128 slots of 16 bytes:
+ *   offset = ((strip*G + g)*128 + slot)*16 + b,  slot = c + 16*j + 64*h
+ *   (c = channel in strip, j = 0..3, h = 0..1, b = 0..15) holds
+ *   w8[16*strip + c][128*g + 64*h + 16*j + b].
+ * scale_fp16: N_pad entries, 0 for padded channels.  Same shape rules and
+ * error behaviour as qoq_pack_weights.
+ */
+QOQ_API int qoq_pack_weights_w8(const uint16_t* w_fp16, int64_t N, int64_t K, void* qweight8, uint16_t* scale_fp16);
+
+/* Workspace (bytes) qoq_w8a8_gemm / qoq_w8a8_gemm_i32 need for this shape. */
+QOQ_API size_t qoq_w8a8_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/*
+ * W8A8 GEMM (device): y[m,n] = fp16(float(acc[m,n]) * s_x[m] * s_w[n]) with
+ * acc[m,n] = sum_k x8[m,k] * w8[n,k] (exact INT32).  Arguments as for
+ * qoq_w4a8_gemm, with the INT8 packed weights in place of qweight/meta.
+ */
+QOQ_API int qoq_w8a8_gemm(const int8_t* x8, const void* sx_fp16, const void* qweight8, const void* scale_fp16,
+                  void* y_fp16, int64_t M, int64_t N, int64_t K, int64_t ldy, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/* W8A8 debug entry: writes the exact INT32 accumulators (row stride ldacc). */
+QOQ_API int qoq_w8a8_gemm_i32(const int8_t* x8, const void* qweight8, int32_t* acc, int64_t M, int64_t N,
+                      int64_t K, int64_t ldacc, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Saturating-dequantization ablation of the g128 W4A8 GEMM (device).  [PL §4,
+ * progressive group quantization]: the protective range [-119, 119] keeps
+ * (q4 - z)*s1 inside INT8 so the GEMM can dequantize with plain packed-byte
+ * arithmetic; without it every value must be clamped, which the pages report
+ * as costly.  This entry clamps: w8 = clamp((q4 - z)*s1, -128, 127), computed
+ * in 16-bit lanes, for any s1 in [1,16] and z in [0,15].  For weights packed
+ * by qoq_pack_weights or qoq_pack_codes the result equals qoq_w4a8_gemm's
+ * (group_size 128), bit for bit.  Same arguments as qoq_w4a8_gemm with
+ * group_size 128 (workspace size from qoq_w4a8_gemm_workspace_size).
+ */
+QOQ_API int qoq_w4a8_gemm_saturating(const int8_t* x8, const void* sx_fp16, const void* qweight, const void* meta,
+                             const void* scale_fp16, void* y_fp16, int64_t M, int64_t N, int64_t K,
+                             int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Saturating ablation, INT32 debug entry. */
+QOQ_API int qoq_w4a8_gemm_saturating_i32(const int8_t* x8, const void* qweight, const void* meta, int32_t* acc,
+                                 int64_t M, int64_t N, int64_t K, int64_t ldacc, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

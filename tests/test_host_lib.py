@@ -25,7 +25,7 @@ def header_symbols():
 def test_library_exports_every_header_symbol():
     lib = q.load_library()
     syms = header_symbols()
-    assert len(syms) == 10, syms
+    assert len(syms) == 16, syms
     assert sorted(_native.EXPORTS) == syms
     for s in syms:
         assert hasattr(lib, s), s
@@ -256,3 +256,63 @@ def test_device_entry_points_validate_before_launch():
     # misaligned qweight
     assert lib.qoq_w4a8_gemm_i32(d, d + 4, d, d, 4, 16, 128, 16, 128, None, 0, None) == 3
     assert lib.qoq_w4a8_gemm_workspace_size(4, 16, 128, 128) == 0
+
+
+# ------------------------------------------------------------ comparators (f1)
+
+def _documented_w8_blocks(w8, N, K):
+    """Scatter INT8 codes by the layout comment of qoq_pack_weights_w8."""
+    N_pad = (N + 15) // 16 * 16
+    G = K // 128
+    out = np.zeros(N_pad * K, np.uint8)
+    for n in range(N):
+        strip, c = divmod(n, 16)
+        for g in range(G):
+            for h in range(2):
+                for j in range(4):
+                    slot = c + 16 * j + 64 * h
+                    k0 = 128 * g + 64 * h + 16 * j
+                    off = ((strip * G + g) * 128 + slot) * 16
+                    out[off:off + 16] = w8[n, k0:k0 + 16].astype(np.int8).view(np.uint8)
+    return out
+
+
+@pytest.mark.parametrize("N,K,seed", [(16, 256, 0), (77, 1152, 4), (40, 384, 9)])
+def test_pack_weights_w8_matches_oracle_and_layout(N, K, seed):
+    W = synthetic.make_w(N, K, seed=seed)
+    p = q.qoq_pack_weights_w8(W)
+    w8, s = O.quant_weight_w8(W)
+    assert np.array_equal(np.asarray(p.scale)[:N].view(np.float16), s)
+    assert not np.asarray(p.scale)[N:].any()
+    assert np.array_equal(p.qweight, _documented_w8_blocks(w8, N, K))
+
+
+def test_pack_weights_w8_edge_rows_and_rejects():
+    K = 256
+    rows = [np.zeros(K), np.full(K, 3.0), np.r_[65504.0, -65504.0, np.zeros(K - 2)],
+            np.r_[np.full(K - 1, 1e-7), 6e-8], np.linspace(-1, 1, K)]
+    W = np.array(rows, dtype=np.float16)
+    p = q.qoq_pack_weights_w8(W)
+    w8, s = O.quant_weight_w8(W)
+    assert np.array_equal(np.asarray(p.scale)[:len(rows)].view(np.float16), s)
+    assert np.array_equal(p.qweight, _documented_w8_blocks(w8, len(rows), K))
+    W[2, 3] = np.float16(np.nan)
+    with pytest.raises(q.QoQError):
+        q.qoq_pack_weights_w8(W)
+    with pytest.raises(q.QoQError):
+        q.qoq_pack_weights_w8(np.zeros((4, 100), np.float16))
+
+
+def test_comparator_entry_points_validate_before_launch():
+    lib = q.load_library()
+    d = 4096
+    # null pointers
+    assert lib.qoq_w8a8_gemm(None, None, None, None, None, 4, 16, 128, 16, None, 0, None) == 1
+    assert lib.qoq_w4a8_gemm_saturating(None, None, None, None, None, None, 4, 16, 128, 16, None, 0, None) == 1
+    # K not a multiple of 128, ldacc < N, misaligned weights
+    assert lib.qoq_w8a8_gemm_i32(d, d, d, 4, 16, 100, 16, None, 0, None) == 2
+    assert lib.qoq_w8a8_gemm_i32(d, d, d, 4, 16, 128, 8, None, 0, None) == 1
+    assert lib.qoq_w8a8_gemm_i32(d, d + 4, d, 4, 16, 128, 16, None, 0, None) == 3
+    assert lib.qoq_w4a8_gemm_saturating_i32(d, d, d, d, 4, 16, 100, 16, None, 0, None) == 2
+    assert lib.qoq_w8a8_gemm_workspace_size(4, 16, 128) == 0
+    assert lib.qoq_w8a8_gemm_workspace_size(300, 96, 2048) == lib.qoq_w4a8_gemm_workspace_size(300, 96, 2048, 128)

@@ -9,6 +9,7 @@ from ._native import (  # noqa: F401
     GROUP,
     LIB_PATH,
     PackedWeight,
+    PackedWeightW8,
     QoQError,
     load_library,
     qoq_pack_codes,
@@ -18,5 +19,10 @@ from ._native import (  # noqa: F401
     qoq_w4a8_forward,
     qoq_w4a8_gemm,
     qoq_w4a8_gemm_i32,
+    qoq_w4a8_gemm_saturating,
+    qoq_w4a8_gemm_saturating_i32,
+    qoq_pack_weights_w8,
+    qoq_w8a8_gemm,
+    qoq_w8a8_gemm_i32,
     qoq_weight_layout_query,
 )

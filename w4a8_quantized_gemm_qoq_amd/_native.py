@@ -30,6 +30,12 @@ EXPORTS = [
     "qoq_w4a8_gemm_workspace_size",
     "qoq_w4a8_gemm",
     "qoq_w4a8_gemm_i32",
+    "qoq_pack_weights_w8",
+    "qoq_w8a8_gemm_workspace_size",
+    "qoq_w8a8_gemm",
+    "qoq_w8a8_gemm_i32",
+    "qoq_w4a8_gemm_saturating",
+    "qoq_w4a8_gemm_saturating_i32",
 ]
 
 GROUP = 128
@@ -84,6 +90,12 @@ def load_library():
         "qoq_w4a8_gemm_workspace_size": (sz, [i64, i64, i64, i32]),
         "qoq_w4a8_gemm": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]),
         "qoq_w4a8_gemm_i32": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]),
+        "qoq_pack_weights_w8": (ctypes.c_int, [vp, i64, i64, vp, vp]),
+        "qoq_w8a8_gemm_workspace_size": (sz, [i64, i64, i64]),
+        "qoq_w8a8_gemm": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]),
+        "qoq_w8a8_gemm_i32": (ctypes.c_int, [vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]),
+        "qoq_w4a8_gemm_saturating": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]),
+        "qoq_w4a8_gemm_saturating_i32": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -276,3 +288,134 @@ def qoq_w4a8_forward(x, w: PackedWeight, stream=None):
     """One pass of the online path: per-token quantization then the W4A8 GEMM."""
     x8, sx = qoq_quant_act_per_token(x, stream=stream)
     return qoq_w4a8_gemm(x8, sx, w, stream=stream)
+
+
+# ------------------------------------------------- comparators (same kernels)
+
+@dataclass
+class PackedWeightW8:
+    """Per-channel INT8 weights of the W8A8 comparator (host or device)."""
+    qweight: object
+    scale: object
+    N: int
+    K: int
+
+    def to(self, device="cuda") -> "PackedWeightW8":
+        import torch
+        qw = torch.from_numpy(np.ascontiguousarray(self.qweight)).to(device)
+        sc = torch.from_numpy(np.ascontiguousarray(self.scale)).view(torch.float16).to(device)
+        return PackedWeightW8(qw, sc, self.N, self.K)
+
+
+def qoq_pack_weights_w8(W: np.ndarray) -> PackedWeightW8:
+    """Per-channel symmetric INT8 encode + pack of W [N, K] on the host."""
+    W = np.ascontiguousarray(W, dtype=np.float16)
+    N, K = W.shape
+    N_pad = (N + 15) // 16 * 16
+    qw = np.empty(N_pad * K, np.uint8)
+    scale = np.empty(N_pad, np.uint16)
+    lib = load_library()
+    _check(lib.qoq_pack_weights_w8(_np_ptr(W.view(np.uint16)), N, K, _np_ptr(qw), _np_ptr(scale)),
+           "qoq_pack_weights_w8")
+    return PackedWeightW8(qw, scale, N, K)
+
+
+def _workspace(ws_bytes, workspace, device):
+    import torch
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+    return _t_ptr(workspace) if ws_bytes else None
+
+
+def _out(x8, N, out, dtype):
+    import torch
+    M = x8.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=dtype, device=x8.device)
+    _require_cuda(out)
+    if out.dtype != dtype or out.shape != (M, N) or out.stride(1) != 1:
+        raise ValueError(f"output must be {dtype} [M, N] with unit column stride")
+    return out
+
+
+def _check_x8(x8, K):
+    import torch
+    _require_cuda(x8)
+    if x8.dtype != torch.int8 or x8.dim() != 2 or not x8.is_contiguous():
+        raise ValueError("x8 must be a contiguous int8 [M, K] tensor")
+    if x8.shape[1] != K:
+        raise ValueError(f"x8 has K={x8.shape[1]}, weights have K={K}")
+
+
+def _check_sx(sx, M):
+    import torch
+    _require_cuda(sx)
+    if sx.dtype != torch.float16 or sx.numel() != M or not sx.is_contiguous():
+        raise ValueError("sx must be contiguous float16 [M]")
+
+
+def qoq_w8a8_gemm(x8, sx, w: PackedWeightW8, y=None, workspace=None, stream=None):
+    """W8A8 comparator: y = fp16(x8 @ w8^T * s_x * s_w) on the GPU."""
+    import torch
+    _check_x8(x8, w.K)
+    _require_cuda(w.qweight, w.scale)
+    M = x8.shape[0]
+    _check_sx(sx, M)
+    y = _out(x8, w.N, y, torch.float16)
+    lib = load_library()
+    ws = lib.qoq_w8a8_gemm_workspace_size(M, w.N, w.K)
+    _check(lib.qoq_w8a8_gemm(_t_ptr(x8), _t_ptr(sx), _t_ptr(w.qweight), _t_ptr(w.scale), _t_ptr(y), M, w.N, w.K,
+                             y.stride(0), _workspace(ws, workspace, x8.device), ws, _stream(stream)), "qoq_w8a8_gemm")
+    return y
+
+
+def qoq_w8a8_gemm_i32(x8, w: PackedWeightW8, acc=None, workspace=None, stream=None):
+    """W8A8 comparator, exact INT32 accumulators."""
+    import torch
+    _check_x8(x8, w.K)
+    _require_cuda(w.qweight)
+    M = x8.shape[0]
+    acc = _out(x8, w.N, acc, torch.int32)
+    lib = load_library()
+    ws = lib.qoq_w8a8_gemm_workspace_size(M, w.N, w.K)
+    _check(lib.qoq_w8a8_gemm_i32(_t_ptr(x8), _t_ptr(w.qweight), _t_ptr(acc), M, w.N, w.K, acc.stride(0),
+                                 _workspace(ws, workspace, x8.device), ws, _stream(stream)), "qoq_w8a8_gemm_i32")
+    return acc
+
+
+def _check_g128(w: PackedWeight):
+    if w.group_size != GROUP:
+        raise ValueError("the saturating ablation takes g128 weights")
+    _require_cuda(w.qweight, w.meta)
+
+
+def qoq_w4a8_gemm_saturating(x8, sx, w: PackedWeight, y=None, workspace=None, stream=None):
+    """Saturating-dequantization ablation of the g128 W4A8 GEMM."""
+    import torch
+    _check_g128(w)
+    _check_x8(x8, w.K)
+    _require_cuda(w.scale)
+    M = x8.shape[0]
+    _check_sx(sx, M)
+    y = _out(x8, w.N, y, torch.float16)
+    lib = load_library()
+    ws = lib.qoq_w4a8_gemm_workspace_size(M, w.N, w.K, GROUP)
+    _check(lib.qoq_w4a8_gemm_saturating(_t_ptr(x8), _t_ptr(sx), _t_ptr(w.qweight), _t_ptr(w.meta), _t_ptr(w.scale),
+                                        _t_ptr(y), M, w.N, w.K, y.stride(0), _workspace(ws, workspace, x8.device), ws,
+                                        _stream(stream)), "qoq_w4a8_gemm_saturating")
+    return y
+
+
+def qoq_w4a8_gemm_saturating_i32(x8, w: PackedWeight, acc=None, workspace=None, stream=None):
+    """Saturating ablation, exact INT32 accumulators."""
+    import torch
+    _check_g128(w)
+    _check_x8(x8, w.K)
+    M = x8.shape[0]
+    acc = _out(x8, w.N, acc, torch.int32)
+    lib = load_library()
+    ws = lib.qoq_w4a8_gemm_workspace_size(M, w.N, w.K, GROUP)
+    _check(lib.qoq_w4a8_gemm_saturating_i32(_t_ptr(x8), _t_ptr(w.qweight), _t_ptr(w.meta), _t_ptr(acc), M, w.N, w.K,
+                                            acc.stride(0), _workspace(ws, workspace, x8.device), ws,
+                                            _stream(stream)), "qoq_w4a8_gemm_saturating_i32")
+    return acc

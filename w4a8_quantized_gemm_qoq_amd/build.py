@@ -3,7 +3,8 @@
     python -m w4a8_quantized_gemm_qoq_amd.build
 
 Compiles the HIP kernels, the host packer and the C-ABI shims into one shared
-library next to this file.  No fast-math: the quantizers rely on IEEE FP32
+library next to this file (one object per source, compiled in parallel under
+_build/, then linked).  No fast-math: the quantizers rely on IEEE FP32
 division and round-half-to-even.
 """
 
@@ -20,7 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqoq.so")
 
-SOURCES = ["status.cpp", "pack.cpp", "act_quant.hip", "gemm.hip"]
+SOURCES = ["status.cpp", "pack.cpp", "act_quant.hip", "gemm_w4.hip", "gemm_w8.hip", "gemm_sat.hip"]
+OBJDIR = os.path.join(PKG, "_build")
 
 
 def hipcc() -> str:
@@ -30,15 +32,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libqoq.so)")
 
 
-def build_command(out: str = LIB, arch: str = "gfx950") -> list[str]:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+def compile_flags(arch: str = "gfx950") -> list[str]:
     return [
-        hipcc(),
         f"--offload-arch={arch}",
         "-O3",
         "-std=c++17",
         "-fPIC",
-        "-shared",
         "-fvisibility=hidden",
         "-Wall",
         "-Wno-unused-command-line-argument",
@@ -46,21 +45,46 @@ def build_command(out: str = LIB, arch: str = "gfx950") -> list[str]:
         "-I", INCLUDE,
         "-I", CSRC,
         "-DQOQ_BUILD",
-        "-o", out,
-        *srcs,
     ]
+
+
+def build_commands(out: str = LIB, arch: str = "gfx950") -> tuple[list[list[str]], list[str]]:
+    """One compile command per source (independent, run in parallel), then the link."""
+    flags = compile_flags(arch)
+    objs, compiles = [], []
+    for src in SOURCES:
+        obj = os.path.join(OBJDIR, src + ".o")
+        objs.append(obj)
+        compiles.append([hipcc(), *flags, "-c", os.path.join(CSRC, src), "-o", obj])
+    link = [hipcc(), f"--offload-arch={arch}", "-shared", "-fPIC", "-o", out, *objs]
+    return compiles, link
 
 
 def build(verbose: bool = False) -> str:
     """Compile libqoq.so; returns its path.  Always recompiles."""
+    os.makedirs(OBJDIR, exist_ok=True)
     tmp = LIB + ".tmp"
-    cmd = build_command(tmp)
+    compiles, link = build_commands(tmp)
+    procs = []
+    for cmd in compiles:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+    failed = []
+    for cmd, p in procs:
+        out, _ = p.communicate()
+        if p.returncode != 0:
+            failed.append((cmd[-3], p.returncode, out))
+    if failed:
+        for src, rc, out in failed:
+            sys.stderr.write(f"{src}: exit code {rc}\n{out}")
+        raise RuntimeError(f"hipcc failed on {', '.join(f[0] for f in failed)}")
     if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+        print(" ".join(link), flush=True)
+    res = subprocess.run(link, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+        raise RuntimeError(f"hipcc link failed with exit code {res.returncode}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -1,5 +1,7 @@
-// W4A8 GEMM for gfx950 (MI355X): UINT4 weights dequantized to INT8 in
-// registers, INT8 MFMA with INT32 accumulation, fused FP32 scale epilogue.
+#pragma once
+// Kernels of the W4A8 GEMM for gfx950 (MI355X), shared by the entry points
+// of gemm_w4.hip, gemm_w8.hip and gemm_sat.hip: UINT4 weights dequantized to
+// INT8 in registers, INT8 MFMA with INT32 accumulation, fused FP32 scale epilogue.
 //
 // Follows "QServe: W4A8KV4 Quantization and System Co-design for Efficient
 // LLM Serving" (paperlayer.ai abs/2405.04532v3 summary):
@@ -21,6 +23,16 @@
 // so neither the 16-bit multiply-add nor the byte lanes carry, and XOR 0x80
 // turns the biased byte into the two's-complement INT8 w8.  For the
 // per-channel variant s1 = 1 and c = 128 - z.
+//
+// Weight formats (template parameter WF of every kernel):
+//   kWfG128:       progressive g128 UINT4 (the path above);
+//   kWfPerChannel: per-channel UINT4, w8 = q4 - z;
+//   kWfW8:         per-channel INT8 weights used as they are (the W8A8
+//                  comparator: same kernels, twice the weight bytes, no
+//                  dequantization);
+//   kWfG128Sat:    g128 with a saturating dequantization (ablation of the
+//                  protective range): each value goes through a 16-bit lane,
+//                  clamp(q4*s1 + 128 - z*s1, 0, 255) ^ 0x80.
 //
 // Three kernels share the packed layout (see qoq.h):
 //   strip:  v_mfma_i32_16x16x64_i8, up to 16 rows; one contiguous weight
@@ -112,6 +124,22 @@ __device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t 
   return d;
 }
 
+__device__ __forceinline__ uint32_t pk_mad_i16(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_pk_mad_i16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+__device__ __forceinline__ uint32_t pk_max_i16(uint32_t a, uint32_t b) {
+  uint32_t d;
+  asm("v_pk_max_i16 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ uint32_t pk_min_i16(uint32_t a, uint32_t b) {
+  uint32_t d;
+  asm("v_pk_min_i16 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
 // Two packed words (16 codes) -> one 16-byte INT8 MFMA operand.
 __device__ __forceinline__ v4i dequant16(uint32_t v0, uint32_t v1, uint32_t S, uint32_t C) {
   v4i r;
@@ -122,17 +150,64 @@ __device__ __forceinline__ v4i dequant16(uint32_t v0, uint32_t v1, uint32_t S, u
   return r;
 }
 
+// Saturating form of dequant16 (ablation): every code gets a 16-bit lane,
+// t = q4*s1 + (128 - z*s1) is clamped to [0, 255] and the bytes are packed
+// back, XOR 0x80 giving clamp((q4 - z)*s1, -128, 127).  C holds the signed
+// 16-bit 128 - z*s1 in both lanes, so no bound on z*s1 is assumed.  Same
+// output bytes as dequant16 wherever that one is exact.
+__device__ __forceinline__ uint32_t sat_lanes(uint32_t e, uint32_t S, uint32_t C) {
+  return pk_min_i16(pk_max_i16(pk_mad_i16(e, S, C), 0u), 0x00ff00ffu);
+}
+__device__ __forceinline__ void dequant_word_sat(uint32_t v, uint32_t S, uint32_t C, int& even, int& odd) {
+  // 16-bit lanes of codes (0,4) and (2,6) give the bytes of codes 0,2,4,6;
+  // lanes (1,5) and (3,7) those of 1,3,5,7 -- the byte order of dequant16
+  even = int((sat_lanes(v & 0x000f000fu, S, C) | (sat_lanes((v >> 8) & 0x000f000fu, S, C) << 8)) ^ 0x80808080u);
+  odd = int((sat_lanes((v >> 4) & 0x000f000fu, S, C) | (sat_lanes((v >> 12) & 0x000f000fu, S, C) << 8)) ^ 0x80808080u);
+}
+__device__ __forceinline__ v4i dequant16_sat(uint32_t v0, uint32_t v1, uint32_t S, uint32_t C) {
+  int e0, o0, e1, o1;
+  dequant_word_sat(v0, S, C, e0, o0);
+  dequant_word_sat(v1, S, C, e1, o1);
+  return v4i{e0, o0, e1, o1};
+}
+
+// Weight formats the kernels are instantiated for.
+constexpr int kWfG128 = 0;
+constexpr int kWfPerChannel = 1;
+constexpr int kWfW8 = 2;
+constexpr int kWfG128Sat = 3;
+// formats with a metadata byte per (channel, group)
+constexpr bool wf_group_meta(int wf) { return wf == kWfG128 || wf == kWfG128Sat; }
+// bytes of one (16-channel strip, 128-wide group) block, and 16-byte loads
+// per lane of a wave reading one such block
+constexpr int wf_block_bytes(int wf) { return wf == kWfW8 ? 2048 : 1024; }
+constexpr int wf_vec(int wf) { return wf == kWfW8 ? 2 : 1; }
+
 // Metadata byte -> (S, C) operands of the dequantization.
+template <int WF>
 __device__ __forceinline__ void meta_g128(uint32_t mbyte, uint32_t& S, uint32_t& C) {
   const uint32_t s1 = (mbyte & 15u) + 1u;
   const uint32_t z = mbyte >> 4;
   const uint32_t c = 128u - z * s1;
   S = s1 * 0x00010001u;
-  C = c * 0x01010101u;
+  C = WF == kWfG128Sat ? (c & 0xffffu) * 0x00010001u : c * 0x01010101u;
 }
 __device__ __forceinline__ void meta_perchannel(uint32_t z, uint32_t& S, uint32_t& C) {
   S = 0x00010001u;
   C = (128u - z) * 0x01010101u;
+}
+
+// 16x16x64 B operand h (K 0-63 or 64-127 of the group) of one lane, from
+// that lane's loads of one (strip, group) block.
+template <int WF>
+__device__ __forceinline__ v4i b_op16(const u32x4 (&q)[wf_vec(WF)], int h, uint32_t S, uint32_t C) {
+  if constexpr (WF == kWfW8) {
+    return __builtin_bit_cast(v4i, q[h]);
+  } else if constexpr (WF == kWfG128Sat) {
+    return dequant16_sat(h ? q[0][2] : q[0][0], h ? q[0][3] : q[0][1], S, C);
+  } else {
+    return dequant16(h ? q[0][2] : q[0][0], h ? q[0][3] : q[0][1], S, C);
+  }
 }
 
 // LDS tile of BM rows x 128 bytes; 16-byte chunk kc of row r lives at chunk
@@ -195,7 +270,7 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int row, int col, i
 // blocks), and streams its weights through a PF-deep register ring of 128-bit
 // loads so that enough bytes are in flight to cover HBM latency.  The KS
 // partial INT32 accumulators are summed exactly through LDS at the end.
-template <int TM, int TN, int KS, int PF, int AD, bool PERCH, bool I32OUT>
+template <int TM, int TN, int KS, int PF, int AD, int WF, bool I32OUT>
 __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
   static_assert(PF % AD == 0 && PF % 2 == 0, "the activation ring and the LDS ping-pong must tile the weight ring");
   // LDS: while multiplying, each wave stages its own activations in two
@@ -218,8 +293,9 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
 #pragma unroll
   for (int t = 0; t < TN; ++t) strip[t] = min(sbase + t, a.n_strips - 1);
 
-  uint32_t S[TN], C[TN];
-  if constexpr (PERCH) {
+  constexpr int kVec = wf_vec(WF);
+  uint32_t S[TN] = {}, C[TN] = {};
+  if constexpr (WF == kWfPerChannel) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) meta_perchannel(a.meta8[strip[t] * 16 + c16], S[t], C[t]);
   }
@@ -230,24 +306,26 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) acc[i][t] = v4i{0, 0, 0, 0};
 
-  u32x4 bq[PF][TN];
+  u32x4 bq[PF][TN][kVec];
   uint32_t mq[PF][TN];
   u32x4 aq[AD][TM][2];
 
   // The block's strips are contiguous in the packed weights: one descriptor
   // covers exactly the valid ones, so strips past N and groups past this
   // wave's K range load zeros without touching memory.
-  const int strip_bytes = a.G * 1024;
-  const __amdgpu_buffer_rsrc_t wrs =
-      make_rsrc(a.qw + int64_t(sbase) * a.G * 64, min(TN, a.n_strips - sbase) * strip_bytes);
-  auto load_b = [&](int g, u32x4 (&b)[TN], uint32_t (&m)[TN]) {
-    const int gofs = g < g1 ? g * 1024 : kDeadOffset;
+  constexpr int kBlk = wf_block_bytes(WF);
+  const int strip_bytes = a.G * kBlk;
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(reinterpret_cast<const int8_t*>(a.qw) + int64_t(sbase) * strip_bytes,
+                                               min(TN, a.n_strips - sbase) * strip_bytes);
+  auto load_b = [&](int g, u32x4 (&b)[TN][kVec], uint32_t (&m)[TN]) {
+    const int gofs = g < g1 ? g * kBlk : kDeadOffset;
     const int gm = min(g, g1 - 1);
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       // weights are streamed once per call: non-temporal loads
-      b[t] = buf_load16<kCacheStream>(wrs, lane * 16 + t * strip_bytes + gofs);
-      if constexpr (!PERCH) m[t] = a.meta[(int64_t(strip[t]) * a.G4q + (gm >> 2)) * 16 + c16];
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) b[t][v] = buf_load16<kCacheStream>(wrs, lane * 16 + v * 1024 + t * strip_bytes + gofs);
+      if constexpr (wf_group_meta(WF)) m[t] = a.meta[(int64_t(strip[t]) * a.G4q + (gm >> 2)) * 16 + c16];
     }
   };
   // Activations are read in whole 128-byte rows: one load covers 8 rows x one
@@ -286,22 +364,22 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
 
   // Multiply group g: its activations come out of LDS buffer (g - g0) % 2,
   // read here so that the fragments are live only while they are used.
-  auto compute = [&](int g, const u32x4 (&bc)[TN], const uint32_t (&mc)[TN]) {
+  auto compute = [&](int g, const u32x4 (&bc)[TN][kVec], const uint32_t (&mc)[TN]) {
     v4i af[TM][2];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         af[i][h] = *reinterpret_cast<const v4i*>(stage + ((g - g0) & 1) * (TM * 16 * 128) + lds_off(16 * i + c16, j + 4 * h));
-    if constexpr (!PERCH) {
+    if constexpr (wf_group_meta(WF)) {
 #pragma unroll
-      for (int t = 0; t < TN; ++t) meta_g128((mc[t] >> (8 * (g & 3))) & 0xffu, S[t], C[t]);
+      for (int t = 0; t < TN; ++t) meta_g128<WF>((mc[t] >> (8 * (g & 3))) & 0xffu, S[t], C[t]);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
       for (int t = 0; t < TN; ++t) {
-        const v4i bf = dequant16(h ? bc[t][2] : bc[t][0], h ? bc[t][3] : bc[t][1], S[t], C[t]);
+        const v4i bf = b_op16<WF>(bc[t], h, S[t], C[t]);
 #pragma unroll
         for (int i = 0; i < TM; ++i) acc[i][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i][h], bf, acc[i][t], 0, 0, 0);
       }
@@ -434,7 +512,7 @@ __device__ __forceinline__ int strip_lds_off(int lrow, int q) { return lrow * 12
 // operations of this wave are outstanding, leaving the other counters free.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <int PF, bool PERCH, bool I32OUT>
+template <int PF, int WF, bool I32OUT>
 __global__ __launch_bounds__(512) void gemm_strip_kernel(GemmArgs a, int spb, int ks) {
   extern __shared__ __align__(16) int8_t smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -450,8 +528,9 @@ __global__ __launch_bounds__(512) void gemm_strip_kernel(GemmArgs a, int spb, in
   const int R = min(a.M, 16);
   const int g0 = (a.G * wk) / ks, g1 = (a.G * (wk + 1)) / ks, ng = g1 - g0;
 
+  constexpr int kVec = wf_vec(WF);
   uint32_t S = 0, C = 0;
-  if constexpr (PERCH) meta_perchannel(a.meta8[cstrip * 16 + c16], S, C);
+  if constexpr (WF == kWfPerChannel) meta_perchannel(a.meta8[cstrip * 16 + c16], S, C);
 
   // activations -> LDS.  Lane l of a wave-wide copy fills LDS chunk base + l;
   // lanes past the end fetch a valid chunk into the allocation's padding.
@@ -467,7 +546,7 @@ __global__ __launch_bounds__(512) void gemm_strip_kernel(GemmArgs a, int spb, in
   // group metadata of the block's strips -> LDS, after the activations (the
   // strips' metadata is one contiguous run of G4q * 64 bytes per strip)
   const int act_bytes = round_up_lds(n_chunks * 16);
-  if constexpr (!PERCH) {
+  if constexpr (wf_group_meta(WF)) {
     const int m_chunks = min(spb, a.n_strips - sb) * a.G4q * 4;
     const int8_t* msrc = reinterpret_cast<const int8_t*>(a.meta) + int64_t(sb) * a.G4q * 64;
     for (int base = wave * 64; base < m_chunks; base += nwaves * 64) {
@@ -480,10 +559,15 @@ __global__ __launch_bounds__(512) void gemm_strip_kernel(GemmArgs a, int spb, in
 
   // weights: one descriptor over this wave's strip (empty past N), PF groups
   // in flight from here on
-  const int strip_bytes = a.G * 1024;
-  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(a.qw + int64_t(cstrip) * a.G * 64, live ? strip_bytes : 0);
-  u32x4 bq[PF];
-  auto load_b = [&](int g, u32x4& b) { b = buf_load16<kCacheStream>(wrs, lane * 16 + (g < g1 ? g * 1024 : kDeadOffset)); };
+  constexpr int kBlk = wf_block_bytes(WF);
+  const int strip_bytes = a.G * kBlk;
+  const __amdgpu_buffer_rsrc_t wrs =
+      make_rsrc(reinterpret_cast<const int8_t*>(a.qw) + int64_t(cstrip) * strip_bytes, live ? strip_bytes : 0);
+  u32x4 bq[PF][kVec];
+  auto load_b = [&](int g, u32x4 (&b)[kVec]) {
+#pragma unroll
+    for (int v = 0; v < kVec; ++v) b[v] = buf_load16<kCacheStream>(wrs, lane * 16 + v * 1024 + (g < g1 ? g * kBlk : kDeadOffset));
+  };
   // Wait for this wave's direct-to-LDS copies only (they were issued before
   // the weight loads, and loads retire in order), then meet the other waves.
   // A plain __syncthreads would also wait for the PF weight loads and drain
@@ -492,19 +576,19 @@ __global__ __launch_bounds__(512) void gemm_strip_kernel(GemmArgs a, int spb, in
   // main loop is entered on a single path.
 #pragma unroll
   for (int p = 0; p < PF; ++p) load_b(g0 + p, bq[p]);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(PF));
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(PF * kVec));
   __builtin_amdgcn_s_barrier();
   QOQ_COMPILER_FENCE();
 
   const int ra = c16 < R ? c16 : 0;  // rows past M reuse row 0; they are never stored
   v4i acc = {0, 0, 0, 0};
-  auto compute = [&](int g, const u32x4& bc) {
-    if constexpr (!PERCH) meta_g128((lmeta[(g >> 2) * 16] >> (8 * (g & 3))) & 0xffu, S, C);
+  auto compute = [&](int g, const u32x4 (&bc)[kVec]) {
+    if constexpr (wf_group_meta(WF)) meta_g128<WF>((lmeta[(g >> 2) * 16] >> (8 * (g & 3))) & 0xffu, S, C);
     const int lrow = g * R + ra;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const v4i af = *reinterpret_cast<const v4i*>(smem + strip_lds_off(lrow, j + 4 * h));
-      const v4i bf = dequant16(h ? bc[2] : bc[0], h ? bc[3] : bc[1], S, C);
+      const v4i bf = b_op16<WF>(bc, h, S, C);
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf, acc, 0, 0, 0);
     }
   };
@@ -593,27 +677,51 @@ __device__ __forceinline__ void a_store(const u32x4 (&r)[NA], int8_t* lds) {
   }
 }
 
-template <int TN, bool PERCH>
-__device__ __forceinline__ void b_load(u32x4 (&b)[TN][2], uint32_t (&m)[TN], const GemmArgs& a, const int (&strip)[TN],
-                                       int c16, int hh, int g) {
+// 16-byte weight loads per lane, per 32-column tile and group: UINT4 slots
+// (c16, hh) and (c16, 2+hh) hold K steps {0, 2} and {1, 3}; INT8 slots hold
+// one K step each.
+constexpr int wf_large_vec(int wf) { return wf == kWfW8 ? 4 : 2; }
+
+template <int TN, int WF>
+__device__ __forceinline__ void b_load(u32x4 (&b)[TN][wf_large_vec(WF)], uint32_t (&m)[TN], const GemmArgs& a,
+                                       const int (&strip)[TN], int c16, int hh, int g) {
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
-    const u32x4* blk = a.qw + (int64_t(strip[t]) * a.G + g) * 64;
-    b[t][0] = blk[c16 + 16 * hh];
-    b[t][1] = blk[c16 + 16 * (2 + hh)];
-    if constexpr (!PERCH) m[t] = a.meta[(int64_t(strip[t]) * a.G4q + (g >> 2)) * 16 + c16];
+    if constexpr (WF == kWfW8) {
+      // K step s of lane (c32, hh) is K chunk 2s + hh = 16j + 64h of slot c16 + 16j + 64h
+      const u32x4* blk = a.qw + (int64_t(strip[t]) * a.G + g) * 128;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) b[t][st] = blk[c16 + 16 * ((2 * st + hh) & 3) + 64 * ((2 * st + hh) >> 2)];
+    } else {
+      const u32x4* blk = a.qw + (int64_t(strip[t]) * a.G + g) * 64;
+      b[t][0] = blk[c16 + 16 * hh];
+      b[t][1] = blk[c16 + 16 * (2 + hh)];
+    }
+    if constexpr (wf_group_meta(WF)) m[t] = a.meta[(int64_t(strip[t]) * a.G4q + (g >> 2)) * 16 + c16];
+  }
+}
+
+// 32x32x32 B operand of K step s from one lane's loads of a group.
+template <int WF>
+__device__ __forceinline__ v4i b_op32(const u32x4 (&b)[wf_large_vec(WF)], int s, uint32_t S, uint32_t C) {
+  if constexpr (WF == kWfW8) {
+    return __builtin_bit_cast(v4i, b[s]);
+  } else {
+    const u32x4& q = b[s & 1];
+    if constexpr (WF == kWfG128Sat) return dequant16_sat((s >> 1) ? q[2] : q[0], (s >> 1) ? q[3] : q[1], S, C);
+    else return dequant16((s >> 1) ? q[2] : q[0], (s >> 1) ? q[3] : q[1], S, C);
   }
 }
 
 // Multiply one 128-wide K group: 4 K steps of 32.  Weight slot 0 of a column
 // tile holds K steps 0 and 2 (low / high half), slot 1 holds steps 1 and 3.
-template <int TM, int TN, bool PERCH>
-__device__ __forceinline__ void large_group(v16i (&acc)[TM][TN], const int8_t* lds, const u32x4 (&b)[TN][2],
-                                            const uint32_t (&m)[TN], uint32_t (&S)[TN], uint32_t (&C)[TN], int g,
-                                            int row0, int c32, int hh) {
-  if constexpr (!PERCH) {
+template <int TM, int TN, int WF>
+__device__ __forceinline__ void large_group(v16i (&acc)[TM][TN], const int8_t* lds,
+                                            const u32x4 (&b)[TN][wf_large_vec(WF)], const uint32_t (&m)[TN],
+                                            uint32_t (&S)[TN], uint32_t (&C)[TN], int g, int row0, int c32, int hh) {
+  if constexpr (wf_group_meta(WF)) {
 #pragma unroll
-    for (int t = 0; t < TN; ++t) meta_g128((m[t] >> (8 * (g & 3))) & 0xffu, S[t], C[t]);
+    for (int t = 0; t < TN; ++t) meta_g128<WF>((m[t] >> (8 * (g & 3))) & 0xffu, S[t], C[t]);
   }
   // A fragments are double-buffered across the 4 K steps: the reads of step
   // s+1 are issued before the multiplies of step s, so LDS latency hides
@@ -633,8 +741,7 @@ __device__ __forceinline__ void large_group(v16i (&acc)[TM][TN], const int8_t* l
 #endif
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
-      const u32x4& q = b[t][s & 1];
-      const v4i bf = dequant16((s >> 1) ? q[2] : q[0], (s >> 1) ? q[3] : q[1], S[t], C[t]);
+      const v4i bf = b_op32<WF>(b[t], s, S[t], C[t]);
 #pragma unroll
       for (int i = 0; i < TM; ++i) acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[s & 1][i], bf, acc[i][t], 0, 0, 0);
     }
@@ -642,7 +749,7 @@ __device__ __forceinline__ void large_group(v16i (&acc)[TM][TN], const int8_t* l
 }
 
 
-template <int WM, int WN, int TM, int TN, int D, int DA, bool PERCH, bool I32OUT>
+template <int WM, int WN, int TM, int TN, int D, int DA, int WF, bool I32OUT>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
   static_assert(D % 2 == 0, "ring depth must be even (LDS ping-pong parity)");
   static_assert(D % DA == 0, "the activation ring must tile the weight ring");
@@ -682,8 +789,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
 #pragma unroll
   for (int t = 0; t < TN; ++t) strip[t] = min((n0 + 32 * t + c32) >> 4, a.n_strips - 1);
 
-  uint32_t S[TN], C[TN];
-  if constexpr (PERCH) {
+  uint32_t S[TN] = {}, C[TN] = {};
+  if constexpr (WF == kWfPerChannel) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) meta_perchannel(a.meta8[strip[t] * 16 + c16], S[t], C[t]);
   }
@@ -705,7 +812,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
   // activations loaded DA steps earlier: DA steps of work must cover the
   // load latency.
   u32x4 ra[DA][NA];
-  u32x4 rb[D][TN][2];
+  u32x4 rb[D][TN][wf_large_vec(WF)];
   uint32_t rm[D][TN];
   const int n = ge - gb;
   auto gcl = [&](int l) { return gb + min(l, n - 1); };
@@ -715,7 +822,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
 #pragma unroll
   for (int d = 1; d <= DA; ++d) a_load<NA, THREADS>(ra[d % DA], a, K, m0, gcl(d));
 #pragma unroll
-  for (int d = 0; d < D; ++d) b_load<TN, PERCH>(rb[d], rm[d], a, strip, c16, hh, gcl(d));
+  for (int d = 0; d < D; ++d) b_load<TN, WF>(rb[d], rm[d], a, strip, c16, hh, gcl(d));
   __syncthreads();
 
   int l0 = 0;
@@ -726,9 +833,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
       a_store<NA, THREADS>(ra[(u + 1) % DA], (u & 1) ? As0 : As1);
       a_load<NA, THREADS>(ra[(u + 1) % DA], a, K, m0, gcl(l + 1 + DA));
       QOQ_COMPILER_FENCE();
-      large_group<TM, TN, PERCH>(acc, (u & 1) ? As1 : As0, rb[u], rm[u], S, C, gb + l, row0, c32, hh);
+      large_group<TM, TN, WF>(acc, (u & 1) ? As1 : As0, rb[u], rm[u], S, C, gb + l, row0, c32, hh);
       __syncthreads();
-      b_load<TN, PERCH>(rb[u], rm[u], a, strip, c16, hh, gcl(l + D));
+      b_load<TN, WF>(rb[u], rm[u], a, strip, c16, hh, gcl(l + D));
       QOQ_COMPILER_FENCE();
     }
   }
@@ -738,7 +845,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
   for (int u = 0; u < D; ++u) {
     if (u < rem) {
       if (u + 1 < rem) a_store<NA, THREADS>(ra[(u + 1) % DA], (u & 1) ? As0 : As1);
-      large_group<TM, TN, PERCH>(acc, (u & 1) ? As1 : As0, rb[u], rm[u], S, C, gb + l0 + u, row0, c32, hh);
+      large_group<TM, TN, WF>(acc, (u & 1) ? As1 : As0, rb[u], rm[u], S, C, gb + l0 + u, row0, c32, hh);
       __syncthreads();
     }
   }
@@ -848,10 +955,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const int* __restric
 #endif
 constexpr int kStripWavesTarget = 1024;  // 4 waves per CU
 
-template <int TM, int TN, int KS, int PF, int AD, bool PERCH, bool I32>
+template <int TM, int TN, int KS, int PF, int AD, int WF, bool I32>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
   const dim3 grid((a.n_strips + TN - 1) / TN, (a.M + TM * 16 - 1) / (TM * 16));
-  hipLaunchKernelGGL((gemm_skinny_kernel<TM, TN, KS, PF, AD, PERCH, I32>), grid, dim3(64 * KS), 0, st, a);
+  hipLaunchKernelGGL((gemm_skinny_kernel<TM, TN, KS, PF, AD, WF, I32>), grid, dim3(64 * KS), 0, st, a);
   return hipGetLastError();
 }
 
@@ -876,39 +983,40 @@ inline int pick_skinny_tn(int n_strips, int ny, int hi) {
 #define QOQ_SAD 2
 #endif
 // Most strips per skinny block: 8, or 7 with 64-row tiles (eight would not
-// fit the register file beside four row tiles of accumulators).
-constexpr int skinny_tn_max(int tm) { return tm >= 4 ? 7 : 8; }
+// fit the register file beside four row tiles of accumulators); 6 for INT8
+// weights, whose ring holds twice the bytes per strip.
+constexpr int skinny_tn_max(int tm, int wf = kWfG128) { return wf == kWfW8 ? 6 : (tm >= 4 ? 7 : 8); }
 
-template <int TM, bool PERCH, bool I32>
-hipError_t dispatch_skinny_tn(const GemmArgs& a, hipStream_t st) {
-  constexpr int KS = QOQ_SKS4, PF = QOQ_SPF, AD = QOQ_SAD;
-  constexpr int kHi = skinny_tn_max(TM);
-  switch (pick_skinny_tn(a.n_strips, (a.M + TM * 16 - 1) / (TM * 16), kHi)) {
-    case 1: return launch_skinny<TM, 1, KS, PF, AD, PERCH, I32>(a, st);
-    case 2: return launch_skinny<TM, 2, KS, PF, AD, PERCH, I32>(a, st);
-    case 3: return launch_skinny<TM, 3, KS, PF, AD, PERCH, I32>(a, st);
-    case 4: return launch_skinny<TM, 4, KS, PF, AD, PERCH, I32>(a, st);
-    case 5: return launch_skinny<TM, 5, KS, PF, AD, PERCH, I32>(a, st);
-    case 6: return launch_skinny<TM, 6, KS, PF, AD, PERCH, I32>(a, st);
-    case 7: return launch_skinny<TM, 7, KS, PF, AD, PERCH, I32>(a, st);
-    default: return launch_skinny<TM, kHi, KS, PF, AD, PERCH, I32>(a, st);
+// launch_skinny with TN = tn, instantiated for 1 <= TN <= T only
+template <int TM, int WF, bool I32, int T>
+hipError_t launch_skinny_upto(int tn, const GemmArgs& a, hipStream_t st) {
+  if constexpr (T > 1) {
+    if (tn < T) return launch_skinny_upto<TM, WF, I32, T - 1>(tn, a, st);
   }
+  return launch_skinny<TM, T, QOQ_SKS4, QOQ_SPF, QOQ_SAD, WF, I32>(a, st);
+}
+
+template <int TM, int WF, bool I32>
+hipError_t dispatch_skinny_tn(const GemmArgs& a, hipStream_t st) {
+  constexpr int kHi = skinny_tn_max(TM, WF);
+  const int tn = pick_skinny_tn(a.n_strips, (a.M + TM * 16 - 1) / (TM * 16), kHi);
+  return launch_skinny_upto<TM, WF, I32, kHi>(tn, a, st);
 }
 
 // Dynamic LDS of the strip kernel: the activations, or the K-part partial
 // sums, whichever is larger.
-inline size_t strip_lds_bytes(int G, int R, int spb, int ks, bool perch) {
+inline size_t strip_lds_bytes(int G, int R, int spb, int ks, bool group_meta) {
   const size_t act = size_t(round_up(int64_t(G) * R * 8 * 16, 1024));
-  const size_t meta = perch ? 0 : size_t(round_up(int64_t(spb) * round_up(G, 4) / 4 * 64, 1024));
+  const size_t meta = group_meta ? size_t(round_up(int64_t(spb) * round_up(G, 4) / 4 * 64, 1024)) : 0;
   const size_t red = size_t(spb) * size_t(ks - 1) * 1024;
   return act + meta > red ? act + meta : red;
 }
 constexpr size_t kStripMaxLds = 160 * 1024;
 
-template <bool PERCH, bool I32>
+template <int WF, bool I32>
 hipError_t launch_strip(const GemmArgs& a, int spb, int ks, size_t lds, hipStream_t st) {
   constexpr int PF = QOQ_S1PF;
-  auto* fn = gemm_strip_kernel<PF, PERCH, I32>;
+  auto* fn = gemm_strip_kernel<PF, WF, I32>;
   if (lds > 64 * 1024) {
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(kStripMaxLds));
@@ -922,15 +1030,15 @@ hipError_t launch_strip(const GemmArgs& a, int spb, int ks, size_t lds, hipStrea
 // Up to 16 rows: the strip kernel when the activations fit in LDS, else the
 // K-split skinny kernel.  Strips per block as for the skinny kernel (rounds of
 // 256 blocks); the K split fills a block up to 8 waves.
-template <bool PERCH, bool I32>
+template <int WF, bool I32>
 hipError_t dispatch_skinny_strip(const GemmArgs& a, hipStream_t st) {
   const int R = a.M < 16 ? a.M : 16;
   const int spb = pick_skinny_tn(a.n_strips, 1, 8);
   int ks = 8 / spb;
   if (ks < 1) ks = 1;
-  const size_t lds = strip_lds_bytes(a.G, R, spb, ks, PERCH);
-  if (lds <= kStripMaxLds) return launch_strip<PERCH, I32>(a, spb, ks, lds, st);
-  return dispatch_skinny_tn<1, PERCH, I32>(a, st);
+  const size_t lds = strip_lds_bytes(a.G, R, spb, ks, wf_group_meta(WF));
+  if (lds <= kStripMaxLds) return launch_strip<WF, I32>(a, spb, ks, lds, st);
+  return dispatch_skinny_tn<1, WF, I32>(a, st);
 }
 
 
@@ -992,34 +1100,38 @@ inline size_t workspace_bytes_of(int64_t M, int64_t N, int64_t K) {
   return p.ksplit > 1 ? size_t(p.ksplit) * size_t(M) * size_t(round_up(N, kStrip)) * sizeof(int) : 0;
 }
 
-template <int WM, int WN, int TM, int TN, int D, int DA, bool PERCH, bool I32>
+template <int WM, int WN, int TM, int TN, int D, int DA, int WF, bool I32>
 hipError_t launch_large(const GemmArgs& a, hipStream_t st) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   const dim3 grid((a.n_strips * 16 + BN - 1) / BN, (a.M + BM - 1) / BM, a.ksplit);
-  hipLaunchKernelGGL((gemm_large_kernel<WM, WN, TM, TN, D, DA, PERCH, I32>), grid, dim3(64 * WM * WN), 0, st, a);
+  hipLaunchKernelGGL((gemm_large_kernel<WM, WN, TM, TN, D, DA, WF, I32>), grid, dim3(64 * WM * WN), 0, st, a);
   return hipGetLastError();
 }
 
-template <bool PERCH, bool I32>
+template <int WF, bool I32>
 hipError_t launch_large_tile(int tile, const GemmArgs& a, hipStream_t st) {
-  if (tile == 0) return launch_large<QOQ_LWM, QOQ_LWN, QOQ_LTM, QOQ_LTN, QOQ_LD, QOQ_LDA, PERCH, I32>(a, st);
-  return launch_large<QOQ_SWM, QOQ_SWN, QOQ_STM, QOQ_STN, QOQ_SD, QOQ_SDA, PERCH, I32>(a, st);
+  // On the 256x256 tile the INT8 weight ring and the 16-bit lanes of the
+  // saturating dequantization leave room for one group of activations in
+  // flight instead of two (two would spill).
+  constexpr int kLDA = (WF == kWfW8 || WF == kWfG128Sat) ? 1 : QOQ_LDA;
+  if (tile == 0) return launch_large<QOQ_LWM, QOQ_LWN, QOQ_LTM, QOQ_LTN, QOQ_LD, kLDA, WF, I32>(a, st);
+  return launch_large<QOQ_SWM, QOQ_SWN, QOQ_STM, QOQ_STN, QOQ_SD, QOQ_SDA, WF, I32>(a, st);
 }
 
-template <bool PERCH, bool I32>
+template <int WF, bool I32>
 hipError_t dispatch(const GemmArgs& a0, void* ws, hipStream_t st) {
-  if (a0.M <= 16) return dispatch_skinny_strip<PERCH, I32>(a0, st);
-  if (a0.M <= 32) return dispatch_skinny_tn<2, PERCH, I32>(a0, st);
-  if (a0.M <= kSkinnyMaxM || skinny_mid(a0.M, a0.N)) return dispatch_skinny_tn<4, PERCH, I32>(a0, st);
+  if (a0.M <= 16) return dispatch_skinny_strip<WF, I32>(a0, st);
+  if (a0.M <= 32) return dispatch_skinny_tn<2, WF, I32>(a0, st);
+  if (a0.M <= kSkinnyMaxM || skinny_mid(a0.M, a0.N)) return dispatch_skinny_tn<4, WF, I32>(a0, st);
   const LargePlan p = plan_large(a0.M, a0.N, int64_t(a0.G) * kGroup);
-  if (p.ksplit == 1) return launch_large_tile<PERCH, I32>(p.tile, a0, st);
+  if (p.ksplit == 1) return launch_large_tile<WF, I32>(p.tile, a0, st);
   // split K: INT32 partials into the workspace, then reduce + epilogue
   GemmArgs a = a0;
   a.ksplit = p.ksplit;
   a.out = ws;
   a.ldo = int64_t(a.n_strips) * kStrip;
   a.zstride = int64_t(a.M) * a.ldo;
-  hipError_t e = launch_large_tile<PERCH, true>(p.tile, a, st);
+  hipError_t e = launch_large_tile<WF, true>(p.tile, a, st);
   if (e != hipSuccess) return e;
   const int ldw = a.n_strips * kStrip;
   const int64_t threads = int64_t(a.M) * (ldw / 8);
@@ -1032,17 +1144,22 @@ hipError_t dispatch(const GemmArgs& a0, void* ws, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Argument checks and launch of one weight format.  meta may be NULL for the
+// INT8 weights; group_size is the one of the UINT4 formats (128 or 0).
+template <int WF>
 int run_gemm(const char* fn, const int8_t* x8, const void* sx, const void* qweight, const void* meta,
              const void* scale, void* out, int64_t M, int64_t N, int64_t K, int64_t ldo, int32_t group_size,
              void* workspace, size_t workspace_bytes, bool i32, hipStream_t st) {
   clear_error();
-  if (!x8 || !qweight || !meta || !out || (!i32 && (!sx || !scale)))
+  const bool need_meta = WF != kWfW8;
+  if (!x8 || !qweight || (need_meta && !meta) || !out || (!i32 && (!sx || !scale)))
     return fail(QOQ_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   if (int stt = check_weight_shape(N, K, group_size)) return stt;
   if (M < 1 || M > 0x7fffffffLL - 4096) return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "%s: M=%lld out of range", fn, (long long)M);
   if (ldo < N) return fail(QOQ_ERR_INVALID_ARG, "%s: leading dimension %lld < N=%lld", fn, (long long)ldo, (long long)N);
   const auto al = [](const void* p, uintptr_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; };
-  if (!al(x8, 16) || !al(qweight, 16) || !al(meta, 4) || !al(out, i32 ? 4 : 2) || (!i32 && (!al(sx, 2) || !al(scale, 2))))
+  if (!al(x8, 16) || !al(qweight, 16) || (need_meta && !al(meta, 4)) || !al(out, i32 ? 4 : 2) ||
+      (!i32 && (!al(sx, 2) || !al(scale, 2))))
     return fail(QOQ_ERR_ALIGNMENT, "%s: x8/qweight need 16-byte, meta 4-byte, FP16 2-byte alignment", fn);
   GemmArgs a;
   a.x8 = x8;
@@ -1062,23 +1179,16 @@ int run_gemm(const char* fn, const int8_t* x8, const void* sx, const void* qweig
   a.zstride = 0;
   const size_t need = workspace_bytes_of(M, N, K);
   if (need && (!workspace || workspace_bytes < need))
-    return fail(QOQ_ERR_INVALID_ARG, "%s: workspace of %zu bytes required (got %zu); see qoq_w4a8_gemm_workspace_size",
+    return fail(QOQ_ERR_INVALID_ARG, "%s: workspace of %zu bytes required (got %zu); see the workspace-size query",
                 fn, need, workspace ? workspace_bytes : size_t(0));
   if (need && reinterpret_cast<uintptr_t>(workspace) % 16)
     return fail(QOQ_ERR_ALIGNMENT, "%s: workspace must be 16-byte aligned", fn);
-  hipError_t e;
-  if (group_size) e = i32 ? dispatch<false, true>(a, workspace, st) : dispatch<false, false>(a, workspace, st);
-  else e = i32 ? dispatch<true, true>(a, workspace, st) : dispatch<true, false>(a, workspace, st);
+  const hipError_t e = i32 ? dispatch<WF, true>(a, workspace, st) : dispatch<WF, false>(a, workspace, st);
   if (e != hipSuccess) return fail(QOQ_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return QOQ_OK;
 }
 
-}  // namespace
-}  // namespace qoq
-
-using namespace qoq;
-
-extern "C" size_t qoq_w4a8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_size) {
+inline size_t workspace_size_query(int64_t M, int64_t N, int64_t K, int32_t group_size) {
   if (M < 1 || check_weight_shape(N, K, group_size) != QOQ_OK) {
     clear_error();
     return 0;
@@ -1086,18 +1196,5 @@ extern "C" size_t qoq_w4a8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, 
   return workspace_bytes_of(M, N, K);
 }
 
-extern "C" int qoq_w4a8_gemm(const int8_t* x8, const void* sx_fp16, const void* qweight, const void* meta,
-                             const void* scale_fp16, void* y_fp16, int64_t M, int64_t N, int64_t K, int64_t ldy,
-                             int32_t group_size, void* workspace, size_t workspace_bytes, void* stream) {
-  return run_gemm("qoq_w4a8_gemm", x8, sx_fp16, qweight, meta, scale_fp16, y_fp16, M, N, K, ldy, group_size,
-                  workspace, workspace_bytes, false,
-                  static_cast<hipStream_t>(stream));
-}
-
-extern "C" int qoq_w4a8_gemm_i32(const int8_t* x8, const void* qweight, const void* meta, int32_t* acc, int64_t M,
-                                 int64_t N, int64_t K, int64_t ldacc, int32_t group_size, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
-  return run_gemm("qoq_w4a8_gemm_i32", x8, nullptr, qweight, meta, nullptr, acc, M, N, K, ldacc, group_size,
-                  workspace, workspace_bytes, true,
-                  static_cast<hipStream_t>(stream));
-}
+}  // namespace
+}  // namespace qoq

@@ -227,6 +227,38 @@ bool encode_row_per_channel(const uint16_t* w, int64_t K, uint8_t* q4, uint8_t* 
   return true;
 }
 
+// Per-channel symmetric INT8 of one channel (the W8A8 comparator's weights):
+// s = fp16(max_k |W| / 127), q = clamp(round(W / s), -127, 127); a zero scale
+// gives a zero row.  Returns false on non-finite input.
+bool encode_row_w8(const uint16_t* w, int64_t K, int8_t* q, uint16_t* s_out) {
+  float b = 0.0f;
+  for (int64_t k = 0; k < K; ++k) {
+    const float v = half_to_float(w[k]);
+    if (!std::isfinite(v)) return false;
+    b = std::max(b, std::fabs(v));
+  }
+  const uint16_t sh = float_to_half_rne(b / 127.0f);
+  const float s = half_to_float(sh);
+  *s_out = sh;
+  for (int64_t k = 0; k < K; ++k)
+    q[k] = s == 0.0f ? int8_t(0) : int8_t(clampi(int(std::rint(half_to_float(w[k]) / s)), -127, 127));
+  return true;
+}
+
+// INT8 block of (strip, group): 128 slots of 16 bytes, slot c + 16j + 64h
+// holding input channels 128g + 64h + 16j + [0, 16) of channel c.
+void scatter_row_w8(const Dims& d, int64_t n, const int8_t* qrow, uint8_t* qw) {
+  const int64_t strip = n / kStrip;
+  const int c = int(n % kStrip);
+  for (int64_t g = 0; g < d.G; ++g) {
+    uint8_t* blk = qw + size_t(strip * d.G + g) * kBlockBytesW8;
+    for (int kl = 0; kl < kGroup; ++kl) {
+      const int slot = c + 16 * ((kl >> 4) & 3) + 64 * (kl >> 6);
+      blk[slot * 16 + (kl & 15)] = uint8_t(qrow[g * kGroup + kl]);
+    }
+  }
+}
+
 void write_meta_g128(const Dims& d, int64_t n, const uint8_t* s1, const uint8_t* z, uint8_t* meta) {
   for (int64_t g = 0; g < d.G; ++g) meta[meta_index(d, n, g)] = uint8_t((s1[g] - 1) | (z[g] << 4));
 }
@@ -308,6 +340,32 @@ extern "C" int qoq_pack_weights(const uint16_t* w_fp16, int64_t N, int64_t K, in
   });
   for (int64_t n = 0; n < N; ++n)
     if (bad[size_t(n)]) return fail(QOQ_ERR_INVALID_ARG, "qoq_pack_weights: non-finite weight in row %lld", (long long)n);
+  return QOQ_OK;
+}
+
+extern "C" int qoq_pack_weights_w8(const uint16_t* w_fp16, int64_t N, int64_t K, void* qweight8,
+                                   uint16_t* scale_fp16) {
+  clear_error();
+  if (int st = check_ptrs("qoq_pack_weights_w8", {w_fp16, qweight8, scale_fp16})) return st;
+  if (int st = check_weight_shape(N, K, kGroup)) return st;
+  const Dims d = dims_of(N, K, kGroup);
+  uint8_t* qw = static_cast<uint8_t*>(qweight8);
+  std::memset(qw, 0, size_t(d.N_pad) * size_t(K));
+  std::memset(scale_fp16, 0, size_t(d.N_pad) * 2);
+  std::vector<char> bad(size_t(N), 0);
+  parallel_rows(N, [&](int64_t n0, int64_t n1) {
+    std::vector<int8_t> q(static_cast<size_t>(K));
+    for (int64_t n = n0; n < n1; ++n) {
+      if (!encode_row_w8(w_fp16 + size_t(n) * size_t(K), K, q.data(), &scale_fp16[n])) {
+        bad[size_t(n)] = 1;
+        continue;
+      }
+      scatter_row_w8(d, n, q.data(), qw);
+    }
+  });
+  for (int64_t n = 0; n < N; ++n)
+    if (bad[size_t(n)])
+      return fail(QOQ_ERR_INVALID_ARG, "qoq_pack_weights_w8: non-finite weight in row %lld", (long long)n);
   return QOQ_OK;
 }
 

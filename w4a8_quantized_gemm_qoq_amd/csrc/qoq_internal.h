@@ -19,6 +19,7 @@ constexpr int kGroup = QOQ_GROUP;   // K-loop unit and g128 group size
 constexpr int kStrip = 16;          // output channels per packed strip
 constexpr int kSlots = 64;          // 16-byte slots per (strip, group) block
 constexpr int kBlockBytes = kSlots * 16;
+constexpr int kBlockBytesW8 = 2 * kBlockBytes;  // INT8 weights: 128 slots per (strip, group)
 
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
