@@ -44,6 +44,11 @@ def algo_bytes(w) -> int:
     return wq + meta + 2 * w.N + w.M * w.K + 2 * w.M + 2 * w.M * w.N
 
 
+def algo_bytes_w8(w) -> int:
+    """The same for the W8A8 comparator: INT8 weights and their FP16 scale."""
+    return w.N * w.K + 2 * w.N + w.M * w.K + 2 * w.M + 2 * w.M * w.N
+
+
 def act_bytes(w) -> int:
     return 2 * w.M * w.K + w.M * w.K + 2 * w.M
 
@@ -58,7 +63,7 @@ def src_hash() -> str:
     """Hash of the kernel sources' code (line comments and blank lines dropped),
     so that a stored traffic measurement goes stale only when code changes."""
     h = hashlib.sha256()
-    for f in ("gemm.hip", "act_quant.hip"):
+    for f in ("gemm_kernels.h", "gemm_w4.hip", "act_quant.hip"):
         with open(os.path.join(ROOT, "w4a8_quantized_gemm_qoq_amd", "csrc", f), encoding="utf-8") as fh:
             for line in fh:
                 code = line.split("//", 1)[0].rstrip()
@@ -115,14 +120,42 @@ def cpu_baseline(w, X, W, seconds: float):
             "seconds_per_step": el / reps}
 
 
-def measure_gemm(torch, q, w, X, W, reps: int):
-    """Kernel-level timing of the act quantizer and the GEMM for one workload."""
+def _copies(w, wbytes):
+    """Weight copies cycled from launch to launch so that the weights come
+    from HBM (one copy of a decode-size weight would stay in the 256 MB
+    last-level cache); one copy for the compute-bound prefill shapes."""
+    c = 1 if bound_of(w) == "mfma" and w.M >= 1024 else max(1, math.ceil(3 * MALL_BYTES / max(wbytes, 1)))
+    return min(c, 64)
+
+
+def measure_comparators(torch, q, w, W, x8, sx, y, ws, t_g, reps: int):
+    """The two comparators on the same inputs and launch plans: the W8A8
+    GEMM (INT8 weights, no dequantization) and the saturating-dequantization
+    ablation of the g128 GEMM."""
+    p8h = q.qoq_pack_weights_w8(W)
+    c8 = _copies(w, p8h.qweight.nbytes)
+    w8s = [p8h.to(x8.device) for _ in range(c8)]
+    for p8 in w8s:
+        q.qoq_w8a8_gemm(x8, sx, p8, y=y)
+    t8 = time_kernel(torch, lambda i: q.qoq_w8a8_gemm(x8, sx, w8s[i % c8], y=y), reps)
+    del w8s
+    r = {"w8a8_us": round(t8, 3), "w8a8_tops": round(w.ops / t8 / 1e6, 2),
+         "w8a8_gbs": round(algo_bytes_w8(w) / t8 / 1e3, 1), "w8a8_weight_copies": c8,
+         "w4a8_over_w8a8": round(t8 / t_g, 3)}
+    if w.group_size:
+        t_sat = time_kernel(torch, lambda i: q.qoq_w4a8_gemm_saturating(x8, sx, ws[i % len(ws)], y=y), reps)
+        r.update({"saturating_us": round(t_sat, 3), "saturating_slowdown": round(t_sat / t_g, 3)})
+    return r
+
+
+def measure_gemm(torch, q, w, X, W, reps: int, comparators: bool = False):
+    """Kernel-level timing of the act quantizer and the GEMM for one workload
+    (and, if asked, of the two comparators on the same inputs)."""
     import numpy as np
     dev = torch.device("cuda")
     packed_host = q.qoq_pack_weights(W, w.group_size)
     wbytes = packed_host.qweight.nbytes + packed_host.meta.nbytes
-    copies = 1 if bound_of(w) == "mfma" and w.M >= 1024 else max(1, math.ceil(3 * MALL_BYTES / max(wbytes, 1)))
-    copies = min(copies, 64)
+    copies = _copies(w, wbytes)
     ws = [packed_host.to(dev) for _ in range(copies)]
     x = torch.from_numpy(np.ascontiguousarray(X)).to(dev)
     x8 = torch.empty((w.M, w.K), dtype=torch.int8, device=dev)
@@ -139,11 +172,14 @@ def measure_gemm(torch, q, w, X, W, reps: int):
     tops = w.ops / t_g / 1e6
     gbs = b / t_g / 1e3
     frac = tops / PEAK_INT8_TOPS if bnd == "mfma" else gbs / PEAK_HBM_GBS
+    r = {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "group_size": w.group_size,
+         "gemm_us": round(t_g, 3), "tops": round(tops, 2), "gbs": round(gbs, 1), "bound": bnd,
+         "frac": round(frac, 4), "weight_copies": copies, "act_quant_us": round(t_q, 3),
+         "act_quant_gbs": round(act_bytes(w) / t_q / 1e3, 1)}
+    if comparators:
+        r.update(measure_comparators(torch, q, w, W, x8, sx, y, ws, t_g, reps))
     del ws
-    return {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "group_size": w.group_size,
-            "gemm_us": round(t_g, 3), "tops": round(tops, 2), "gbs": round(gbs, 1), "bound": bnd,
-            "frac": round(frac, 4), "weight_copies": copies, "act_quant_us": round(t_q, 3),
-            "act_quant_gbs": round(act_bytes(w) / t_q / 1e3, 1)}
+    return r
 
 
 def main():
@@ -155,6 +191,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--sweep", default=",".join(SWEEP), help="comma-separated workload names")
     ap.add_argument("--sweep-reps", type=int, default=20)
+    ap.add_argument("--no-comparators", action="store_true",
+                    help="skip the W8A8 comparator and the saturating ablation in the sweep")
     ap.add_argument("--kernel-reps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -295,7 +333,7 @@ def main():
             sw = synthetic.get_workload(name)
             SX, SW = synthetic.make_inputs(sw)
             try:
-                r = measure_gemm(torch, q, sw, SX, SW, args.sweep_reps)
+                r = measure_gemm(torch, q, sw, SX, SW, args.sweep_reps, comparators=not args.no_comparators)
             except Exception as ex:  # report, do not hide
                 r = {"workload": name, "error": repr(ex)}
             print(f"[sweep] {json.dumps(r)}", file=sys.stderr, flush=True)
@@ -303,6 +341,14 @@ def main():
             del SX, SW
             torch.cuda.empty_cache()
         out["sweep"] = sweep
+        if not args.no_comparators:
+            out["comparators"] = {
+                "w4a8_over_w8a8": {r["workload"]: r["w4a8_over_w8a8"] for r in sweep if "w4a8_over_w8a8" in r},
+                "saturating_slowdown": {r["workload"]: r["saturating_slowdown"] for r in sweep
+                                        if "saturating_slowdown" in r},
+                "note": "same kernels and plans; W8A8 = per-channel INT8 weights without dequantization; "
+                        "saturating = g128 GEMM with a clamping 16-bit-lane dequantization",
+            }
 
     if args.copy_calib_mb:
         n = args.copy_calib_mb * 2 ** 20

@@ -983,9 +983,11 @@ inline int pick_skinny_tn(int n_strips, int ny, int hi) {
 #define QOQ_SAD 2
 #endif
 // Most strips per skinny block: 8, or 7 with 64-row tiles (eight would not
-// fit the register file beside four row tiles of accumulators); 6 for INT8
-// weights, whose ring holds twice the bytes per strip.
-constexpr int skinny_tn_max(int tm, int wf = kWfG128) { return wf == kWfW8 ? 6 : (tm >= 4 ? 7 : 8); }
+// fit the register file beside four row tiles of accumulators).
+constexpr int skinny_tn_max(int tm) { return tm >= 4 ? 7 : 8; }
+// Weight-ring depth of the skinny kernel: the same bytes in flight for every
+// format (INT8 blocks are twice as large, so half as many groups).
+constexpr int skinny_pf(int wf) { return QOQ_SPF / wf_vec(wf); }
 
 // launch_skinny with TN = tn, instantiated for 1 <= TN <= T only
 template <int TM, int WF, bool I32, int T>
@@ -993,12 +995,12 @@ hipError_t launch_skinny_upto(int tn, const GemmArgs& a, hipStream_t st) {
   if constexpr (T > 1) {
     if (tn < T) return launch_skinny_upto<TM, WF, I32, T - 1>(tn, a, st);
   }
-  return launch_skinny<TM, T, QOQ_SKS4, QOQ_SPF, QOQ_SAD, WF, I32>(a, st);
+  return launch_skinny<TM, T, QOQ_SKS4, skinny_pf(WF), QOQ_SAD, WF, I32>(a, st);
 }
 
 template <int TM, int WF, bool I32>
 hipError_t dispatch_skinny_tn(const GemmArgs& a, hipStream_t st) {
-  constexpr int kHi = skinny_tn_max(TM, WF);
+  constexpr int kHi = skinny_tn_max(TM);
   const int tn = pick_skinny_tn(a.n_strips, (a.M + TM * 16 - 1) / (TM * 16), kHi);
   return launch_skinny_upto<TM, WF, I32, kHi>(tn, a, st);
 }
