@@ -64,6 +64,8 @@ __all__ = [
     "quant_weight_w8",
     "encode_weight_w8",
     "dequant_level1_saturating",
+    "rmsnorm_fp16",
+    "rmsnorm_quant_per_token",
 ]
 
 ACT_QMAX = 127   # symmetric INT8 activation range [-127, 127]
@@ -370,3 +372,51 @@ def dequant_level1_saturating(q4, s1, z, group=GROUP):
     ``dequant_level1`` (their values stay within [-121, 121]).
     """
     return np.clip(dequant_level1(q4, s1, z, group), -128, 127)
+
+
+# ------------------------------------------------------- fused producer (f2)
+
+def rmsnorm_fp16(X, gamma, eps):
+    """RMS normalization of FP16 token rows, rounded to FP16.
+
+    [PL §5, runtime and precision mapping]: activation quantization is fused
+    into the preceding normalization layer; what is fused is the RMS
+    normalization of the token (x / rms(x) * gamma, the Llama-family norm)
+    followed by the per-token INT8 quantization.  The pages give no
+    arithmetic, so the statistic is taken exactly and rounded once:
+      S    = sum_k x_k^2, exact (every FP16 value is an integer times 2^-24,
+             so S is an integer times 2^-48: Python integers hold it);
+      ms   = fp32(fp64(S) / K)        -- S rounded to FP64, IEEE division;
+      r    = 1 / sqrt(ms + eps)       -- FP32 add, sqrt and division;
+      h_k  = fp16((x_k * r) * gamma_k) -- two FP32 products, then FP16.
+    Every step is a single correctly rounded IEEE operation, so the result
+    does not depend on any summation order.
+
+    Returns h float16 [M, K].
+    """
+    X16 = np.asarray(X, dtype=np.float16)
+    g32 = np.asarray(gamma, dtype=np.float16).astype(np.float32)
+    M, K = X16.shape
+    if g32.shape != (K,):
+        raise ValueError("gamma must have K entries")
+    eps32 = np.float32(eps)
+    if not eps32 > 0:
+        raise ValueError("eps must be positive")
+    units = (X16.astype(np.float64) * 2.0 ** 24).astype(np.int64)  # exact integers
+    h = np.empty((M, K), np.float16)
+    for m in range(M):
+        S = sum(v * v for v in units[m].tolist())
+        ms = np.float32(float(S) * 2.0 ** -48 / K)
+        r = np.float32(1.0) / np.sqrt(np.float32(ms + eps32))
+        h[m] = ((X16[m].astype(np.float32) * r) * g32).astype(np.float16)
+    return h
+
+
+def rmsnorm_quant_per_token(X, gamma, eps):
+    """Fused producer: RMS normalization then per-token INT8 quantization.
+
+    The quantization is ``quant_act_per_token`` applied to the FP16
+    normalized rows of ``rmsnorm_fp16`` -- fusing the two moves no value.
+    Returns (x8 int8 [M,K], s_x float16 [M]).
+    """
+    return quant_act_per_token(rmsnorm_fp16(X, gamma, eps))

@@ -359,3 +359,72 @@ def test_saturating_dequant_is_exact_inside_the_protective_range():
     enc = O.encode_weight_g128(W)
     sat = O.dequant_level1_saturating(enc["q4"], enc["s1"], enc["z"])
     assert np.array_equal(sat, enc["w8"])
+
+
+# ------------------------------------------------------- fused producer (f2)
+
+def test_rmsnorm_quant_hand_worked_rows():
+    fx = read_fixture("rmsnorm_quant_rows.txt")
+    eps = fx["eps"][0]
+    assert eps == 2.0 ** -40
+    for r in "ab":
+        X = np.array([fx["x" + r]], np.float16)
+        g = np.array(fx["g" + r], np.float16)
+        h = O.rmsnorm_fp16(X, g, eps)
+        assert h[0].astype(np.float64).tolist() == fx["h" + r]
+        x8, sx = O.rmsnorm_quant_per_token(X, g, eps)
+        assert float(sx[0]) == fx["s" + r][0]
+        assert x8[0].tolist() == [int(v) for v in fx["q" + r]]
+
+
+def test_rmsnorm_power_of_two_row_scaling_is_invisible():
+    # scaling a row by 2^j scales the exact mean square by 4^j and the rms by
+    # 2^j exactly, so with eps below the last bit nothing downstream changes
+    X = synthetic.make_x(8, 512, "frac", seed=3)
+    g = (synthetic.make_w(1, 512, seed=4)[0] * 40).astype(np.float16)
+    x8, sx = O.rmsnorm_quant_per_token(X, g, 2.0 ** -60)
+    for j in (-3, 2):
+        x8j, sxj = O.rmsnorm_quant_per_token((X.astype(np.float32) * 2.0 ** j).astype(np.float16), g, 2.0 ** -60)
+        assert np.array_equal(x8j, x8) and np.array_equal(sxj, sx)
+
+
+def test_rmsnorm_constant_row_reduces_to_plain_quantizer():
+    # a constant row of c = +-2^j has rms |c|, so x * r = +-1 exactly and the
+    # fused producer must equal the plain per-token quantizer of +-gamma
+    K = 384
+    g = (synthetic.make_w(1, K, seed=11)[0] * 100).astype(np.float16)
+    for c in (0.125, -4.0, 1.0):
+        X = np.full((1, K), c, np.float16)
+        x8, sx = O.rmsnorm_quant_per_token(X, g, 2.0 ** -50)
+        ref8, refs = O.quant_act_per_token((np.sign(c) * g.astype(np.float32))[None, :].astype(np.float16))
+        assert np.array_equal(x8, ref8) and np.array_equal(sx, refs)
+
+
+def test_rmsnorm_mean_square_is_exact():
+    # small integers: the FP64 mean of squares is exact, so ms must equal it;
+    # and one huge plus many tiny entries, where the exact sum still rounds
+    # to the same FP32 as the huge square alone
+    rng = np.random.default_rng(2)
+    X = rng.integers(-30, 31, size=(5, 256)).astype(np.float16)
+    g = np.ones(256, np.float16)
+    h = O.rmsnorm_fp16(X, g, 2.0 ** -60)
+    ms = np.mean(X.astype(np.float64) ** 2, axis=1).astype(np.float32)
+    r = np.float32(1) / np.sqrt(ms)
+    assert np.array_equal(h, (X.astype(np.float32) * r[:, None]).astype(np.float16))
+    Y = np.full((1, 1024), 2.0 ** -24, np.float16)
+    Y[0, 0] = 60000.0
+    hy = O.rmsnorm_fp16(Y, np.ones(1024, np.float16), 2.0 ** -60)
+    assert float(hy[0, 0]) == 32.0       # 60000 / (60000 / 32) = 32: rms = 60000 / sqrt(1024)
+    assert float(hy[0, 1]) == 0.0        # 2^-24 / 1875 underflows FP16
+
+
+def test_rmsnorm_zero_row_and_bad_args():
+    X = np.zeros((2, 128), np.float16)
+    X[1, 3] = 1.0
+    x8, sx = O.rmsnorm_quant_per_token(X, np.ones(128, np.float16), 1e-5)
+    assert float(sx[0]) == 0 and not x8[0].any()
+    assert x8[1, 3] == 127 and int(np.count_nonzero(x8[1])) == 1
+    with pytest.raises(ValueError):
+        O.rmsnorm_fp16(X, np.ones(128, np.float16), 0.0)
+    with pytest.raises(ValueError):
+        O.rmsnorm_fp16(X, np.ones(64, np.float16), 1e-5)
