@@ -162,6 +162,26 @@ QOQ_API int qoq_unpack_weights(const void* qweight, const void* meta, const uint
 QOQ_API int qoq_quant_act_per_token(const void* x_fp16, int64_t M, int64_t K, int64_t ldx,
                             int8_t* x8, void* sx_fp16, void* stream);
 
+/*
+ * Fused producer (device): RMS normalization of each token row, then the
+ * per-token INT8 quantization above, in one kernel that reads x once and
+ * writes only x8 and s_x.  [PL §5, runtime and precision mapping: activation
+ * quantization is fused into the preceding normalization layer].  Per row m:
+ *   S    = sum_k x[m,k]^2, exact (FP16 squares are integers times 2^-48);
+ *   ms   = fp32(fp64(S) / K), r = 1 / sqrt(ms + eps) (FP32 IEEE add, sqrt and
+ *          divide);
+ *   h[k] = fp16((x[m,k] * r) * gamma[k]) (two FP32 products, round half even);
+ *   then s_x[m] and x8[m,:] from h exactly as qoq_quant_act_per_token.
+ * Each step rounds once, so the result does not depend on the launch shape.
+ * x_fp16: device [M][ldx] FP16, ldx >= K.  gamma_fp16: device [K] FP16.
+ * eps > 0 and finite (QOQ_ERR_INVALID_ARG otherwise).  x8: device [M][K]
+ * int8.  sx_fp16: device [M].  Vector path when K and ldx are multiples of 8
+ * and x, gamma are 16-byte aligned (else a scalar path).  Non-finite x or an
+ * FP16 overflow of h is undefined behaviour.
+ */
+QOQ_API int qoq_rmsnorm_quant_per_token(const void* x_fp16, const void* gamma_fp16, float eps, int64_t M, int64_t K,
+                                int64_t ldx, int8_t* x8, void* sx_fp16, void* stream);
+
 /* Device workspace (bytes) qoq_w4a8_gemm / qoq_w4a8_gemm_i32 need for this
  * shape; 0 means the workspace arguments may be NULL / 0. */
 QOQ_API size_t qoq_w4a8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_size);

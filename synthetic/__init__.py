@@ -12,7 +12,9 @@ Recipe (seed 0 unless stated):
     by 20 (channels {3, 77} for the tiny and attention-projection shapes,
     otherwise ceil(0.5% of K) channels drawn without replacement); then cast
     to FP16;
-  * W = 0.02 * standard normal FP32 [N, K], cast to FP16.
+  * W = 0.02 * standard normal FP32 [N, K], cast to FP16;
+  * gamma (the weight of the normalization before a quantized layer)
+    = 1 + 0.1 * standard normal FP32 [K], cast to FP16, from a fourth stream.
 The weight stream does not depend on M, so workloads that share (N, K) share
 W, and a smaller M takes the first rows of the largest M's draw.
 """
@@ -24,7 +26,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "get_workload", "make_x", "make_w", "make_inputs"]
+__all__ = ["Workload", "WORKLOADS", "get_workload", "make_x", "make_w", "make_gamma", "make_inputs"]
 
 
 @dataclass(frozen=True)
@@ -104,6 +106,14 @@ def make_w(N: int, K: int, seed: int = 0) -> np.ndarray:
     W32 = rw.standard_normal((N, K), dtype=np.float32)
     W32 *= np.float32(0.02)
     return W32.astype(np.float16)
+
+
+def make_gamma(K: int, seed: int = 0) -> np.ndarray:
+    """FP16 normalization weight [K]: 1 + 0.1 N(0, 1) (a fourth stream; the
+    first three are those of ``_streams``)."""
+    rg = np.random.default_rng(np.random.SeedSequence(seed).spawn(4)[3])
+    g32 = np.float32(1.0) + np.float32(0.1) * rg.standard_normal(K, dtype=np.float32)
+    return g32.astype(np.float16)
 
 
 def make_inputs(w: Workload | str, seed: int = 0, M: int | None = None):

@@ -25,7 +25,7 @@ def header_symbols():
 def test_library_exports_every_header_symbol():
     lib = q.load_library()
     syms = header_symbols()
-    assert len(syms) == 16, syms
+    assert len(syms) == 17, syms
     assert sorted(_native.EXPORTS) == syms
     for s in syms:
         assert hasattr(lib, s), s
@@ -316,3 +316,14 @@ def test_comparator_entry_points_validate_before_launch():
     assert lib.qoq_w4a8_gemm_saturating_i32(d, d, d, d, 4, 16, 100, 16, None, 0, None) == 2
     assert lib.qoq_w8a8_gemm_workspace_size(4, 16, 128) == 0
     assert lib.qoq_w8a8_gemm_workspace_size(300, 96, 2048) == lib.qoq_w4a8_gemm_workspace_size(300, 96, 2048, 128)
+
+
+def test_rmsnorm_quant_validates_before_launch():
+    lib = q.load_library()
+    d = 4096
+    assert lib.qoq_rmsnorm_quant_per_token(None, d, 1e-5, 4, 128, 128, d, d, None) == 1
+    assert lib.qoq_rmsnorm_quant_per_token(d, d, 0.0, 4, 128, 128, d, d, None) == 1       # eps must be > 0
+    assert lib.qoq_rmsnorm_quant_per_token(d, d, float("inf"), 4, 128, 128, d, d, None) == 1
+    assert lib.qoq_rmsnorm_quant_per_token(d, d, 1e-5, 4, 128, 64, d, d, None) == 1       # ldx < K
+    assert lib.qoq_rmsnorm_quant_per_token(d, d, 1e-5, 0, 128, 128, d, d, None) == 2
+    assert lib.qoq_rmsnorm_quant_per_token(d + 1, d, 1e-5, 4, 128, 128, d, d, None) == 3  # odd FP16 pointer

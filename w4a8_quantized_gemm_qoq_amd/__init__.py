@@ -15,6 +15,7 @@ from ._native import (  # noqa: F401
     qoq_pack_codes,
     qoq_pack_weights,
     qoq_quant_act_per_token,
+    qoq_rmsnorm_quant_per_token,
     qoq_unpack_weights,
     qoq_w4a8_forward,
     qoq_w4a8_gemm,

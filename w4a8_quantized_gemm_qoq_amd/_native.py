@@ -27,6 +27,7 @@ EXPORTS = [
     "qoq_pack_codes",
     "qoq_unpack_weights",
     "qoq_quant_act_per_token",
+    "qoq_rmsnorm_quant_per_token",
     "qoq_w4a8_gemm_workspace_size",
     "qoq_w4a8_gemm",
     "qoq_w4a8_gemm_i32",
@@ -87,6 +88,7 @@ def load_library():
         "qoq_pack_codes": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i32, vp, vp, vp]),
         "qoq_unpack_weights": (ctypes.c_int, [vp, vp, vp, i64, i64, i32, vp, vp, vp, vp]),
         "qoq_quant_act_per_token": (ctypes.c_int, [vp, i64, i64, i64, vp, vp, vp]),
+        "qoq_rmsnorm_quant_per_token": (ctypes.c_int, [vp, vp, ctypes.c_float, i64, i64, i64, vp, vp, vp]),
         "qoq_w4a8_gemm_workspace_size": (sz, [i64, i64, i64, i32]),
         "qoq_w4a8_gemm": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]),
         "qoq_w4a8_gemm_i32": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]),
@@ -230,6 +232,30 @@ def qoq_quant_act_per_token(x, x8=None, sx=None, stream=None):
     lib = load_library()
     _check(lib.qoq_quant_act_per_token(_t_ptr(x), M, K, x.stride(0), _t_ptr(x8), _t_ptr(sx), _stream(stream)),
            "qoq_quant_act_per_token")
+    return x8, sx
+
+
+def qoq_rmsnorm_quant_per_token(x, gamma, eps: float, x8=None, sx=None, stream=None):
+    """Fused RMS normalization + per-token INT8 quantization of FP16 x [M, K] on the GPU."""
+    import torch
+    _require_cuda(x, gamma)
+    if x.dtype != torch.float16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D FP16 tensor with unit column stride")
+    M, K = x.shape
+    if gamma.dtype != torch.float16 or gamma.numel() != K or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous float16 [K] tensor")
+    if x8 is None:
+        x8 = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if sx is None:
+        sx = torch.empty((M,), dtype=torch.float16, device=x.device)
+    _require_cuda(x8, sx)
+    if not (x8.is_contiguous() and x8.shape == (M, K) and x8.dtype == torch.int8):
+        raise ValueError("x8 must be a contiguous int8 [M, K] tensor")
+    if not (sx.is_contiguous() and sx.numel() == M and sx.dtype == torch.float16):
+        raise ValueError("sx must be a contiguous float16 [M] tensor")
+    lib = load_library()
+    _check(lib.qoq_rmsnorm_quant_per_token(_t_ptr(x), _t_ptr(gamma), float(eps), M, K, x.stride(0), _t_ptr(x8),
+                                           _t_ptr(sx), _stream(stream)), "qoq_rmsnorm_quant_per_token")
     return x8, sx
 
 

@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
+#include <cmath>
+
 #include "qoq_internal.h"
 
 namespace qoq {
@@ -143,10 +145,226 @@ __global__ __launch_bounds__(kThreads) void act_quant_scalar_kernel(const unsign
     x8[m * K + k] = s != 0.0f ? static_cast<int8_t>(quant1(row[k], s)) : int8_t(0);
 }
 
+// ---------------------------------------------------------------------------
+// Fused producer: RMS normalization of each token row, then the per-token
+// quantization above ("QServe: W4A8KV4 Quantization and System Co-design for
+// Efficient LLM Serving", paperlayer.ai summary, §5 runtime and precision
+// mapping: activation quantization is fused into the preceding
+// normalization).  Per row:
+//   S   = sum_k x_k^2, exactly: an FP16 value is an integer times 2^-24, so
+//         its square is an integer times 2^-48 below 2^80, and a 128-bit
+//         integer holds the sum of any row;
+//   ms  = fp32(fp64(S) * 2^-48 / K),  r = 1 / sqrtf(ms + eps),
+//   h_k = fp16((x_k * r) * gamma_k), then s_x and x8 from h as above.
+// Every rounding is one IEEE operation on a value that does not depend on the
+// order of the reduction, so the result is the same for every launch shape.
+
+typedef unsigned __int128 u128;
+
+// x^2 in units of 2^-48 from the FP16 bits (finite x)
+__device__ __forceinline__ u128 square_units(uint32_t hbits) {
+  const uint32_t e = (hbits >> 10) & 31u;
+  const uint32_t mant = e ? ((hbits & 0x3ffu) | 0x400u) : (hbits & 0x3ffu);
+  const uint32_t sh = e ? 2u * e - 2u : 0u;
+  return u128(uint64_t(mant) * mant) << sh;
+}
+
+__device__ __forceinline__ u128 square_units8(uint4 v) {
+  return square_units(v.x & 0xffffu) + square_units(v.x >> 16) + square_units(v.y & 0xffffu) +
+         square_units(v.y >> 16) + square_units(v.z & 0xffffu) + square_units(v.z >> 16) +
+         square_units(v.w & 0xffffu) + square_units(v.w >> 16);
+}
+
+// Block-wide sum of a 128-bit integer; every thread gets the result.
+__device__ __forceinline__ u128 block_sum_u128(u128 v, u128* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const unsigned long long lo = static_cast<unsigned long long>(v);
+    const unsigned long long hi = static_cast<unsigned long long>(v >> 64);
+    v += (u128(__shfl_xor(hi, off, 64)) << 64) | u128(__shfl_xor(lo, off, 64));
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  u128 r = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) r += red[w];
+  return r;
+}
+
+// Round-to-nearest-even conversion of a 128-bit integer to FP64: the top 64
+// bits, with every bit below them folded into bit 0 as a sticky bit (the
+// rounding position of a 64-bit value with its top bit set is bit 10).
+__device__ __forceinline__ double u128_to_double_rn(u128 v) {
+  const unsigned long long hi = static_cast<unsigned long long>(v >> 64);
+  if (hi == 0) return static_cast<double>(static_cast<unsigned long long>(v));
+  const int n = 64 - __clzll(static_cast<long long>(hi));  // 1..64
+  const unsigned long long top =
+      static_cast<unsigned long long>(v >> n) | static_cast<unsigned long long>((v << (128 - n)) != 0);
+  return ldexp(static_cast<double>(top), n);
+}
+
+__device__ __forceinline__ float rms_factor(u128 S, int64_t K, float eps) {
+  const float ms = static_cast<float>(ldexp(u128_to_double_rn(S), -48) / static_cast<double>(K));
+  return 1.0f / sqrtf(ms + eps);
+}
+
+__device__ __forceinline__ uint32_t norm1(uint32_t xbits, uint32_t gbits, float r) {
+  const float x = __half2float(__ushort_as_half(static_cast<unsigned short>(xbits)));
+  const float g = __half2float(__ushort_as_half(static_cast<unsigned short>(gbits)));
+  return __half_as_ushort(__float2half_rn((x * r) * g));
+}
+__device__ __forceinline__ uint32_t norm2(uint32_t x2, uint32_t g2, float r) {
+  return norm1(x2 & 0xffffu, g2 & 0xffffu, r) | (norm1(x2 >> 16, g2 >> 16, r) << 16);
+}
+__device__ __forceinline__ uint4 norm8(uint4 x, uint4 g, float r) {
+  return make_uint4(norm2(x.x, g.x, r), norm2(x.y, g.y, r), norm2(x.z, g.z, r), norm2(x.w, g.w, r));
+}
+
+// Vector path, row held in registers: VPT vectors of 8 halves per thread.
+template <int VPT>
+__global__ __launch_bounds__(kThreads) void rmsnorm_quant_reg_kernel(const uint4* __restrict__ x, int64_t ldx_vec,
+                                                                      int k_vec, const uint4* __restrict__ gamma,
+                                                                      float eps, uint2* __restrict__ x8,
+                                                                      unsigned short* __restrict__ sx) {
+  __shared__ u128 red_sum[kThreads / 64];
+  __shared__ uint32_t red[kThreads / 64];
+  const int64_t m = blockIdx.x;
+  const uint4* row = x + m * ldx_vec;
+  uint4 v[VPT];
+  u128 S = 0;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int idx = threadIdx.x + i * kThreads;
+    v[i] = idx < k_vec ? row[idx] : make_uint4(0, 0, 0, 0);
+    S += square_units8(v[i]);
+  }
+  const float r = rms_factor(block_sum_u128(S, red_sum), int64_t(k_vec) * 8, eps);
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int idx = threadIdx.x + i * kThreads;
+    if (idx < k_vec) {
+      v[i] = norm8(v[i], gamma[idx], r);
+      amax = max(amax, max_abs_bits8(v[i]));
+    }
+  }
+  amax = block_max(amax, red);
+  unsigned short s_bits;
+  const float s = scale_from_absmax(amax, &s_bits);
+  if (threadIdx.x == 0) sx[m] = s_bits;
+  uint2* out = x8 + m * k_vec;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int idx = threadIdx.x + i * kThreads;
+    if (idx < k_vec) {
+      uint2 q = make_uint2(0u, 0u);
+      if (s != 0.0f) q = make_uint2(quant4(v[i].x, v[i].y, s), quant4(v[i].z, v[i].w, s));
+      out[idx] = q;
+    }
+  }
+}
+
+// Vector path for long rows: three passes over the row (the later ones from
+// cache); the normalized values are recomputed, not stored.
+__global__ __launch_bounds__(kThreads) void rmsnorm_quant_stream_kernel(const uint4* __restrict__ x, int64_t ldx_vec,
+                                                                         int k_vec, const uint4* __restrict__ gamma,
+                                                                         float eps, uint2* __restrict__ x8,
+                                                                         unsigned short* __restrict__ sx) {
+  __shared__ u128 red_sum[kThreads / 64];
+  __shared__ uint32_t red[kThreads / 64];
+  const int64_t m = blockIdx.x;
+  const uint4* row = x + m * ldx_vec;
+  u128 S = 0;
+  for (int idx = threadIdx.x; idx < k_vec; idx += kThreads) S += square_units8(row[idx]);
+  const float r = rms_factor(block_sum_u128(S, red_sum), int64_t(k_vec) * 8, eps);
+  uint32_t amax = 0;
+  for (int idx = threadIdx.x; idx < k_vec; idx += kThreads)
+    amax = max(amax, max_abs_bits8(norm8(row[idx], gamma[idx], r)));
+  amax = block_max(amax, red);
+  unsigned short s_bits;
+  const float s = scale_from_absmax(amax, &s_bits);
+  if (threadIdx.x == 0) sx[m] = s_bits;
+  uint2* out = x8 + m * k_vec;
+  for (int idx = threadIdx.x; idx < k_vec; idx += kThreads) {
+    const uint4 h = norm8(row[idx], gamma[idx], r);
+    uint2 q = make_uint2(0u, 0u);
+    if (s != 0.0f) q = make_uint2(quant4(h.x, h.y, s), quant4(h.z, h.w, s));
+    out[idx] = q;
+  }
+}
+
+// Scalar path for any K / alignment.
+__global__ __launch_bounds__(kThreads) void rmsnorm_quant_scalar_kernel(const unsigned short* __restrict__ x,
+                                                                         int64_t ldx, int64_t K,
+                                                                         const unsigned short* __restrict__ gamma,
+                                                                         float eps, int8_t* __restrict__ x8,
+                                                                         unsigned short* __restrict__ sx) {
+  __shared__ u128 red_sum[kThreads / 64];
+  __shared__ uint32_t red[kThreads / 64];
+  const int64_t m = blockIdx.x;
+  const unsigned short* row = x + m * ldx;
+  u128 S = 0;
+  for (int64_t k = threadIdx.x; k < K; k += kThreads) S += square_units(row[k]);
+  const float r = rms_factor(block_sum_u128(S, red_sum), K, eps);
+  uint32_t amax = 0;
+  for (int64_t k = threadIdx.x; k < K; k += kThreads) amax = max(amax, norm1(row[k], gamma[k], r) & 0x7fffu);
+  amax = block_max(amax, red);
+  unsigned short s_bits;
+  const float s = scale_from_absmax(amax, &s_bits);
+  if (threadIdx.x == 0) sx[m] = s_bits;
+  for (int64_t k = threadIdx.x; k < K; k += kThreads)
+    x8[m * K + k] = s != 0.0f ? static_cast<int8_t>(quant1(norm1(row[k], gamma[k], r), s)) : int8_t(0);
+}
+
 }  // namespace
 }  // namespace qoq
 
 using namespace qoq;
+
+extern "C" int qoq_rmsnorm_quant_per_token(const void* x_fp16, const void* gamma_fp16, float eps, int64_t M,
+                                           int64_t K, int64_t ldx, int8_t* x8, void* sx_fp16, void* stream) {
+  clear_error();
+  if (!x_fp16 || !gamma_fp16 || !x8 || !sx_fp16)
+    return fail(QOQ_ERR_INVALID_ARG, "qoq_rmsnorm_quant_per_token: null pointer argument");
+  if (!(eps > 0.0f) || !(eps < INFINITY))
+    return fail(QOQ_ERR_INVALID_ARG, "qoq_rmsnorm_quant_per_token: eps must be positive and finite");
+  if (M < 1 || K < 1) return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "qoq_rmsnorm_quant_per_token: M and K must be >= 1");
+  if (ldx < K) return fail(QOQ_ERR_INVALID_ARG, "qoq_rmsnorm_quant_per_token: ldx < K");
+  if (M > 0x7fffffff || K > 0x7fffffff)
+    return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "qoq_rmsnorm_quant_per_token: M or K too large");
+  const auto al = [](const void* p, uintptr_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; };
+  if (!al(x_fp16, 2) || !al(gamma_fp16, 2) || !al(sx_fp16, 2))
+    return fail(QOQ_ERR_ALIGNMENT, "qoq_rmsnorm_quant_per_token: FP16 pointers must be 2-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>(M)), block(kThreads);
+  const bool vec = K % 8 == 0 && ldx % 8 == 0 && al(x_fp16, 16) && al(gamma_fp16, 16) && al(x8, 8);
+  auto* sx = static_cast<unsigned short*>(sx_fp16);
+  if (vec) {
+    const auto* xv = static_cast<const uint4*>(x_fp16);
+    const auto* gv = static_cast<const uint4*>(gamma_fp16);
+    auto* qv = reinterpret_cast<uint2*>(x8);
+    const int k_vec = static_cast<int>(K / 8);
+    const int64_t ldv = ldx / 8;
+    if (k_vec <= kThreads)
+      hipLaunchKernelGGL(rmsnorm_quant_reg_kernel<1>, grid, block, 0, st, xv, ldv, k_vec, gv, eps, qv, sx);
+    else if (k_vec <= 2 * kThreads)
+      hipLaunchKernelGGL(rmsnorm_quant_reg_kernel<2>, grid, block, 0, st, xv, ldv, k_vec, gv, eps, qv, sx);
+    else if (k_vec <= 4 * kThreads)
+      hipLaunchKernelGGL(rmsnorm_quant_reg_kernel<4>, grid, block, 0, st, xv, ldv, k_vec, gv, eps, qv, sx);
+    else if (k_vec <= 8 * kThreads)
+      hipLaunchKernelGGL(rmsnorm_quant_reg_kernel<8>, grid, block, 0, st, xv, ldv, k_vec, gv, eps, qv, sx);
+    else
+      hipLaunchKernelGGL(rmsnorm_quant_stream_kernel, grid, block, 0, st, xv, ldv, k_vec, gv, eps, qv, sx);
+  } else {
+    hipLaunchKernelGGL(rmsnorm_quant_scalar_kernel, grid, block, 0, st, static_cast<const unsigned short*>(x_fp16),
+                       ldx, K, static_cast<const unsigned short*>(gamma_fp16), eps, x8, sx);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(QOQ_ERR_HIP, "qoq_rmsnorm_quant_per_token: launch failed: %s", hipGetErrorString(e));
+  return QOQ_OK;
+}
 
 extern "C" int qoq_quant_act_per_token(const void* x_fp16, int64_t M, int64_t K, int64_t ldx, int8_t* x8,
                                        void* sx_fp16, void* stream) {
