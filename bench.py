@@ -53,6 +53,13 @@ def act_bytes(w) -> int:
     return 2 * w.M * w.K + w.M * w.K + 2 * w.M
 
 
+def producer_bytes(w) -> int:
+    """Fused RMS normalization + quantization: FP16 rows and gamma in, INT8
+    rows and FP16 scales out (an unfused norm would add 4 bytes per element:
+    its FP16 output written and read back)."""
+    return 2 * w.M * w.K + 2 * w.K + w.M * w.K + 2 * w.M
+
+
 def bound_of(w) -> str:
     t_hbm = algo_bytes(w) / (PEAK_HBM_GBS * 1e9)
     t_mfma = w.ops / (PEAK_INT8_TOPS * 1e12)
@@ -148,6 +155,11 @@ def measure_comparators(torch, q, w, W, x8, sx, y, ws, t_g, reps: int):
     return r
 
 
+def synthetic_gamma(K: int):
+    import synthetic
+    return synthetic.make_gamma(K)
+
+
 def measure_gemm(torch, q, w, X, W, reps: int, comparators: bool = False):
     """Kernel-level timing of the act quantizer and the GEMM for one workload
     (and, if asked, of the two comparators on the same inputs)."""
@@ -166,6 +178,8 @@ def measure_gemm(torch, q, w, X, W, reps: int, comparators: bool = False):
         q.qoq_w4a8_gemm(x8, sx, p, y=y)
     torch.cuda.synchronize()
     t_q = time_kernel(torch, lambda i: q.qoq_quant_act_per_token(x, x8, sx), reps)
+    gamma = torch.from_numpy(synthetic_gamma(w.K)).to(dev)
+    t_n = time_kernel(torch, lambda i: q.qoq_rmsnorm_quant_per_token(x, gamma, 1e-5, x8, sx), reps)
     t_g = time_kernel(torch, lambda i: q.qoq_w4a8_gemm(x8, sx, ws[i % copies], y=y), reps)
     b = algo_bytes(w)
     bnd = bound_of(w)
@@ -175,7 +189,8 @@ def measure_gemm(torch, q, w, X, W, reps: int, comparators: bool = False):
     r = {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "group_size": w.group_size,
          "gemm_us": round(t_g, 3), "tops": round(tops, 2), "gbs": round(gbs, 1), "bound": bnd,
          "frac": round(frac, 4), "weight_copies": copies, "act_quant_us": round(t_q, 3),
-         "act_quant_gbs": round(act_bytes(w) / t_q / 1e3, 1)}
+         "act_quant_gbs": round(act_bytes(w) / t_q / 1e3, 1),
+         "rmsnorm_quant_us": round(t_n, 3), "rmsnorm_quant_gbs": round(producer_bytes(w) / t_n / 1e3, 1)}
     if comparators:
         r.update(measure_comparators(torch, q, w, W, x8, sx, y, ws, t_g, reps))
     del ws

@@ -161,19 +161,33 @@ __global__ __launch_bounds__(kThreads) void act_quant_scalar_kernel(const unsign
 
 typedef unsigned __int128 u128;
 
-// x^2 in units of 2^-48 from the FP16 bits (finite x)
-__device__ __forceinline__ u128 square_units(uint32_t hbits) {
-  const uint32_t e = (hbits >> 10) & 31u;
-  const uint32_t mant = e ? ((hbits & 0x3ffu) | 0x400u) : (hbits & 0x3ffu);
-  const uint32_t sh = e ? 2u * e - 2u : 0u;
-  return u128(uint64_t(mant) * mant) << sh;
-}
-
-__device__ __forceinline__ u128 square_units8(uint4 v) {
-  return square_units(v.x & 0xffffu) + square_units(v.x >> 16) + square_units(v.y & 0xffffu) +
-         square_units(v.y >> 16) + square_units(v.z & 0xffffu) + square_units(v.z >> 16) +
-         square_units(v.w & 0xffffu) + square_units(v.w >> 16);
-}
+// Exact sum of squares of one thread's FP16 values, in units of 2^-48.  A
+// square is mant^2 * 2^sh with mant^2 < 2^22 and sh = 2e - 2 in [0, 58] (e
+// the biased exponent, 1 for subnormals).  Squares with sh < 32 are added
+// into `lo`, the others (in units of 2^32) into `hi`: each addend is below
+// 2^54, so 64 of them fit 64-bit sums without carry; flush() moves the pair
+// into the 128-bit total before that bound is reached.
+struct SumSq {
+  uint64_t lo = 0, hi = 0;
+  u128 total = 0;
+  __device__ __forceinline__ void add(uint32_t hbits) {
+    const uint32_t e = (hbits >> 10) & 31u;
+    const uint32_t mant = e ? ((hbits & 0x3ffu) | 0x400u) : (hbits & 0x3ffu);
+    const uint32_t sh = e ? 2u * e - 2u : 0u;
+    const bool big = sh >= 32u;
+    const uint64_t v = uint64_t(mant * mant) << (big ? sh - 32u : sh);
+    lo += big ? 0 : v;
+    hi += big ? v : 0;
+  }
+  __device__ __forceinline__ void add8(uint4 q) {
+    add(q.x & 0xffffu); add(q.x >> 16); add(q.y & 0xffffu); add(q.y >> 16);
+    add(q.z & 0xffffu); add(q.z >> 16); add(q.w & 0xffffu); add(q.w >> 16);
+  }
+  __device__ __forceinline__ void flush() {
+    total += (u128(hi) << 32) + u128(lo);
+    lo = hi = 0;
+  }
+};
 
 // Block-wide sum of a 128-bit integer; every thread gets the result.
 __device__ __forceinline__ u128 block_sum_u128(u128 v, u128* red) {
@@ -231,15 +245,17 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_reg_kernel(const uint4
   __shared__ uint32_t red[kThreads / 64];
   const int64_t m = blockIdx.x;
   const uint4* row = x + m * ldx_vec;
+  static_assert(VPT * 8 <= 64, "one flush per row");
   uint4 v[VPT];
-  u128 S = 0;
+  SumSq S;
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     const int idx = threadIdx.x + i * kThreads;
     v[i] = idx < k_vec ? row[idx] : make_uint4(0, 0, 0, 0);
-    S += square_units8(v[i]);
+    S.add8(v[i]);
   }
-  const float r = rms_factor(block_sum_u128(S, red_sum), int64_t(k_vec) * 8, eps);
+  S.flush();
+  const float r = rms_factor(block_sum_u128(S.total, red_sum), int64_t(k_vec) * 8, eps);
   uint32_t amax = 0;
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
@@ -275,9 +291,17 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_stream_kernel(const ui
   __shared__ uint32_t red[kThreads / 64];
   const int64_t m = blockIdx.x;
   const uint4* row = x + m * ldx_vec;
-  u128 S = 0;
-  for (int idx = threadIdx.x; idx < k_vec; idx += kThreads) S += square_units8(row[idx]);
-  const float r = rms_factor(block_sum_u128(S, red_sum), int64_t(k_vec) * 8, eps);
+  SumSq S;
+  int n = 0;
+  for (int idx = threadIdx.x; idx < k_vec; idx += kThreads) {
+    S.add8(row[idx]);
+    if (++n == 8) {  // 64 squares
+      S.flush();
+      n = 0;
+    }
+  }
+  S.flush();
+  const float r = rms_factor(block_sum_u128(S.total, red_sum), int64_t(k_vec) * 8, eps);
   uint32_t amax = 0;
   for (int idx = threadIdx.x; idx < k_vec; idx += kThreads)
     amax = max(amax, max_abs_bits8(norm8(row[idx], gamma[idx], r)));
@@ -304,9 +328,17 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_scalar_kernel(const un
   __shared__ uint32_t red[kThreads / 64];
   const int64_t m = blockIdx.x;
   const unsigned short* row = x + m * ldx;
-  u128 S = 0;
-  for (int64_t k = threadIdx.x; k < K; k += kThreads) S += square_units(row[k]);
-  const float r = rms_factor(block_sum_u128(S, red_sum), K, eps);
+  SumSq S;
+  int n = 0;
+  for (int64_t k = threadIdx.x; k < K; k += kThreads) {
+    S.add(row[k]);
+    if (++n == 64) {
+      S.flush();
+      n = 0;
+    }
+  }
+  S.flush();
+  const float r = rms_factor(block_sum_u128(S.total, red_sum), K, eps);
   uint32_t amax = 0;
   for (int64_t k = threadIdx.x; k < K; k += kThreads) amax = max(amax, norm1(row[k], gamma[k], r) & 0x7fffu);
   amax = block_max(amax, red);
