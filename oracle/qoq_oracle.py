@@ -66,6 +66,9 @@ __all__ = [
     "dequant_level1_saturating",
     "rmsnorm_fp16",
     "rmsnorm_quant_per_token",
+    "kv4_quant_per_head",
+    "kv4_dequant",
+    "kv4_decode_attention",
 ]
 
 ACT_QMAX = 127   # symmetric INT8 activation range [-127, 127]
@@ -420,3 +423,70 @@ def rmsnorm_quant_per_token(X, gamma, eps):
     Returns (x8 int8 [M,K], s_x float16 [M]).
     """
     return quant_act_per_token(rmsnorm_fp16(X, gamma, eps))
+
+
+# ------------------------------------------------------------------ KV4 (f3)
+
+def kv4_quant_per_head(X):
+    """Per-head dynamic asymmetric INT4 quantization of key or value vectors.
+
+    [PL §6, experimental setup]: the KV cache is per-head asymmetric INT4;
+    [PL §5, KV4 attention]: the scaling factors and zero points are per head
+    and computed at run time.  Every row of X (last axis = one head's vector
+    of one token) gets its own FP16 scale and UINT4 zero point, by the same
+    asymmetric UINT4 map as the per-channel weights:
+      s = fp16((max x - min x) / 15),  z = clamp(round(-min x / s), 0, 15),
+      q = clamp(round(x / s) + z, 0, 15);  a zero scale gives zero codes.
+
+    X: float16 [..., d].  Returns (q uint8 [..., d], s float16 [...],
+    z uint8 [...]).
+    """
+    X16 = np.asarray(X, dtype=np.float16)
+    lead, d = X16.shape[:-1], X16.shape[-1]
+    q4, s, z = quant_weight_per_channel(X16.reshape(-1, d))
+    return q4.reshape(*lead, d), s.reshape(lead), z.reshape(lead)
+
+
+def kv4_dequant(q4, s, z):
+    """(q - z) * s, exactly, in FP64 (broadcast over the last axis)."""
+    q = np.asarray(q4, dtype=np.float64)
+    zz = np.asarray(z, dtype=np.float64)[..., None]
+    ss = np.asarray(s, dtype=np.float16).astype(np.float64)[..., None]
+    return (q - zz) * ss
+
+
+def kv4_decode_attention(q, kq, ks, kz, vq, vs, vz, lengths, softmax_scale):
+    """Decode attention over a KV4 cache, in FP64, rounded once to FP16.
+
+    [PL §5, KV4 attention]: the attention of the newest token reads the INT4
+    cache, dequantizes it with the per-head scales and zero points, and
+    computes in floating point; [PL §4, SmoothAttention]: queries stay
+    unquantized.  Per sequence b and query head h, with kv head
+    g = h // (H / Hkv) and L = lengths[b] cached tokens:
+      k_t = (kq - kz) * ks, v_t = (vq - vz) * vs       (t < L)
+      a_t = softmax_t(scale * <q[b,h], k_t>)
+      o[b,h] = fp16(sum_t a_t v_t);  L = 0 gives o = 0.
+
+    q float16 [B, H, d]; kq/vq uint8 codes [B, Hkv, T, d]; ks/vs float16 and
+    kz/vz uint8 [B, Hkv, T]; lengths int [B]; softmax_scale a float (taken
+    as FP32).  Returns float16 [B, H, d].
+    """
+    q64 = np.asarray(q, dtype=np.float16).astype(np.float64)
+    B, H, d = q64.shape
+    Hkv = np.asarray(kq).shape[1]
+    if H % Hkv:
+        raise ValueError("query heads must be a multiple of kv heads")
+    scale = float(np.float32(softmax_scale))
+    out = np.zeros((B, H, d), np.float64)
+    for b in range(B):
+        L = int(lengths[b])
+        if L == 0:
+            continue
+        for h in range(H):
+            g = h // (H // Hkv)
+            K = kv4_dequant(kq[b, g, :L], ks[b, g, :L], kz[b, g, :L])
+            V = kv4_dequant(vq[b, g, :L], vs[b, g, :L], vz[b, g, :L])
+            sc = scale * (K @ q64[b, h])
+            e = np.exp(sc - sc.max())
+            out[b, h] = (e / e.sum()) @ V
+    return fp16_rne(out)

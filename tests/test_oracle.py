@@ -428,3 +428,93 @@ def test_rmsnorm_zero_row_and_bad_args():
         O.rmsnorm_fp16(X, np.ones(128, np.float16), 0.0)
     with pytest.raises(ValueError):
         O.rmsnorm_fp16(X, np.ones(64, np.float16), 1e-5)
+
+
+# ------------------------------------------------------------------ KV4 (f3)
+
+def test_kv4_quant_hand_worked_row():
+    fx = read_fixture("kv4_row.txt")
+    q, sc, z = O.kv4_quant_per_head(np.array([fx["x"]], np.float16))
+    assert q[0].tolist() == [int(v) for v in fx["q"]]
+    assert float(sc[0]) == fx["s"][0] and int(z[0]) == fx["z"][0]
+
+
+def test_kv4_quant_is_per_row_over_leading_axes():
+    X = synthetic.make_x(2 * 3 * 5, 128, "frac", seed=2).reshape(2, 3, 5, 128)
+    q, sc, z = O.kv4_quant_per_head(X)
+    assert q.shape == X.shape and sc.shape == (2, 3, 5) and z.shape == (2, 3, 5)
+    q2, s2, z2 = O.quant_weight_per_channel(X[1, 2])
+    assert np.array_equal(q[1, 2], q2) and np.array_equal(sc[1, 2], s2) and np.array_equal(z[1, 2], z2)
+    deq = O.kv4_dequant(q, sc, z)
+    err = np.abs(deq - X.astype(np.float64))
+    assert np.all(err <= 0.5 * sc.astype(np.float64)[..., None] + 1e-12)
+
+
+def _kv_case(B, H, Hkv, T, d=128, seed=0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, d)).astype(np.float16)
+    K = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    V = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    return q, O.kv4_quant_per_head(K), O.kv4_quant_per_head(V)
+
+
+def _attn(q, kk, vv, lengths, scale=0.08838834764831845):
+    return O.kv4_decode_attention(q, *kk, *vv, lengths, scale)
+
+
+def test_kv4_attention_single_token_returns_its_value():
+    q, kk, vv = _kv_case(2, 2, 2, 1, seed=1)
+    o = _attn(q, kk, vv, [1, 1])
+    assert np.array_equal(o, O.fp16_rne(O.kv4_dequant(*vv)[:, :, 0]))
+
+
+def test_kv4_attention_zero_query_averages_values():
+    q, kk, vv = _kv_case(1, 2, 2, 37, seed=2)
+    o = _attn(np.zeros_like(q), kk, vv, [37])
+    assert np.array_equal(o, O.fp16_rne(O.kv4_dequant(*vv).mean(axis=2)))
+    assert np.array_equal(o, _attn(q, kk, vv, [37], scale=0.0))
+
+
+def test_kv4_attention_token_order_does_not_matter():
+    q, kk, vv = _kv_case(1, 3, 3, 50, seed=3)
+    perm = np.random.default_rng(0).permutation(50)
+    pk = tuple(a[:, :, perm] for a in kk)
+    pv = tuple(a[:, :, perm] for a in vv)
+    a, b = _attn(q, kk, vv, [50]).astype(np.float64), _attn(q, pk, pv, [50]).astype(np.float64)
+    assert np.all(np.abs(a - b) <= 2.0 ** -10 * np.abs(a) + 2.0 ** -24)
+
+
+def test_kv4_attention_dominant_key_selects_its_value():
+    q, kk, vv = _kv_case(1, 1, 1, 20, seed=4)
+    kq, ks, kz = (a.copy() for a in kk)
+    j = 13
+    qs = np.sign(q[0, 0].astype(np.float64))
+    kq[0, 0, j] = np.where(qs > 0, 15, 0)      # key aligned with q at the range ends
+    kz[0, 0, j] = 8
+    ks[0, 0, j] = np.float16(8.0)               # score ~ 8 * 7.5 * sum|q| * scale: hundreds
+    o = _attn(q, (kq, ks, kz), vv, [20])
+    assert np.array_equal(o[0, 0], O.fp16_rne(O.kv4_dequant(*vv)[0, 0, j]))
+    # the opposite sign picks some other token instead
+    o2 = _attn(-q, (kq, ks, kz), vv, [20])
+    assert not np.array_equal(o2[0, 0], o[0, 0])
+
+
+def test_kv4_attention_gqa_equals_duplicated_heads():
+    q, kk, vv = _kv_case(2, 4, 2, 9, seed=5)
+    dup = lambda t: tuple(np.repeat(a, 2, axis=1) for a in t)
+    assert np.array_equal(_attn(q, kk, vv, [9, 9]), _attn(q, dup(kk), dup(vv), [9, 9]))
+
+
+def test_kv4_attention_lengths_are_prefixes():
+    q, kk, vv = _kv_case(3, 2, 2, 16, seed=6)
+    o = _attn(q, kk, vv, [16, 5, 0])
+    cut = lambda t, n: tuple(a[:, :, :n] for a in t)
+    assert np.array_equal(o[1], _attn(q[1:2], cut(tuple(a[1:2] for a in kk), 5), cut(tuple(a[1:2] for a in vv), 5), [5])[0])
+    assert not o[2].any()
+
+
+def test_kv4_attention_query_scale_equals_softmax_scale():
+    q, kk, vv = _kv_case(1, 2, 2, 30, seed=7)
+    a = _attn(q, kk, vv, [30], scale=0.25)
+    b = _attn((q.astype(np.float32) * 2).astype(np.float16), kk, vv, [30], scale=0.125)
+    assert np.array_equal(a, b)
