@@ -214,6 +214,50 @@ QOQ_API int qoq_w4a8_gemm_i32(const int8_t* x8, const void* qweight, const void*
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * KV4: the INT4 KV cache and the decode attention that reads it.
+ * [PL §6, experimental setup: per-head asymmetric INT4 KV caches]; [PL §5,
+ * KV4 attention: per-head scaling factors and zero points computed at run
+ * time; the attention runs in floating point on the vector units and is
+ * memory-bound]; [PL §4, SmoothAttention: queries stay unquantized].
+ * head_dim must be 128.
+ *
+ * Cache layout: one row per (token, kv head) of 128 values:
+ *   codes [rows][64 bytes]: byte j = code of dim 2j | (code of dim 2j+1) << 4;
+ *   scale FP16 [rows]; zero [rows] (one byte, 0..15).
+ * The attention takes rows ordered [B][Hkv][T_max] (a head's tokens
+ * consecutive).
+ */
+
+/*
+ * Per-head asymmetric INT4 quantization (device) of n_rows rows of 128 FP16
+ * values (row r at x_fp16 + r*ldx, ldx even and >= 128), the same map as the
+ * per-channel weights: s = fp16((max - min) / 15) (FP32 subtract and divide,
+ * round half even), z = clamp(rint(-min / s), 0, 15),
+ * q = clamp(rint(x / s) + z, 0, 15); s == 0 gives z = 0 and zero codes.
+ * codes: device [n_rows][64]; scale_fp16, zero: device [n_rows].
+ */
+QOQ_API int qoq_kv4_quant(const void* x_fp16, int64_t n_rows, int32_t head_dim, int64_t ldx, uint8_t* codes,
+                  void* scale_fp16, uint8_t* zero, void* stream);
+
+/*
+ * Decode attention over a KV4 cache (device).  For sequence b < B and query
+ * head h < H (kv head g = h / (H / Hkv)), with L = lengths[b] (clamped to
+ * [0, T_max]) cached tokens:
+ *   k_t = (kc_t - kz_t) * ks_t, v_t = (vc_t - vz_t) * vs_t,
+ *   a = softmax_t(softmax_scale * <q[b,h], k_t>),  o[b,h] = fp16(sum_t a_t v_t),
+ * in FP32 (scores as ks_t * (<q', kc_t> - kz_t * sum(q')) with
+ * q' = softmax_scale * q); L = 0 gives o = 0.  q_fp16: device [B][H][128];
+ * the k and v arrays: cache rows [B][Hkv][T_max]; lengths: device int32 [B];
+ * o_fp16: device [B][H][128].  1 <= T_max <= 32768; q and the code arrays
+ * 16-byte aligned.  Accuracy: see the parity tolerance in the design notes
+ * (FP32 arithmetic, exp to a few FP32 ulp).
+ */
+QOQ_API int qoq_kv4_decode_attention(const void* q_fp16, const uint8_t* k_codes, const void* k_scale_fp16,
+                             const uint8_t* k_zero, const uint8_t* v_codes, const void* v_scale_fp16,
+                             const uint8_t* v_zero, const int32_t* lengths, int32_t B, int32_t H, int32_t Hkv,
+                             int32_t T_max, int32_t head_dim, float softmax_scale, void* o_fp16, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Comparators of the W4A8 GEMM.  They run the same kernels, launch plans and
  * epilogue, so that the cost of the weight format is measured on its own.
  */

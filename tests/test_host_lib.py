@@ -25,7 +25,7 @@ def header_symbols():
 def test_library_exports_every_header_symbol():
     lib = q.load_library()
     syms = header_symbols()
-    assert len(syms) == 17, syms
+    assert len(syms) == 19, syms
     assert sorted(_native.EXPORTS) == syms
     for s in syms:
         assert hasattr(lib, s), s
@@ -327,3 +327,19 @@ def test_rmsnorm_quant_validates_before_launch():
     assert lib.qoq_rmsnorm_quant_per_token(d, d, 1e-5, 4, 128, 64, d, d, None) == 1       # ldx < K
     assert lib.qoq_rmsnorm_quant_per_token(d, d, 1e-5, 0, 128, 128, d, d, None) == 2
     assert lib.qoq_rmsnorm_quant_per_token(d + 1, d, 1e-5, 4, 128, 128, d, d, None) == 3  # odd FP16 pointer
+
+
+def test_kv4_entry_points_validate_before_launch():
+    lib = q.load_library()
+    d = 4096
+    assert lib.qoq_kv4_quant(None, 4, 128, 128, d, d, d, None) == 1
+    assert lib.qoq_kv4_quant(d, 4, 64, 64, d, d, d, None) == 2            # head_dim must be 128
+    assert lib.qoq_kv4_quant(d, 4, 128, 127, d, d, d, None) == 1          # ldx odd / < head_dim
+    assert lib.qoq_kv4_quant(d + 2, 4, 128, 128, d, d, d, None) == 3      # x needs 4-byte alignment
+    args = [d] * 8
+    assert lib.qoq_kv4_decode_attention(*args, 2, 4, 3, 16, 128, 0.1, d, None) == 2      # H % Hkv
+    assert lib.qoq_kv4_decode_attention(*args, 2, 4, 2, 40000, 128, 0.1, d, None) == 2   # T_max too large
+    assert lib.qoq_kv4_decode_attention(*args, 2, 4, 2, 16, 64, 0.1, d, None) == 2       # head_dim
+    assert lib.qoq_kv4_decode_attention(*args, 2, 4, 2, 16, 128, float("nan"), d, None) == 1
+    assert lib.qoq_kv4_decode_attention(d + 8, *args[1:], 2, 4, 2, 16, 128, 0.1, d, None) == 3
+    assert lib.qoq_kv4_decode_attention(None, *args[1:], 2, 4, 2, 16, 128, 0.1, d, None) == 1

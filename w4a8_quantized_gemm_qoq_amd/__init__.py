@@ -12,6 +12,8 @@ from ._native import (  # noqa: F401
     PackedWeightW8,
     QoQError,
     load_library,
+    qoq_kv4_decode_attention,
+    qoq_kv4_quant,
     qoq_pack_codes,
     qoq_pack_weights,
     qoq_quant_act_per_token,

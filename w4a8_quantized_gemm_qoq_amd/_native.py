@@ -37,6 +37,8 @@ EXPORTS = [
     "qoq_w8a8_gemm_i32",
     "qoq_w4a8_gemm_saturating",
     "qoq_w4a8_gemm_saturating_i32",
+    "qoq_kv4_quant",
+    "qoq_kv4_decode_attention",
 ]
 
 GROUP = 128
@@ -98,6 +100,9 @@ def load_library():
         "qoq_w8a8_gemm_i32": (ctypes.c_int, [vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]),
         "qoq_w4a8_gemm_saturating": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]),
         "qoq_w4a8_gemm_saturating_i32": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]),
+        "qoq_kv4_quant": (ctypes.c_int, [vp, i64, i32, i64, vp, vp, vp, vp]),
+        "qoq_kv4_decode_attention": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                                    ctypes.c_float, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -445,3 +450,58 @@ def qoq_w4a8_gemm_saturating_i32(x8, w: PackedWeight, acc=None, workspace=None, 
                                             acc.stride(0), _workspace(ws, workspace, x8.device), ws,
                                             _stream(stream)), "qoq_w4a8_gemm_saturating_i32")
     return acc
+
+
+# ------------------------------------------------------------------------ KV4
+
+HEAD_DIM = 128
+
+
+def qoq_kv4_quant(x, codes=None, scale=None, zero=None, stream=None):
+    """Per-head asymmetric INT4 quantization of FP16 rows x [..., 128] on the GPU.
+
+    Returns (codes uint8 [..., 64], scale float16 [...], zero uint8 [...]).
+    """
+    import torch
+    _require_cuda(x)
+    if x.dtype != torch.float16 or x.shape[-1] != HEAD_DIM or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float16 tensor with a last axis of 128")
+    lead = tuple(x.shape[:-1])
+    n = int(np.prod(lead)) if lead else 1
+    codes = torch.empty(lead + (HEAD_DIM // 2,), dtype=torch.uint8, device=x.device) if codes is None else codes
+    scale = torch.empty(lead, dtype=torch.float16, device=x.device) if scale is None else scale
+    zero = torch.empty(lead, dtype=torch.uint8, device=x.device) if zero is None else zero
+    _require_cuda(codes, scale, zero)
+    if codes.numel() != n * HEAD_DIM // 2 or scale.numel() != n or zero.numel() != n:
+        raise ValueError("output sizes do not match x")
+    lib = load_library()
+    _check(lib.qoq_kv4_quant(_t_ptr(x), n, HEAD_DIM, HEAD_DIM, _t_ptr(codes), _t_ptr(scale), _t_ptr(zero),
+                             _stream(stream)), "qoq_kv4_quant")
+    return codes, scale, zero
+
+
+def qoq_kv4_decode_attention(q, k, v, lengths, softmax_scale, o=None, stream=None):
+    """Decode attention of q [B, H, 128] FP16 over KV4 caches k, v = (codes
+    [B, Hkv, T, 64], scale [B, Hkv, T], zero [B, Hkv, T]); lengths int32 [B]."""
+    import torch
+    kc, ks, kz = k
+    vc, vs, vz = v
+    _require_cuda(q, kc, ks, kz, vc, vs, vz, lengths)
+    if q.dtype != torch.float16 or q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous float16 [B, H, 128] tensor")
+    B, H, _ = q.shape
+    if kc.dim() != 4 or kc.shape[0] != B or kc.shape[3] != HEAD_DIM // 2:
+        raise ValueError("k codes must be uint8 [B, Hkv, T, 64]")
+    Hkv, T = kc.shape[1], kc.shape[2]
+    for t, shape in ((kc, (B, Hkv, T, 64)), (vc, (B, Hkv, T, 64)), (ks, (B, Hkv, T)), (vs, (B, Hkv, T)),
+                     (kz, (B, Hkv, T)), (vz, (B, Hkv, T))):
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError("KV cache arrays must be contiguous with matching [B, Hkv, T] shapes")
+    if lengths.dtype != torch.int32 or lengths.numel() != B:
+        raise ValueError("lengths must be int32 [B]")
+    o = torch.empty((B, H, HEAD_DIM), dtype=torch.float16, device=q.device) if o is None else o
+    lib = load_library()
+    _check(lib.qoq_kv4_decode_attention(_t_ptr(q), _t_ptr(kc), _t_ptr(ks), _t_ptr(kz), _t_ptr(vc), _t_ptr(vs),
+                                        _t_ptr(vz), _t_ptr(lengths), B, H, Hkv, T, HEAD_DIM, float(softmax_scale),
+                                        _t_ptr(o), _stream(stream)), "qoq_kv4_decode_attention")
+    return o

@@ -1,0 +1,336 @@
+// KV4: per-head dynamic asymmetric INT4 quantization of the KV cache and the
+// decode attention that reads it, for gfx950.
+//
+// Follows "QServe: W4A8KV4 Quantization and System Co-design for Efficient
+// LLM Serving" (paperlayer.ai abs/2405.04532v3 summary): §6 (experimental
+// setup) keeps the KV cache as per-head asymmetric INT4; §5 (KV4 attention)
+// computes the per-head scaling factors and zero points at run time and runs
+// the attention in floating point on the vector units, as a memory-bound
+// kernel; §4 (SmoothAttention) leaves the queries unquantized; §3 (roofline)
+// motivates KV4 by its halved memory traffic against KV8.
+//
+// Cache layout (head_dim 128): codes [rows][64 bytes], byte j = code of dim
+// 2j | code of dim 2j+1 << 4; scale FP16 [rows]; zero UINT4 in a byte [rows].
+// For attention the rows are ordered [B][Hkv][T_max] (a head's tokens are
+// consecutive).
+//
+// Quantization of one row x (128 FP16 values), exactly the per-channel W4 map:
+//   s = fp16((max - min) / 15)  (FP32 subtract and divide, RNE),
+//   z = clamp(rint(-min / s), 0, 15),  q = clamp(rint(x / s) + z, 0, 15);
+//   s == 0 gives z = 0 and zero codes.
+//
+// Decode attention of one query head h of sequence b (kv head g = h/(H/Hkv),
+// L = lengths[b] tokens): score_t = scale * <q, (c_t - z_t) s_t>, evaluated as
+// s_t * (<q', c_t> - z_t * sum(q')) with q' = scale * q in FP32; then
+// softmax and o = sum_t a_t v_t in FP32, written as FP16.  The scores of a
+// head are kept in LDS (T_max <= 32768).  One 256-thread block per (b, h):
+// four lanes share a token (32 dims, one 16-byte load each), so a wave reads
+// 16 consecutive tokens = 1 KB per load instruction.
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <cmath>
+
+#include "qoq_internal.h"
+
+namespace qoq {
+namespace {
+
+constexpr int kHeadDim = 128;
+constexpr int kRowBytes = kHeadDim / 2;
+constexpr int kAttnThreads = 256;
+constexpr int kMaxCacheLen = 32768;
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fminf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// One wave per row; lane l holds dims 2l and 2l+1.
+__global__ __launch_bounds__(256) void kv4_quant_kernel(const unsigned* __restrict__ x, int64_t ldx_pairs,
+                                                        int64_t n_rows, uint8_t* __restrict__ codes,
+                                                        unsigned short* __restrict__ scale,
+                                                        uint8_t* __restrict__ zero) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= n_rows) return;
+  const unsigned pr = x[row * ldx_pairs + lane];
+  const float x0 = __half2float(__ushort_as_half(static_cast<unsigned short>(pr & 0xffffu)));
+  const float x1 = __half2float(__ushort_as_half(static_cast<unsigned short>(pr >> 16)));
+  const float hi = wave_max(fmaxf(x0, x1));
+  const float lo = wave_min(fminf(x0, x1));
+  const __half sh = __float2half_rn((hi - lo) / 15.0f);
+  const float s = __half2float(sh);
+  unsigned q = 0, zz = 0;
+  if (s != 0.0f) {
+    const float z = fminf(15.0f, fmaxf(0.0f, rintf(-lo / s)));
+    const float q0 = fminf(15.0f, fmaxf(0.0f, rintf(x0 / s) + z));
+    const float q1 = fminf(15.0f, fmaxf(0.0f, rintf(x1 / s) + z));
+    q = unsigned(q0) | (unsigned(q1) << 4);
+    zz = unsigned(z);
+  }
+  codes[row * kRowBytes + lane] = static_cast<uint8_t>(q);
+  if (lane == 0) {
+    scale[row] = __half_as_ushort(sh);
+    zero[row] = static_cast<uint8_t>(zz);
+  }
+}
+
+// byte k of v as a float (one v_cvt_f32_ubyte{k})
+template <int k>
+__device__ __forceinline__ float ubyte(unsigned v) {
+  return static_cast<float>((v >> (8 * k)) & 0xffu);
+}
+
+// <q[0..32), codes of 32 dims> for one 16-byte load: dword w holds dims
+// 8w..8w+7 (byte b: dims 8w+2b (low) and 8w+2b+1 (high)).
+__device__ __forceinline__ float dot32(const float (&q)[32], uint4 c) {
+  const unsigned w[4] = {c.x, c.y, c.z, c.w};
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned lo = w[i] & 0x0f0f0f0fu, hi = (w[i] >> 4) & 0x0f0f0f0fu;
+    acc = fmaf(q[8 * i + 0], ubyte<0>(lo), acc);
+    acc = fmaf(q[8 * i + 1], ubyte<0>(hi), acc);
+    acc = fmaf(q[8 * i + 2], ubyte<1>(lo), acc);
+    acc = fmaf(q[8 * i + 3], ubyte<1>(hi), acc);
+    acc = fmaf(q[8 * i + 4], ubyte<2>(lo), acc);
+    acc = fmaf(q[8 * i + 5], ubyte<2>(hi), acc);
+    acc = fmaf(q[8 * i + 6], ubyte<3>(lo), acc);
+    acc = fmaf(q[8 * i + 7], ubyte<3>(hi), acc);
+  }
+  return acc;
+}
+
+// acc[d] += w * code[d] over the 32 dims of one 16-byte load.
+__device__ __forceinline__ void axpy32(float (&acc)[32], float w, uint4 c) {
+  const unsigned v[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned lo = v[i] & 0x0f0f0f0fu, hi = (v[i] >> 4) & 0x0f0f0f0fu;
+    acc[8 * i + 0] = fmaf(w, ubyte<0>(lo), acc[8 * i + 0]);
+    acc[8 * i + 1] = fmaf(w, ubyte<0>(hi), acc[8 * i + 1]);
+    acc[8 * i + 2] = fmaf(w, ubyte<1>(lo), acc[8 * i + 2]);
+    acc[8 * i + 3] = fmaf(w, ubyte<1>(hi), acc[8 * i + 3]);
+    acc[8 * i + 4] = fmaf(w, ubyte<2>(lo), acc[8 * i + 4]);
+    acc[8 * i + 5] = fmaf(w, ubyte<2>(hi), acc[8 * i + 5]);
+    acc[8 * i + 6] = fmaf(w, ubyte<3>(lo), acc[8 * i + 6]);
+    acc[8 * i + 7] = fmaf(w, ubyte<3>(hi), acc[8 * i + 7]);
+  }
+}
+
+struct AttnArgs {
+  const unsigned short* q;
+  const uint8_t *kc, *vc;
+  const unsigned short *ks, *vs;
+  const uint8_t *kz, *vz;
+  const int* lengths;
+  unsigned short* o;
+  int H, Hkv, T;
+  float scale;
+};
+
+// Tokens in flight per wave and pass: U loads of 16 tokens each.
+constexpr int kUnroll = 4;
+
+__global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(AttnArgs a) {
+  extern __shared__ float sc[];  // [T] scores, then weights
+  __shared__ float red[kAttnThreads / 64];
+  __shared__ float part[kAttnThreads / 64][kHeadDim + 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p = lane & 3;          // which 32 dims of the head
+  const int tq = lane >> 2;        // token slot within the wave's 16
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int g = h / (a.H / a.Hkv);
+  const int L = min(max(a.lengths[b], 0), a.T);
+  const int64_t row0 = (int64_t(b) * a.Hkv + g) * a.T;  // first cache row of this head
+
+  // q' = scale * q for this lane's 32 dims, and their sum
+  float q[32];
+  const uint4* qv = reinterpret_cast<const uint4*>(a.q + (int64_t(b) * a.H + h) * kHeadDim + 32 * p);
+  float qsum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 u = qv[i];
+    const unsigned w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      q[8 * i + 2 * j] = a.scale * __half2float(__ushort_as_half(static_cast<unsigned short>(w[j] & 0xffffu)));
+      q[8 * i + 2 * j + 1] = a.scale * __half2float(__ushort_as_half(static_cast<unsigned short>(w[j] >> 16)));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) qsum += q[i];
+
+  // pass 1: scores
+  float mx = -INFINITY;
+  const uint4* kc = reinterpret_cast<const uint4*>(a.kc + row0 * kRowBytes);
+  for (int base = wave * 16 * kUnroll; base < L; base += kAttnThreads / 4 * kUnroll) {
+    uint4 c[kUnroll];
+    float s[kUnroll];
+    int z[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int t = min(base + 16 * u + tq, L - 1);  // past L: a valid token, result dropped
+      c[u] = kc[int64_t(t) * 4 + p];
+      s[u] = __half2float(__ushort_as_half(a.ks[row0 + t]));
+      z[u] = a.kz[row0 + t];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float v = s[u] * (dot32(q, c[u]) - float(z[u]) * qsum);
+      v += __shfl_xor(v, 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      const int t = base + 16 * u + tq;
+      if (t < L) {
+        mx = fmaxf(mx, v);
+        if (p == 0) sc[t] = v;
+      }
+    }
+  }
+  mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+
+  // weights and their sum
+  float lsum = 0.0f;
+  for (int t = threadIdx.x; t < L; t += kAttnThreads) {
+    const float e = __expf(sc[t] - mx);
+    sc[t] = e;
+    lsum += e;
+  }
+  lsum = wave_sum(lsum);
+  if (lane == 0) red[wave] = lsum;
+  __syncthreads();
+  lsum = red[0] + red[1] + red[2] + red[3];
+
+  // pass 2: o = sum_t a_t s_t (c_t - z_t), accumulated as
+  // sum (a_t s_t) c_t - sum (a_t s_t z_t)
+  float acc[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) acc[i] = 0.0f;
+  float zacc = 0.0f;
+  const uint4* vc = reinterpret_cast<const uint4*>(a.vc + row0 * kRowBytes);
+  for (int base = wave * 16 * kUnroll; base < L; base += kAttnThreads / 4 * kUnroll) {
+    uint4 c[kUnroll];
+    float w[kUnroll];
+    int z[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int t = base + 16 * u + tq;
+      const int tc = min(t, L - 1);
+      c[u] = vc[int64_t(tc) * 4 + p];
+      w[u] = t < L ? sc[tc] * __half2float(__ushort_as_half(a.vs[row0 + tc])) : 0.0f;
+      z[u] = a.vz[row0 + tc];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      axpy32(acc, w[u], c[u]);
+      zacc = fmaf(w[u], float(z[u]), zacc);
+    }
+  }
+  // sum over the 16 token slots of the wave (lanes with equal p)
+#pragma unroll
+  for (int off = 4; off < 64; off <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] += __shfl_xor(acc[i], off, 64);
+    zacc += __shfl_xor(zacc, off, 64);
+  }
+  if (tq == 0) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) part[wave][32 * p + i] = acc[i] - zacc;
+  }
+  __syncthreads();
+  if (threadIdx.x < kHeadDim) {
+    const int d = threadIdx.x;
+    const float v = part[0][d] + part[1][d] + part[2][d] + part[3][d];
+    const float o = L > 0 ? v / lsum : 0.0f;
+    a.o[(int64_t(b) * a.H + h) * kHeadDim + d] = __half_as_ushort(__float2half_rn(o));
+  }
+}
+
+}  // namespace
+}  // namespace qoq
+
+using namespace qoq;
+
+extern "C" int qoq_kv4_quant(const void* x_fp16, int64_t n_rows, int32_t head_dim, int64_t ldx, uint8_t* codes,
+                             void* scale_fp16, uint8_t* zero, void* stream) {
+  clear_error();
+  if (!x_fp16 || !codes || !scale_fp16 || !zero) return fail(QOQ_ERR_INVALID_ARG, "qoq_kv4_quant: null pointer argument");
+  if (head_dim != kHeadDim) return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "qoq_kv4_quant: head_dim must be 128, got %d", head_dim);
+  if (n_rows < 1 || n_rows > (int64_t(1) << 40)) return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "qoq_kv4_quant: n_rows out of range");
+  if (ldx < head_dim || ldx % 2) return fail(QOQ_ERR_INVALID_ARG, "qoq_kv4_quant: ldx must be even and >= head_dim");
+  if (reinterpret_cast<uintptr_t>(x_fp16) % 4 || reinterpret_cast<uintptr_t>(scale_fp16) % 2)
+    return fail(QOQ_ERR_ALIGNMENT, "qoq_kv4_quant: x needs 4-byte, scale 2-byte alignment");
+  const int64_t blocks = (n_rows + 3) / 4;
+  if (blocks > 0x7fffffff) return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "qoq_kv4_quant: too many rows");
+  hipLaunchKernelGGL(kv4_quant_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const unsigned*>(x_fp16), ldx / 2, n_rows, codes,
+                     static_cast<unsigned short*>(scale_fp16), zero);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(QOQ_ERR_HIP, "qoq_kv4_quant: launch failed: %s", hipGetErrorString(e));
+  return QOQ_OK;
+}
+
+extern "C" int qoq_kv4_decode_attention(const void* q_fp16, const uint8_t* k_codes, const void* k_scale_fp16,
+                                        const uint8_t* k_zero, const uint8_t* v_codes, const void* v_scale_fp16,
+                                        const uint8_t* v_zero, const int32_t* lengths, int32_t B, int32_t H,
+                                        int32_t Hkv, int32_t T_max, int32_t head_dim, float softmax_scale,
+                                        void* o_fp16, void* stream) {
+  clear_error();
+  if (!q_fp16 || !k_codes || !k_scale_fp16 || !k_zero || !v_codes || !v_scale_fp16 || !v_zero || !lengths || !o_fp16)
+    return fail(QOQ_ERR_INVALID_ARG, "qoq_kv4_decode_attention: null pointer argument");
+  if (head_dim != kHeadDim)
+    return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "qoq_kv4_decode_attention: head_dim must be 128, got %d", head_dim);
+  if (B < 1 || H < 1 || Hkv < 1 || H % Hkv || B > 65535 || H > 65535)
+    return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "qoq_kv4_decode_attention: need B, H, Hkv >= 1 and H a multiple of Hkv");
+  if (T_max < 1 || T_max > kMaxCacheLen)
+    return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "qoq_kv4_decode_attention: T_max must be in [1, %d]", kMaxCacheLen);
+  if (!std::isfinite(softmax_scale)) return fail(QOQ_ERR_INVALID_ARG, "qoq_kv4_decode_attention: scale not finite");
+  const auto al = [](const void* p, uintptr_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; };
+  if (!al(q_fp16, 16) || !al(k_codes, 16) || !al(v_codes, 16) || !al(k_scale_fp16, 2) || !al(v_scale_fp16, 2) ||
+      !al(lengths, 4) || !al(o_fp16, 2))
+    return fail(QOQ_ERR_ALIGNMENT, "qoq_kv4_decode_attention: q and codes need 16-byte alignment");
+  AttnArgs a;
+  a.q = static_cast<const unsigned short*>(q_fp16);
+  a.kc = k_codes;
+  a.vc = v_codes;
+  a.ks = static_cast<const unsigned short*>(k_scale_fp16);
+  a.vs = static_cast<const unsigned short*>(v_scale_fp16);
+  a.kz = k_zero;
+  a.vz = v_zero;
+  a.lengths = lengths;
+  a.o = static_cast<unsigned short*>(o_fp16);
+  a.H = H;
+  a.Hkv = Hkv;
+  a.T = T_max;
+  a.scale = softmax_scale;
+  const size_t lds = size_t(T_max) * sizeof(float);
+  auto* fn = kv4_decode_attention_kernel;
+  if (lds > 48 * 1024) {
+    const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxCacheLen * 4));
+    if (attr != hipSuccess)
+      return fail(QOQ_ERR_HIP, "qoq_kv4_decode_attention: LDS attribute: %s", hipGetErrorString(attr));
+  }
+  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(H), static_cast<unsigned>(B)), dim3(kAttnThreads), lds,
+                     static_cast<hipStream_t>(stream), a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(QOQ_ERR_HIP, "qoq_kv4_decode_attention: launch failed: %s", hipGetErrorString(e));
+  return QOQ_OK;
+}
