@@ -155,6 +155,53 @@ def measure_comparators(torch, q, w, W, x8, sx, y, ws, t_g, reps: int):
     return r
 
 
+KV4_SHAPES = [("llama2_7b_mha", 64, 32, 32, 1024), ("llama3_8b_gqa", 64, 32, 8, 1024)]
+
+
+def kv4_bytes(B, H, Hkv, T) -> int:
+    """Decode attention over a KV4 cache: K and V codes (64 B per token and
+    head), their FP16 scales and byte zeros, the FP16 queries and outputs."""
+    return 2 * B * Hkv * T * (64 + 2 + 1) + 2 * 2 * B * H * 128 + 4 * B
+
+
+def measure_kv4(torch, q, reps: int):
+    """KV4 decode attention and KV quantization at 64 sequences x 1024 cached
+    tokens (the pages' 64 x 1024 attention input), head_dim 128."""
+    import numpy as np
+    dev = torch.device("cuda")
+    out = []
+    for name, B, H, Hkv, T in KV4_SHAPES:
+        rng = np.random.default_rng(0)
+        kv = torch.from_numpy(rng.standard_normal((2, B, Hkv, T, 128)).astype(np.float16)).to(dev)
+        t_quant = time_kernel(torch, lambda i: q.qoq_kv4_quant(kv), max(3, reps // 4))
+        cache_bytes = 2 * B * Hkv * T * 67
+        copies = max(1, min(16, math.ceil(3 * MALL_BYTES / cache_bytes)))
+        caches = []
+        for _ in range(copies):
+            kc, ks, kz = q.qoq_kv4_quant(kv[0])
+            vc, vs, vz = q.qoq_kv4_quant(kv[1])
+            caches.append(((kc, ks, kz), (vc, vs, vz)))
+        del kv
+        qq = torch.from_numpy(rng.standard_normal((B, H, 128)).astype(np.float16)).to(dev)
+        lengths = torch.full((B,), T, dtype=torch.int32, device=dev)
+        o = torch.empty((B, H, 128), dtype=torch.float16, device=dev)
+        scale = float(np.float32(1.0 / np.sqrt(128.0)))
+        for c in caches:
+            q.qoq_kv4_decode_attention(qq, c[0], c[1], lengths, scale, o=o)
+        t_attn = time_kernel(torch, lambda i: q.qoq_kv4_decode_attention(qq, caches[i % copies][0],
+                                                                         caches[i % copies][1], lengths, scale, o=o),
+                             reps)
+        nb = kv4_bytes(B, H, Hkv, T)
+        out.append({"shape": name, "B": B, "H": H, "Hkv": Hkv, "T": T, "attention_us": round(t_attn, 3),
+                    "attention_gbs": round(nb / t_attn / 1e3, 1),
+                    "attention_frac_hbm": round(nb / t_attn / 1e3 / PEAK_HBM_GBS, 4),
+                    "cache_copies": copies, "kv_quant_us": round(t_quant, 3),
+                    "kv_quant_gbs": round((2 * B * Hkv * T * (256 + 67)) / t_quant / 1e3, 1)})
+        del caches
+        torch.cuda.empty_cache()
+    return out
+
+
 def synthetic_gamma(K: int):
     import synthetic
     return synthetic.make_gamma(K)
@@ -206,6 +253,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--sweep", default=",".join(SWEEP), help="comma-separated workload names")
     ap.add_argument("--sweep-reps", type=int, default=20)
+    ap.add_argument("--no-kv4", action="store_true", help="skip the KV4 attention measurement")
     ap.add_argument("--no-comparators", action="store_true",
                     help="skip the W8A8 comparator and the saturating ablation in the sweep")
     ap.add_argument("--kernel-reps", type=int, default=100)
@@ -364,6 +412,13 @@ def main():
                 "note": "same kernels and plans; W8A8 = per-channel INT8 weights without dequantization; "
                         "saturating = g128 GEMM with a clamping 16-bit-lane dequantization",
             }
+
+    if not args.no_kv4:
+        try:
+            out["kv4"] = measure_kv4(torch, q, args.sweep_reps)
+        except Exception as ex:  # report, do not hide
+            out["kv4"] = [{"error": repr(ex)}]
+        print(f"[kv4] {json.dumps(out['kv4'])}", file=sys.stderr, flush=True)
 
     if args.copy_calib_mb:
         n = args.copy_calib_mb * 2 ** 20

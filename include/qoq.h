@@ -230,7 +230,8 @@ QOQ_API int qoq_w4a8_gemm_i32(const int8_t* x8, const void* qweight, const void*
 
 /*
  * Per-head asymmetric INT4 quantization (device) of n_rows rows of 128 FP16
- * values (row r at x_fp16 + r*ldx, ldx even and >= 128), the same map as the
+ * values (row r at x_fp16 + r*ldx, ldx a multiple of 8 and >= 128; x 16-byte
+ * aligned, codes 4-byte aligned), the same map as the
  * per-channel weights: s = fp16((max - min) / 15) (FP32 subtract and divide,
  * round half even), z = clamp(rint(-min / s), 0, 15),
  * q = clamp(rint(x / s) + z, 0, 15); s == 0 gives z = 0 and zero codes.

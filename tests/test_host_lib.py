@@ -334,8 +334,8 @@ def test_kv4_entry_points_validate_before_launch():
     d = 4096
     assert lib.qoq_kv4_quant(None, 4, 128, 128, d, d, d, None) == 1
     assert lib.qoq_kv4_quant(d, 4, 64, 64, d, d, d, None) == 2            # head_dim must be 128
-    assert lib.qoq_kv4_quant(d, 4, 128, 127, d, d, d, None) == 1          # ldx odd / < head_dim
-    assert lib.qoq_kv4_quant(d + 2, 4, 128, 128, d, d, d, None) == 3      # x needs 4-byte alignment
+    assert lib.qoq_kv4_quant(d, 4, 128, 130, d, d, d, None) == 1          # ldx not a multiple of 8
+    assert lib.qoq_kv4_quant(d + 4, 4, 128, 128, d, d, d, None) == 3      # x needs 16-byte alignment
     args = [d] * 8
     assert lib.qoq_kv4_decode_attention(*args, 2, 4, 3, 16, 128, 0.1, d, None) == 2      # H % Hkv
     assert lib.qoq_kv4_decode_attention(*args, 2, 4, 2, 40000, 128, 0.1, d, None) == 2   # T_max too large

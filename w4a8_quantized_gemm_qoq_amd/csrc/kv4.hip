@@ -58,33 +58,60 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// One wave per row; lane l holds dims 2l and 2l+1.
-__global__ __launch_bounds__(256) void kv4_quant_kernel(const unsigned* __restrict__ x, int64_t ldx_pairs,
-                                                        int64_t n_rows, uint8_t* __restrict__ codes,
+// 16 lanes per row (8 values each, one 16-byte load), 16 rows per block.
+constexpr int kQuantRowsPerBlock = 16;
+
+__device__ __forceinline__ float half_lo(unsigned w) {
+  return __half2float(__ushort_as_half(static_cast<unsigned short>(w & 0xffffu)));
+}
+__device__ __forceinline__ float half_hi(unsigned w) {
+  return __half2float(__ushort_as_half(static_cast<unsigned short>(w >> 16)));
+}
+// max / min over the 16 lanes of a row group
+__device__ __forceinline__ float group16_max(float v) {
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float group16_min(float v) {
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) v = fminf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__global__ __launch_bounds__(256) void kv4_quant_kernel(const uint4* __restrict__ x, int64_t ldx_vec,
+                                                        int64_t n_rows, unsigned* __restrict__ codes,
                                                         unsigned short* __restrict__ scale,
                                                         uint8_t* __restrict__ zero) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= n_rows) return;
-  const unsigned pr = x[row * ldx_pairs + lane];
-  const float x0 = __half2float(__ushort_as_half(static_cast<unsigned short>(pr & 0xffffu)));
-  const float x1 = __half2float(__ushort_as_half(static_cast<unsigned short>(pr >> 16)));
-  const float hi = wave_max(fmaxf(x0, x1));
-  const float lo = wave_min(fminf(x0, x1));
+  const int sub = threadIdx.x & 15;  // which 8 dims of the row
+  const int64_t row = int64_t(blockIdx.x) * kQuantRowsPerBlock + (threadIdx.x >> 4);
+  // rows past the end read the last row; their results are not stored
+  const uint4 u = x[min(row, n_rows - 1) * ldx_vec + sub];
+  float v[8] = {half_lo(u.x), half_hi(u.x), half_lo(u.y), half_hi(u.y),
+                half_lo(u.z), half_hi(u.z), half_lo(u.w), half_hi(u.w)};
+  float hi = v[0], lo = v[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    hi = fmaxf(hi, v[i]);
+    lo = fminf(lo, v[i]);
+  }
+  hi = group16_max(hi);
+  lo = group16_min(lo);
   const __half sh = __float2half_rn((hi - lo) / 15.0f);
   const float s = __half2float(sh);
   unsigned q = 0, zz = 0;
   if (s != 0.0f) {
     const float z = fminf(15.0f, fmaxf(0.0f, rintf(-lo / s)));
-    const float q0 = fminf(15.0f, fmaxf(0.0f, rintf(x0 / s) + z));
-    const float q1 = fminf(15.0f, fmaxf(0.0f, rintf(x1 / s) + z));
-    q = unsigned(q0) | (unsigned(q1) << 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q |= unsigned(fminf(15.0f, fmaxf(0.0f, rintf(v[i] / s) + z))) << (4 * i);
     zz = unsigned(z);
   }
-  codes[row * kRowBytes + lane] = static_cast<uint8_t>(q);
-  if (lane == 0) {
-    scale[row] = __half_as_ushort(sh);
-    zero[row] = static_cast<uint8_t>(zz);
+  if (row < n_rows) {
+    codes[row * (kRowBytes / 4) + sub] = q;
+    if (sub == 0) {
+      scale[row] = __half_as_ushort(sh);
+      zero[row] = static_cast<uint8_t>(zz);
+    }
   }
 }
 
@@ -152,8 +179,23 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int p = lane & 3;          // which 32 dims of the head
   const int tq = lane >> 2;        // token slot within the wave's 16
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int g = h / (a.H / a.Hkv);
+  // Block -> (b, h).  Workgroups are dealt round-robin to the 8 XCDs, each
+  // with its own L2; the query heads that share a kv head are given
+  // consecutive slots on one XCD, so that the cache rows they all read come
+  // from that L2 after the first.  (Plain order when the grid does not tile.)
+  const int rep = a.H / a.Hkv;
+  int h = blockIdx.x, b = blockIdx.y;
+  {
+    const int nb = gridDim.x * gridDim.y;
+    const int d = blockIdx.y * gridDim.x + blockIdx.x;
+    if (rep > 1 && nb % (8 * rep) == 0) {
+      const int xcd = d % 8, slot = d / 8;
+      const int pair = (slot / rep) * 8 + xcd;  // (b, kv head) index
+      b = pair / a.Hkv;
+      h = (pair % a.Hkv) * rep + slot % rep;
+    }
+  }
+  const int g = h / rep;
   const int L = min(max(a.lengths[b], 0), a.T);
   const int64_t row0 = (int64_t(b) * a.Hkv + g) * a.T;  // first cache row of this head
 
@@ -274,14 +316,16 @@ extern "C" int qoq_kv4_quant(const void* x_fp16, int64_t n_rows, int32_t head_di
   if (!x_fp16 || !codes || !scale_fp16 || !zero) return fail(QOQ_ERR_INVALID_ARG, "qoq_kv4_quant: null pointer argument");
   if (head_dim != kHeadDim) return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "qoq_kv4_quant: head_dim must be 128, got %d", head_dim);
   if (n_rows < 1 || n_rows > (int64_t(1) << 40)) return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "qoq_kv4_quant: n_rows out of range");
-  if (ldx < head_dim || ldx % 2) return fail(QOQ_ERR_INVALID_ARG, "qoq_kv4_quant: ldx must be even and >= head_dim");
-  if (reinterpret_cast<uintptr_t>(x_fp16) % 4 || reinterpret_cast<uintptr_t>(scale_fp16) % 2)
-    return fail(QOQ_ERR_ALIGNMENT, "qoq_kv4_quant: x needs 4-byte, scale 2-byte alignment");
-  const int64_t blocks = (n_rows + 3) / 4;
+  if (ldx < head_dim || ldx % 8)
+    return fail(QOQ_ERR_INVALID_ARG, "qoq_kv4_quant: ldx must be a multiple of 8 and >= head_dim");
+  if (reinterpret_cast<uintptr_t>(x_fp16) % 16 || reinterpret_cast<uintptr_t>(codes) % 4 ||
+      reinterpret_cast<uintptr_t>(scale_fp16) % 2)
+    return fail(QOQ_ERR_ALIGNMENT, "qoq_kv4_quant: x needs 16-byte, codes 4-byte, scale 2-byte alignment");
+  const int64_t blocks = (n_rows + kQuantRowsPerBlock - 1) / kQuantRowsPerBlock;
   if (blocks > 0x7fffffff) return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "qoq_kv4_quant: too many rows");
   hipLaunchKernelGGL(kv4_quant_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const unsigned*>(x_fp16), ldx / 2, n_rows, codes,
-                     static_cast<unsigned short*>(scale_fp16), zero);
+                     static_cast<hipStream_t>(stream), static_cast<const uint4*>(x_fp16), ldx / 8, n_rows,
+                     reinterpret_cast<unsigned*>(codes), static_cast<unsigned short*>(scale_fp16), zero);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(QOQ_ERR_HIP, "qoq_kv4_quant: launch failed: %s", hipGetErrorString(e));
   return QOQ_OK;
