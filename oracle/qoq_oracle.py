@@ -69,6 +69,11 @@ __all__ = [
     "kv4_quant_per_head",
     "kv4_dequant",
     "kv4_decode_attention",
+    "hadamard_block_size",
+    "hadamard_matrix",
+    "rotate_rows",
+    "smoothing_factors",
+    "scale_columns",
 ]
 
 ACT_QMAX = 127   # symmetric INT8 activation range [-127, 127]
@@ -490,3 +495,63 @@ def kv4_decode_attention(q, kq, ks, kz, vq, vs, vz, lengths, softmax_scale):
             e = np.exp(sc - sc.max())
             out[b, h] = (e / e.sum()) @ V
     return fp16_rne(out)
+
+
+# ------------------------------------------------- offline transforms (f4)
+
+def hadamard_block_size(K):
+    """Largest power of two dividing K: the block of the rotation."""
+    K = int(K)
+    if K < 1:
+        raise ValueError("K must be positive")
+    return K & -K
+
+
+def hadamard_matrix(K):
+    """Orthogonal rotation of the K input channels, in FP64.
+
+    [PL §4, activation optimizations]: block inputs are rotated by a unitary
+    matrix that is absorbed into the preceding weights.  The pages name no
+    matrix; this is the normalized Walsh-Hadamard one (entries +-1/sqrt(b),
+    the Sylvester construction), block-diagonal with b = the largest power of
+    two dividing K when K is not a power of two (14336 = 7 * 2048).
+    """
+    b = hadamard_block_size(K)
+    h = np.ones((1, 1))
+    while h.shape[0] < b:
+        h = np.block([[h, h], [h, -h]])
+    h = h / np.sqrt(b)
+    return np.kron(np.eye(K // b), h)
+
+
+def rotate_rows(X, K=None):
+    """fp16(X @ H) for FP16 rows X [.., K]: the rotated activations or weights
+    (Y = X W^T = (X H)(W H)^T since H H^T = I)."""
+    X64 = np.asarray(X, dtype=np.float16).astype(np.float64)
+    K = X64.shape[-1] if K is None else K
+    return fp16_rne(X64 @ hadamard_matrix(K))
+
+
+def smoothing_factors(act_absmax, w_absmax, alpha):
+    """Per-channel smoothing factors, lambda_j = a_j^alpha / w_j^(1 - alpha).
+
+    [PL §4, activation optimizations]: output modules use per-channel
+    smoothing factors; [PL §4, SmoothAttention]: keys are scaled down with
+    alpha = 0.5 (there the weight side is absent: w = 1).  The form is the
+    SmoothQuant one the pages build on.  A channel whose activation or weight
+    maximum is 0 gets lambda = 1.  FP64, returned as FP32.
+    """
+    a = np.asarray(act_absmax, dtype=np.float64)
+    w = np.asarray(w_absmax, dtype=np.float64)
+    ok = (a > 0) & (w > 0)
+    lam = np.ones(np.broadcast(a, w).shape)
+    lam[ok] = a[ok] ** alpha / w[ok] ** (1.0 - alpha)
+    return lam.astype(np.float32)
+
+
+def scale_columns(X, factor, divide=False):
+    """fp16(X * factor) (or X / factor) along the last axis, in FP64: weights
+    take lambda, the activations (through the preceding layer) 1/lambda."""
+    X64 = np.asarray(X, dtype=np.float16).astype(np.float64)
+    f = np.asarray(factor, dtype=np.float32).astype(np.float64)
+    return fp16_rne(X64 / f if divide else X64 * f)

@@ -518,3 +518,56 @@ def test_kv4_attention_query_scale_equals_softmax_scale():
     a = _attn(q, kk, vv, [30], scale=0.25)
     b = _attn((q.astype(np.float32) * 2).astype(np.float16), kk, vv, [30], scale=0.125)
     assert np.array_equal(a, b)
+
+
+# ------------------------------------------------- offline transforms (f4)
+
+def test_hadamard_closed_form_and_orthogonality():
+    # entry (i, j) of the normalized Sylvester matrix is (-1)^popcount(i & j) / sqrt(n)
+    n = 64
+    H = O.hadamard_matrix(n)
+    i, j = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+    par = np.vectorize(lambda v: bin(int(v)).count("1") & 1)(i & j)
+    assert np.array_equal(H, np.where(par, -1.0, 1.0) / 8.0)
+    assert np.allclose(H @ H.T, np.eye(n), atol=1e-15)
+    assert np.array_equal(O.hadamard_matrix(2), np.array([[1.0, 1.0], [1.0, -1.0]]) / np.sqrt(2.0))
+
+
+def test_hadamard_blocks_for_non_power_of_two():
+    assert O.hadamard_block_size(14336) == 2048 and O.hadamard_block_size(4096) == 4096
+    assert O.hadamard_block_size(384) == 128
+    H = O.hadamard_matrix(384)
+    assert np.allclose(H @ H.T, np.eye(384), atol=1e-14)
+    assert not H[:128, 128:].any() and np.array_equal(H[128:256, 128:256], O.hadamard_matrix(128))
+
+
+def test_rotation_and_smoothing_leave_the_product_unchanged():
+    X = synthetic.make_x(8, 256, "frac", seed=1).astype(np.float64)
+    W = synthetic.make_w(16, 256, seed=1).astype(np.float64)
+    H = O.hadamard_matrix(256)
+    assert np.allclose((X @ H) @ (W @ H).T, X @ W.T, rtol=0, atol=1e-12)
+    lam = O.smoothing_factors(np.abs(X).max(0), np.abs(W).max(0), 0.5).astype(np.float64)
+    assert np.allclose((X / lam) @ (W * lam).T, X @ W.T, rtol=0, atol=1e-12)
+
+
+def test_smoothing_factor_hand_cases():
+    lam = O.smoothing_factors([4.0, 9.0, 0.0, 2.0, 16.0], [1.0, 4.0, 3.0, 0.0, 1.0], 0.5)
+    assert lam.tolist() == [2.0, 1.5, 1.0, 1.0, 4.0]
+    assert O.smoothing_factors([8.0], [2.0], 1.0).tolist() == [8.0]   # alpha = 1: all on the activation side
+    assert O.smoothing_factors([8.0], [2.0], 0.0).tolist() == [0.5]   # alpha = 0: 1 / w
+
+
+def test_rotation_spreads_activation_outliers():
+    # synthetic rows with x20 outlier channels: after the rotation no channel
+    # dominates, so the per-token INT8 step is finer (information about the
+    # value of the transform, on synthetic data; the rotation is orthogonal,
+    # so the norms compared are those of the same vectors)
+    X = synthetic.make_x(64, 1024, "frac", seed=2)
+
+    def act_err(Xi):
+        x8, sx = O.quant_act_per_token(Xi)
+        d = x8.astype(np.float64) * sx.astype(np.float64)[:, None]
+        return np.linalg.norm(d - Xi.astype(np.float64)) / np.linalg.norm(Xi.astype(np.float64))
+
+    e_plain, e_rot = act_err(X), act_err(O.rotate_rows(X))
+    assert e_rot < 0.25 * e_plain, (e_plain, e_rot)
