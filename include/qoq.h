@@ -214,6 +214,31 @@ QOQ_API int qoq_w4a8_gemm_i32(const int8_t* x8, const void* qweight, const void*
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Offline accuracy transforms (host).  [PL §4, activation optimizations:
+ * block inputs are rotated by a unitary matrix absorbed into the preceding
+ * weights, and output modules use per-channel smoothing factors]; [PL §4,
+ * SmoothAttention: outlier key channels scaled down, alpha = 0.5].  Each is
+ * an identity of the product, X W^T = (X H)(W H)^T = (X / l)(W * l)^T, so
+ * the W4A8 path is run on the transformed tensors.  FP16 in and out, the
+ * arithmetic in FP64 with one rounding to FP16 (half to even).
+ */
+
+/* out = in @ H for rows x K (row stride ld, in place allowed), H the
+ * normalized Walsh-Hadamard matrix, block-diagonal with blocks of the largest
+ * power of two dividing K (entries +-1/sqrt(block)). */
+QOQ_API int qoq_hadamard_rotate(const uint16_t* in_fp16, int64_t rows, int64_t K, int64_t ld, uint16_t* out_fp16);
+
+/* lambda[k] = act_absmax[k]^alpha / w_absmax[k]^(1 - alpha) (FP64, returned
+ * as FP32), 1 where either maximum is 0; 0 <= alpha <= 1. */
+QOQ_API int qoq_smoothing_factors(const float* act_absmax, const float* w_absmax, int64_t K, float alpha,
+                          float* lambda);
+
+/* out[r][k] = fp16(in[r][k] * factor[k]) (divide != 0: / factor[k]); factors
+ * positive and finite.  Weights take lambda, activations 1/lambda. */
+QOQ_API int qoq_scale_columns(const uint16_t* in_fp16, int64_t rows, int64_t K, int64_t ld, const float* factor,
+                      int32_t divide, uint16_t* out_fp16);
+
+/* ---------------------------------------------------------------------------
  * KV4: the INT4 KV cache and the decode attention that reads it.
  * [PL §6, experimental setup: per-head asymmetric INT4 KV caches]; [PL §5,
  * KV4 attention: per-head scaling factors and zero points computed at run

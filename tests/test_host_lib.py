@@ -25,7 +25,7 @@ def header_symbols():
 def test_library_exports_every_header_symbol():
     lib = q.load_library()
     syms = header_symbols()
-    assert len(syms) == 19, syms
+    assert len(syms) == 22, syms
     assert sorted(_native.EXPORTS) == syms
     for s in syms:
         assert hasattr(lib, s), s
@@ -343,3 +343,61 @@ def test_kv4_entry_points_validate_before_launch():
     assert lib.qoq_kv4_decode_attention(*args, 2, 4, 2, 16, 128, float("nan"), d, None) == 1
     assert lib.qoq_kv4_decode_attention(d + 8, *args[1:], 2, 4, 2, 16, 128, 0.1, d, None) == 3
     assert lib.qoq_kv4_decode_attention(None, *args[1:], 2, 4, 2, 16, 128, 0.1, d, None) == 1
+
+
+# ------------------------------------------------- offline transforms (f4)
+
+def _within_1ulp16(a, b):
+    a = np.asarray(a, np.float16).astype(np.float64)
+    b = np.asarray(b, np.float16).astype(np.float64)
+    e = np.floor(np.log2(np.maximum(np.abs(b), 2.0 ** -14)))
+    return np.all(np.abs(a - b) <= 2.0 ** (e - 10))
+
+
+@pytest.mark.parametrize("rows,K,seed", [(8, 4096, 0), (4, 14336, 1), (16, 384, 2), (3, 8, 3), (5, 7, 4)])
+def test_hadamard_rotate_matches_oracle(rows, K, seed):
+    X = synthetic.make_x(rows, K, "frac", seed=seed)
+    got = q.qoq_hadamard_rotate(X)
+    ref = O.rotate_rows(X)
+    assert _within_1ulp16(got, ref)
+    assert int(np.count_nonzero(got.view(np.uint16) != ref.view(np.uint16))) <= max(1, got.size // 100000)
+
+
+def test_hadamard_rotate_is_an_involution_up_to_rounding():
+    # H is symmetric and orthogonal (H H = I for the Sylvester blocks)
+    X = synthetic.make_w(4, 2048, seed=5)
+    back = q.qoq_hadamard_rotate(q.qoq_hadamard_rotate(X)).astype(np.float64)
+    X64 = X.astype(np.float64)
+    # the FP16 rounding of the rotated row (2^-11 relative) spreads over the
+    # whole row when rotated back: bound it by the row's RMS
+    rms = np.sqrt((X64 ** 2).mean(axis=1, keepdims=True))
+    assert np.all(np.abs(back - X64) <= 2.0 ** -8 * rms)
+
+
+def test_scale_columns_bit_exact_and_smoothing_factors():
+    X = synthetic.make_x(6, 512, "frac", seed=6)
+    W = synthetic.make_w(10, 512, seed=6)
+    a = np.abs(X.astype(np.float32)).max(0)
+    w = np.abs(W.astype(np.float32)).max(0)
+    lam = q.qoq_smoothing_factors(a, w, 0.5)
+    ref = O.smoothing_factors(a, w, 0.5)
+    assert np.all(np.abs(lam.astype(np.float64) - ref) <= np.spacing(np.abs(ref)).astype(np.float64))
+    assert np.array_equal(q.qoq_scale_columns(W, ref).view(np.uint16), O.scale_columns(W, ref).view(np.uint16))
+    assert np.array_equal(q.qoq_scale_columns(X, ref, divide=True).view(np.uint16),
+                          O.scale_columns(X, ref, divide=True).view(np.uint16))
+    # FP16 edge values: subnormal results, overflow to inf, exact halving
+    E = np.array([[6e-8, 65504.0, -1.0, 3.0]], np.float16)
+    f = np.array([0.5, 2.0, 1.0, 1.0 / 3.0], np.float32)
+    with np.errstate(over="ignore"):   # 65504 * 2 overflows FP16 to inf on purpose
+        ref_e = O.scale_columns(E, f)
+    assert np.array_equal(q.qoq_scale_columns(E, f).view(np.uint16), ref_e.view(np.uint16))
+
+
+def test_transforms_validate_arguments():
+    lib = q.load_library()
+    d = 4096
+    assert lib.qoq_hadamard_rotate(None, 1, 8, 8, d) == 1
+    assert lib.qoq_hadamard_rotate(d, 1, 8, 4, d) == 1
+    assert lib.qoq_smoothing_factors(d, d, 4, 1.5, d) == 1
+    with pytest.raises(q.QoQError):
+        q.qoq_scale_columns(np.ones((2, 4), np.float16), np.array([1, 0, 1, 1], np.float32))

@@ -12,12 +12,15 @@ from ._native import (  # noqa: F401
     PackedWeightW8,
     QoQError,
     load_library,
+    qoq_hadamard_rotate,
     qoq_kv4_decode_attention,
     qoq_kv4_quant,
     qoq_pack_codes,
     qoq_pack_weights,
     qoq_quant_act_per_token,
     qoq_rmsnorm_quant_per_token,
+    qoq_scale_columns,
+    qoq_smoothing_factors,
     qoq_unpack_weights,
     qoq_w4a8_forward,
     qoq_w4a8_gemm,

@@ -39,6 +39,9 @@ EXPORTS = [
     "qoq_w4a8_gemm_saturating_i32",
     "qoq_kv4_quant",
     "qoq_kv4_decode_attention",
+    "qoq_hadamard_rotate",
+    "qoq_smoothing_factors",
+    "qoq_scale_columns",
 ]
 
 GROUP = 128
@@ -103,6 +106,9 @@ def load_library():
         "qoq_kv4_quant": (ctypes.c_int, [vp, i64, i32, i64, vp, vp, vp, vp]),
         "qoq_kv4_decode_attention": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                                     ctypes.c_float, vp, vp]),
+        "qoq_hadamard_rotate": (ctypes.c_int, [vp, i64, i64, i64, vp]),
+        "qoq_smoothing_factors": (ctypes.c_int, [vp, vp, i64, ctypes.c_float, vp]),
+        "qoq_scale_columns": (ctypes.c_int, [vp, i64, i64, i64, vp, i32, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -505,3 +511,38 @@ def qoq_kv4_decode_attention(q, k, v, lengths, softmax_scale, o=None, stream=Non
                                         _t_ptr(vz), _t_ptr(lengths), B, H, Hkv, T, HEAD_DIM, float(softmax_scale),
                                         _t_ptr(o), _stream(stream)), "qoq_kv4_decode_attention")
     return o
+
+
+# --------------------------------------------------------- offline transforms
+
+def qoq_hadamard_rotate(X: np.ndarray) -> np.ndarray:
+    """X @ H (block Walsh-Hadamard along the last axis), FP16 in and out, on the host."""
+    X = np.ascontiguousarray(X, dtype=np.float16)
+    K = X.shape[-1]
+    rows = X.size // K
+    out = np.empty_like(X)
+    lib = load_library()
+    _check(lib.qoq_hadamard_rotate(_np_ptr(X.view(np.uint16)), rows, K, K, _np_ptr(out.view(np.uint16))),
+           "qoq_hadamard_rotate")
+    return out
+
+
+def qoq_smoothing_factors(act_absmax, w_absmax, alpha: float) -> np.ndarray:
+    a = np.ascontiguousarray(act_absmax, dtype=np.float32)
+    w = np.ascontiguousarray(w_absmax, dtype=np.float32)
+    lam = np.empty_like(a)
+    lib = load_library()
+    _check(lib.qoq_smoothing_factors(_np_ptr(a), _np_ptr(w), a.size, float(alpha), _np_ptr(lam)),
+           "qoq_smoothing_factors")
+    return lam
+
+
+def qoq_scale_columns(X: np.ndarray, factor, divide: bool = False) -> np.ndarray:
+    X = np.ascontiguousarray(X, dtype=np.float16)
+    K = X.shape[-1]
+    f = np.ascontiguousarray(factor, dtype=np.float32)
+    out = np.empty_like(X)
+    lib = load_library()
+    _check(lib.qoq_scale_columns(_np_ptr(X.view(np.uint16)), X.size // K, K, K, _np_ptr(f), int(divide),
+                                 _np_ptr(out.view(np.uint16))), "qoq_scale_columns")
+    return out

@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqoq.so")
 
-SOURCES = ["status.cpp", "pack.cpp", "act_quant.hip", "kv4.hip", "gemm_w4.hip", "gemm_w8.hip", "gemm_sat.hip"]
+SOURCES = ["status.cpp", "pack.cpp", "transforms.cpp", "act_quant.hip", "kv4.hip", "gemm_w4.hip", "gemm_w8.hip", "gemm_sat.hip"]
 OBJDIR = os.path.join(PKG, "_build")
 
 
