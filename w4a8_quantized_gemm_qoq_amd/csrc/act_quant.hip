@@ -11,7 +11,8 @@
 // loads and kept in registers (up to 16384 channels), the max |x| is reduced
 // exactly on the FP16 bit patterns (for non-negative finite halves the integer
 // order is the numeric order), then every element is divided by the stored
-// FP16 scale with a correctly rounded FP32 division and rounded half-even.
+// FP16 scale -- the correctly rounded FP32 quotient, from one IEEE reciprocal
+// per row and two FMAs per element -- and rounded half-even.
 // Build without fast-math: the division must stay IEEE.
 
 #include <hip/hip_runtime.h>
@@ -39,16 +40,28 @@ __device__ __forceinline__ uint32_t max_abs_bits8(uint4 v) {
   return max(r & 0xffffu, r >> 16);
 }
 
-__device__ __forceinline__ int quant1(uint32_t hbits, float s) {
+// x / s rounded to nearest even, for an FP16 value x and a positive FP16
+// scale s, given y = 1 / s correctly rounded (one IEEE division per row):
+// q0 = x * y is within an ulp of x / s, r = x - q0 * s is exact (FMA), and
+// q0 + r * y rounded once is the correctly rounded quotient (Markstein's
+// theorem).  Checked exhaustively on every finite FP16 x and every positive
+// finite FP16 s against the IEEE quotient: identical except for x = -0 (+0
+// here), which yields the same integer code.
+__device__ __forceinline__ float div_rn(float x, float s, float y) {
+  const float q0 = x * y;
+  return __builtin_fmaf(__builtin_fmaf(-q0, s, x), y, q0);
+}
+
+__device__ __forceinline__ int quant1(uint32_t hbits, float s, float y) {
   const float x = __half2float(__ushort_as_half(static_cast<unsigned short>(hbits)));
-  float q = rintf(x / s);
+  float q = rintf(div_rn(x, s, y));
   q = fminf(127.0f, fmaxf(-127.0f, q));
   return static_cast<int>(q);
 }
 
-__device__ __forceinline__ uint32_t quant4(uint32_t h01, uint32_t h23, float s) {
-  const int q0 = quant1(h01 & 0xffffu, s), q1 = quant1(h01 >> 16, s);
-  const int q2 = quant1(h23 & 0xffffu, s), q3 = quant1(h23 >> 16, s);
+__device__ __forceinline__ uint32_t quant4(uint32_t h01, uint32_t h23, float s, float y) {
+  const int q0 = quant1(h01 & 0xffffu, s, y), q1 = quant1(h01 >> 16, s, y);
+  const int q2 = quant1(h23 & 0xffffu, s, y), q3 = quant1(h23 >> 16, s, y);
   return (uint32_t(q0) & 0xffu) | ((uint32_t(q1) & 0xffu) << 8) | ((uint32_t(q2) & 0xffu) << 16) |
          ((uint32_t(q3) & 0xffu) << 24);
 }
@@ -92,6 +105,7 @@ __global__ __launch_bounds__(kThreads) void act_quant_reg_kernel(const uint4* __
   amax = block_max(amax, red);
   unsigned short s_bits;
   const float s = scale_from_absmax(amax, &s_bits);
+  const float y = s != 0.0f ? 1.0f / s : 0.0f;
   if (threadIdx.x == 0) sx[m] = s_bits;
   uint2* out = x8 + m * k_vec;
 #pragma unroll
@@ -99,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void act_quant_reg_kernel(const uint4* __
     const int idx = threadIdx.x + i * kThreads;
     if (idx < k_vec) {
       uint2 q = make_uint2(0u, 0u);
-      if (s != 0.0f) q = make_uint2(quant4(v[i].x, v[i].y, s), quant4(v[i].z, v[i].w, s));
+      if (s != 0.0f) q = make_uint2(quant4(v[i].x, v[i].y, s, y), quant4(v[i].z, v[i].w, s, y));
       out[idx] = q;
     }
   }
@@ -117,12 +131,13 @@ __global__ __launch_bounds__(kThreads) void act_quant_stream_kernel(const uint4*
   amax = block_max(amax, red);
   unsigned short s_bits;
   const float s = scale_from_absmax(amax, &s_bits);
+  const float y = s != 0.0f ? 1.0f / s : 0.0f;
   if (threadIdx.x == 0) sx[m] = s_bits;
   uint2* out = x8 + m * k_vec;
   for (int idx = threadIdx.x; idx < k_vec; idx += kThreads) {
     const uint4 v = row[idx];
     uint2 q = make_uint2(0u, 0u);
-    if (s != 0.0f) q = make_uint2(quant4(v.x, v.y, s), quant4(v.z, v.w, s));
+    if (s != 0.0f) q = make_uint2(quant4(v.x, v.y, s, y), quant4(v.z, v.w, s, y));
     out[idx] = q;
   }
 }
@@ -140,9 +155,10 @@ __global__ __launch_bounds__(kThreads) void act_quant_scalar_kernel(const unsign
   amax = block_max(amax, red);
   unsigned short s_bits;
   const float s = scale_from_absmax(amax, &s_bits);
+  const float y = s != 0.0f ? 1.0f / s : 0.0f;
   if (threadIdx.x == 0) sx[m] = s_bits;
   for (int64_t k = threadIdx.x; k < K; k += kThreads)
-    x8[m * K + k] = s != 0.0f ? static_cast<int8_t>(quant1(row[k], s)) : int8_t(0);
+    x8[m * K + k] = s != 0.0f ? static_cast<int8_t>(quant1(row[k], s, y)) : int8_t(0);
 }
 
 // ---------------------------------------------------------------------------
@@ -268,6 +284,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_reg_kernel(const uint4
   amax = block_max(amax, red);
   unsigned short s_bits;
   const float s = scale_from_absmax(amax, &s_bits);
+  const float y = s != 0.0f ? 1.0f / s : 0.0f;
   if (threadIdx.x == 0) sx[m] = s_bits;
   uint2* out = x8 + m * k_vec;
 #pragma unroll
@@ -275,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_reg_kernel(const uint4
     const int idx = threadIdx.x + i * kThreads;
     if (idx < k_vec) {
       uint2 q = make_uint2(0u, 0u);
-      if (s != 0.0f) q = make_uint2(quant4(v[i].x, v[i].y, s), quant4(v[i].z, v[i].w, s));
+      if (s != 0.0f) q = make_uint2(quant4(v[i].x, v[i].y, s, y), quant4(v[i].z, v[i].w, s, y));
       out[idx] = q;
     }
   }
@@ -308,12 +325,13 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_stream_kernel(const ui
   amax = block_max(amax, red);
   unsigned short s_bits;
   const float s = scale_from_absmax(amax, &s_bits);
+  const float y = s != 0.0f ? 1.0f / s : 0.0f;
   if (threadIdx.x == 0) sx[m] = s_bits;
   uint2* out = x8 + m * k_vec;
   for (int idx = threadIdx.x; idx < k_vec; idx += kThreads) {
     const uint4 h = norm8(row[idx], gamma[idx], r);
     uint2 q = make_uint2(0u, 0u);
-    if (s != 0.0f) q = make_uint2(quant4(h.x, h.y, s), quant4(h.z, h.w, s));
+    if (s != 0.0f) q = make_uint2(quant4(h.x, h.y, s, y), quant4(h.z, h.w, s, y));
     out[idx] = q;
   }
 }
@@ -344,9 +362,10 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_scalar_kernel(const un
   amax = block_max(amax, red);
   unsigned short s_bits;
   const float s = scale_from_absmax(amax, &s_bits);
+  const float y = s != 0.0f ? 1.0f / s : 0.0f;
   if (threadIdx.x == 0) sx[m] = s_bits;
   for (int64_t k = threadIdx.x; k < K; k += kThreads)
-    x8[m * K + k] = s != 0.0f ? static_cast<int8_t>(quant1(norm1(row[k], gamma[k], r), s)) : int8_t(0);
+    x8[m * K + k] = s != 0.0f ? static_cast<int8_t>(quant1(norm1(row[k], gamma[k], r), s, y)) : int8_t(0);
 }
 
 }  // namespace

@@ -101,9 +101,16 @@ __global__ __launch_bounds__(256) void kv4_quant_kernel(const uint4* __restrict_
   const float s = __half2float(sh);
   unsigned q = 0, zz = 0;
   if (s != 0.0f) {
-    const float z = fminf(15.0f, fmaxf(0.0f, rintf(-lo / s)));
+    // correctly rounded quotients from one reciprocal (Markstein): q0 = x*y,
+    // x/s = fma(fma(-q0, s, x), y, q0); exact for FP16 x and FP16 s
+    const float y = 1.0f / s;
+    auto div_rn = [&](float x) {
+      const float q0 = x * y;
+      return __builtin_fmaf(__builtin_fmaf(-q0, s, x), y, q0);
+    };
+    const float z = fminf(15.0f, fmaxf(0.0f, rintf(div_rn(-lo))));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q |= unsigned(fminf(15.0f, fmaxf(0.0f, rintf(v[i] / s) + z))) << (4 * i);
+    for (int i = 0; i < 8; ++i) q |= unsigned(fminf(15.0f, fmaxf(0.0f, rintf(div_rn(v[i])) + z))) << (4 * i);
     zz = unsigned(z);
   }
   if (row < n_rows) {
