@@ -38,7 +38,8 @@
 //   strip:  v_mfma_i32_16x16x64_i8, up to 16 rows; one contiguous weight
 //           strip per wave, activations copied into LDS once (decode).
 //   skinny: v_mfma_i32_16x16x64_i8, 16-row M tiles, K split across the
-//           waves of a block; up to 64 rows (decode, memory-bound).
+//           waves of a block; up to 64 rows (decode, memory-bound), and up
+//           to 256 rows when one round of blocks covers the problem.
 //   large:  v_mfma_i32_32x32x32_i8, 128x128 or 256x256 block tiles, K
 //           optionally split across blocks; above 64 rows (prefill).
 // Weights always go global -> VGPR directly and are dequantized in
