@@ -116,9 +116,9 @@ SMALL = [
     (257, 384, 300, 128),
     (5, 256, 48, 0),
     (70, 384, 100, 0),
-    (200, 2048, 96, 128),   # 128x128 tiles, K split in 4
-    (97, 1920, 40, 128),    # K split in 2 with an odd group count per split
-    (256, 1024, 50, 0),     # per-channel with a K split
+    (200, 2048, 96, 128),   # skinny 64-row tiles: 4 row blocks of one strip, K split over 4 waves
+    (97, 1920, 40, 128),    # ... 15 groups: K parts of 3 and 4 groups per wave
+    (256, 1024, 50, 0),     # ... per-channel, 4 row blocks
     (300, 2048, 96, 128),   # large-M kernel, K split in 4 (INT32 partials + reduction)
     (290, 1920, 40, 128),   # ... K split in 2 with an odd group count per split
     (270, 1024, 50, 0),     # ... per-channel with a K split

@@ -118,27 +118,36 @@ template <int AUX>
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
 }
+// Same, with a wave-uniform part of the offset in an SGPR (soffset).  Callers
+// keep every byte that the descriptor's bound must catch in the per-lane
+// offset and only offsets known to stay inside the buffer in soffset.
+template <int AUX>
+__device__ __forceinline__ u32x4 buf_load16s(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX);
+}
+__device__ __forceinline__ uint32_t buf_load4s(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+// Packed 16-bit lanes, written as vector arithmetic (selected as v_pk_mad_u16
+// and friends) so that the scheduler sees ordinary VALU instructions.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t c) {
-  uint32_t d;
-  asm("v_pk_mad_u16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
-  return d;
+  const u16x2 r = __builtin_bit_cast(u16x2, a) * __builtin_bit_cast(u16x2, b) + __builtin_bit_cast(u16x2, c);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 __device__ __forceinline__ uint32_t pk_mad_i16(uint32_t a, uint32_t b, uint32_t c) {
-  uint32_t d;
-  asm("v_pk_mad_i16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
-  return d;
+  const i16x2 r = __builtin_bit_cast(i16x2, a) * __builtin_bit_cast(i16x2, b) + __builtin_bit_cast(i16x2, c);
+  return __builtin_bit_cast(uint32_t, r);
 }
 __device__ __forceinline__ uint32_t pk_max_i16(uint32_t a, uint32_t b) {
-  uint32_t d;
-  asm("v_pk_max_i16 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
-  return d;
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(i16x2, a), __builtin_bit_cast(i16x2, b)));
 }
 __device__ __forceinline__ uint32_t pk_min_i16(uint32_t a, uint32_t b) {
-  uint32_t d;
-  asm("v_pk_min_i16 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
-  return d;
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(i16x2, a), __builtin_bit_cast(i16x2, b)));
 }
 
 // Two packed words (16 codes) -> one 16-byte INT8 MFMA operand.
@@ -271,6 +280,11 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int row, int col, i
 // blocks), and streams its weights through a PF-deep register ring of 128-bit
 // loads so that enough bytes are in flight to cover HBM latency.  The KS
 // partial INT32 accumulators are summed exactly through LDS at the end.
+// VALU instructions scheduled after each MFMA of the skinny kernel (0: leave
+// the order to the compiler).
+#ifndef QOQ_SIGLP
+#define QOQ_SIGLP 0
+#endif
 template <int TM, int TN, int KS, int PF, int AD, int WF, bool I32OUT>
 __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
   static_assert(PF % AD == 0 && PF % 2 == 0, "the activation ring and the LDS ping-pong must tile the weight ring");
@@ -282,7 +296,9 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
   constexpr int kSmemBytes = KS * kStageBytes > kRedBytes ? KS * kStageBytes : kRedBytes;
   __shared__ __align__(16) int8_t smem[kSmemBytes];
   int* red = reinterpret_cast<int*>(smem);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave-uniform by construction; readfirstlane lets the compiler keep
+  // everything derived from it (K range, group indices) in SGPRs
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int8_t* stage = smem + wave * kStageBytes;
   const int c16 = lane & 15, j = lane >> 4;
   const int sbase = blockIdx.x * TN;
@@ -311,22 +327,34 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
   uint32_t mq[PF][TN];
   u32x4 aq[AD][TM][2];
 
-  // The block's strips are contiguous in the packed weights: one descriptor
-  // covers exactly the valid ones, so strips past N and groups past this
-  // wave's K range load zeros without touching memory.
+  // The block's strips are contiguous in the packed weights.  Every load's
+  // per-lane offset is the same loop-invariant lane * 16; the group moves the
+  // descriptor's base and the strip is a wave-uniform soffset, so a round of
+  // loads costs no vector ALU work.  The strip index in soffset is clamped to
+  // the last valid strip (a ragged last block re-reads it; its columns are
+  // never stored), and a group past this wave's K range gets a descriptor of
+  // size zero: its loads return zeros without touching memory.
   constexpr int kBlk = wf_block_bytes(WF);
   const int strip_bytes = a.G * kBlk;
-  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(reinterpret_cast<const int8_t*>(a.qw) + int64_t(sbase) * strip_bytes,
-                                               min(TN, a.n_strips - sbase) * strip_bytes);
+  const int nvalid = min(TN, a.n_strips - sbase);
+  const int8_t* wbase = reinterpret_cast<const int8_t*>(a.qw) + int64_t(sbase) * strip_bytes;
   auto load_b = [&](int g, u32x4 (&b)[TN][kVec], uint32_t (&m)[TN]) {
-    const int gofs = g < g1 ? g * kBlk : kDeadOffset;
-    const int gm = min(g, g1 - 1);
+    const bool live = g < g1;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase + (live ? g : 0) * kBlk, live ? nvalid * strip_bytes : 0);
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       // weights are streamed once per call: non-temporal loads
 #pragma unroll
-      for (int v = 0; v < kVec; ++v) b[t][v] = buf_load16<kCacheStream>(wrs, lane * 16 + v * 1024 + t * strip_bytes + gofs);
-      if constexpr (wf_group_meta(WF)) m[t] = a.meta[(int64_t(strip[t]) * a.G4q + (gm >> 2)) * 16 + c16];
+      for (int v = 0; v < kVec; ++v)
+        b[t][v] = buf_load16s<kCacheStream>(wr, lane * 16 + v * 1024, min(t, nvalid - 1) * strip_bytes);
+    }
+    if constexpr (wf_group_meta(WF)) {
+      // metadata dword of the group's 4-group run (clamped into the range)
+      const int gm = min(g, g1 - 1);
+      const int8_t* mbase = reinterpret_cast<const int8_t*>(a.meta) + (int64_t(sbase) * a.G4q + (gm >> 2)) * 64;
+      const __amdgpu_buffer_rsrc_t mr = make_rsrc(mbase, nvalid * a.G4q * 64);
+#pragma unroll
+      for (int t = 0; t < TN; ++t) m[t] = buf_load4s(mr, c16 * 4, min(t, nvalid - 1) * a.G4q * 64);
     }
   };
   // Activations are read in whole 128-byte rows: one load covers 8 rows x one
@@ -334,8 +362,12 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
   // used in full (loads in the MFMA operand layout would touch 16 half-used
   // lines each).  The descriptor covers the block's valid rows; rows past M
   // and groups past this wave's range read zeros without touching memory.
+  // As for the weights, the group moves the descriptor's base (a group past
+  // the range gets an empty descriptor); rows past M have a per-lane offset
+  // beyond the descriptor.
   const int ar8 = lane >> 3, aq8 = lane & 7;
-  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x8 + int64_t(m0) * K, int(min(TM * 16, a.M - m0) * K));
+  const int8_t* xbase = a.x8 + int64_t(m0) * K;
+  const int xbytes = int(min(TM * 16, a.M - m0) * K);
   int arow[TM][2];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -345,10 +377,12 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
       arow[i][hh] = m0 + rl < a.M ? int(rl * K) + 16 * aq8 : kDeadOffset;
     }
   auto load_a = [&](int g, u32x4 (&ar)[TM][2]) {
+    const bool live = g < g1;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(xbase + (live ? g : 0) * 128, live ? xbytes : 0);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) ar[i][hh] = buf_load16<0>(xrs, g < g1 ? arow[i][hh] + g * 128 : kDeadOffset);
+      for (int hh = 0; hh < 2; ++hh) ar[i][hh] = buf_load16<0>(xr, arow[i][hh]);
   };
   // Into this wave's LDS buffer (chunk-XOR swizzled, conflict-free both
   // ways), to be read back in the MFMA A layout: lane (c16, j) takes row c16
@@ -385,6 +419,17 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
         for (int i = 0; i < TM; ++i) acc[i][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i][h], bf, acc[i][t], 0, 0, 0);
       }
     }
+#if QOQ_SIGLP > 0
+    // Issue order: the operand reads, then each MFMA followed by a few VALU
+    // instructions, so that the dequantization of the next weight fragment
+    // runs while the matrix unit works on the current one.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * TM, 0);
+#pragma unroll
+    for (int k = 0; k < 2 * TN * TM; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, QOQ_SIGLP, 0);
+    }
+#endif
   };
 
   const int ng = g1 - g0;
@@ -980,6 +1025,29 @@ inline int pick_skinny_tn(int n_strips, int ny, int hi) {
   return best;
 }
 
+// Strips per block of the skinny kernel with 64-row tiles.  Besides its tn
+// weight strips every block reads a 64 x K activation slab (eight strips'
+// worth of bytes per group, mostly from L2); a block takes about
+// kActStrips + tn strip-times (fitted to K = 4096 runs of 1, 2 and 4 strips
+// per block), so the fewest rounds of 256 blocks times that wins, ties going
+// to more strips per block.
+#ifndef QOQ_ACT_STRIPS
+#define QOQ_ACT_STRIPS 4
+#endif
+inline int pick_skinny_tn_rows(int n_strips, int ny, int hi) {
+  int best = 1;
+  long best_cost = -1;
+  for (int tn = 1; tn <= hi; ++tn) {
+    const long blocks = long((n_strips + tn - 1) / tn) * ny;
+    const long cost = ((blocks + 255) / 256) * (QOQ_ACT_STRIPS + tn);
+    if (best_cost < 0 || cost <= best_cost) {
+      best = tn;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 #ifndef QOQ_SAD
 #define QOQ_SAD 2
 #endif
@@ -1002,7 +1070,8 @@ hipError_t launch_skinny_upto(int tn, const GemmArgs& a, hipStream_t st) {
 template <int TM, int WF, bool I32>
 hipError_t dispatch_skinny_tn(const GemmArgs& a, hipStream_t st) {
   constexpr int kHi = skinny_tn_max(TM);
-  const int tn = pick_skinny_tn(a.n_strips, (a.M + TM * 16 - 1) / (TM * 16), kHi);
+  const int ny = (a.M + TM * 16 - 1) / (TM * 16);
+  const int tn = TM == 4 ? pick_skinny_tn_rows(a.n_strips, ny, kHi) : pick_skinny_tn(a.n_strips, ny, kHi);
   return launch_skinny_upto<TM, WF, I32, kHi>(tn, a, st);
 }
 
@@ -1084,17 +1153,17 @@ inline LargePlan plan_large(int64_t M, int64_t N, int64_t K) {
 constexpr int64_t kSkinnyMaxM = QOQ_SKINNY_MAXM;
 
 // Up to 256 rows, the K-split skinny kernel (64-row tiles, partials summed in
-// LDS) also serves when it covers the whole problem in one round of blocks,
-// at least 4 strips each: the large kernel would split K across blocks there,
-// and its INT32 partials need a second pass through memory.
+// LDS) also serves when it covers the whole problem in one round of blocks:
+// the large kernel would split K across blocks there, and its INT32 partials
+// need a second pass through memory.
 constexpr int64_t kSkinnyMidMaxM = 256;
 inline bool skinny_mid(int64_t M, int64_t N) {
   if (M <= kSkinnyMaxM || M > kSkinnyMidMaxM) return false;
   const int n_strips = int(round_up(N, kStrip) / kStrip);
   const int ny = int((M + 63) / 64);
-  const int tn = pick_skinny_tn(n_strips, ny, skinny_tn_max(4));
+  const int tn = pick_skinny_tn_rows(n_strips, ny, skinny_tn_max(4));
   const int64_t blocks = int64_t((n_strips + tn - 1) / tn) * ny;
-  return tn >= 4 && blocks <= 256;
+  return blocks <= 256;
 }
 
 inline size_t workspace_bytes_of(int64_t M, int64_t N, int64_t K) {
