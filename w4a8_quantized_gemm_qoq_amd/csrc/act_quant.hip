@@ -262,14 +262,18 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_reg_kernel(const uint4
   const int64_t m = blockIdx.x;
   const uint4* row = x + m * ldx_vec;
   static_assert(VPT * 8 <= 64, "one flush per row");
-  uint4 v[VPT];
-  SumSq S;
+  // gamma is fetched together with the row, so that its latency overlaps the
+  // row's and the sum of squares instead of following the reduction
+  uint4 v[VPT], gv[VPT];
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     const int idx = threadIdx.x + i * kThreads;
     v[i] = idx < k_vec ? row[idx] : make_uint4(0, 0, 0, 0);
-    S.add8(v[i]);
+    gv[i] = idx < k_vec ? gamma[idx] : make_uint4(0, 0, 0, 0);
   }
+  SumSq S;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) S.add8(v[i]);
   S.flush();
   const float r = rms_factor(block_sum_u128(S.total, red_sum), int64_t(k_vec) * 8, eps);
   uint32_t amax = 0;
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_reg_kernel(const uint4
   for (int i = 0; i < VPT; ++i) {
     const int idx = threadIdx.x + i * kThreads;
     if (idx < k_vec) {
-      v[i] = norm8(v[i], gamma[idx], r);
+      v[i] = norm8(v[i], gv[i], r);
       amax = max(amax, max_abs_bits8(v[i]));
     }
   }

@@ -280,11 +280,6 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int row, int col, i
 // blocks), and streams its weights through a PF-deep register ring of 128-bit
 // loads so that enough bytes are in flight to cover HBM latency.  The KS
 // partial INT32 accumulators are summed exactly through LDS at the end.
-// VALU instructions scheduled after each MFMA of the skinny kernel (0: leave
-// the order to the compiler).
-#ifndef QOQ_SIGLP
-#define QOQ_SIGLP 0
-#endif
 template <int TM, int TN, int KS, int PF, int AD, int WF, bool I32OUT>
 __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
   static_assert(PF % AD == 0 && PF % 2 == 0, "the activation ring and the LDS ping-pong must tile the weight ring");
@@ -295,7 +290,6 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
   constexpr int kRedBytes = KS > 1 ? KS * TN * TM * 4 * 64 * 4 : 0;
   constexpr int kSmemBytes = KS * kStageBytes > kRedBytes ? KS * kStageBytes : kRedBytes;
   __shared__ __align__(16) int8_t smem[kSmemBytes];
-  int* red = reinterpret_cast<int*>(smem);
   // wave-uniform by construction; readfirstlane lets the compiler keep
   // everything derived from it (K range, group indices) in SGPRs
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -419,20 +413,33 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
         for (int i = 0; i < TM; ++i) acc[i][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i][h], bf, acc[i][t], 0, 0, 0);
       }
     }
-#if QOQ_SIGLP > 0
-    // Issue order: the operand reads, then each MFMA followed by a few VALU
-    // instructions, so that the dequantization of the next weight fragment
-    // runs while the matrix unit works on the current one.
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * TM, 0);
-#pragma unroll
-    for (int k = 0; k < 2 * TN * TM; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, QOQ_SIGLP, 0);
-    }
-#endif
   };
 
+  // Epilogue scales, loaded once the prologue's loads are in flight so that
+  // their latency hides behind the main loop (global loads retire in order,
+  // so no wait of the loop is held up by them): row scales of the lane's
+  // rows and column scales of the strips this wave stores.
+  // The raw FP16 bits are kept (addresses clamped into range, so there is no
+  // select on the loaded values) and converted only in the epilogue.
+  constexpr int kScN = KS > 1 ? (TN + KS - 1) / KS : TN;
+  unsigned short sxh[TM][4] = {}, sch[kScN] = {};
+  auto load_scales = [&]() {
+    if constexpr (!I32OUT) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sxh[i][r] = a.sx[min(m0 + i * 16 + 4 * j + r, a.M - 1)];
+#pragma unroll
+      for (int u = 0; u < kScN; ++u) {
+        const int t = min(KS > 1 ? wave + u * KS : u, TN - 1);
+        sch[u] = a.scale[min((sbase + t) * 16 + c16, a.N - 1)];
+      }
+    }
+  };
+  auto fp16 = [](unsigned short h) { return __half2float(__ushort_as_half(h)); };
+
   const int ng = g1 - g0;
+  if (ng <= 0) load_scales();
   if (ng > 0) {
     // prologue: activations of the first AD groups, then weights of the first
     // PF (loads retire in order: the first multiply waits only for what was
@@ -444,6 +451,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
     stage_a(aq[0], 0);
     load_a(g0 + AD, aq[0]);
     QOQ_COMPILER_FENCE();
+    load_scales();
 
     // full rounds of PF groups.  Loads are unconditional (past the range they
     // read zeros for free) so a round is straight-line code.  Step l: multiply
@@ -486,53 +494,41 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
   // Once every wave is done with its activation buffers, every wave parks its
   // partials in the same LDS; after a second barrier wave w sums and stores
   // strips w, w+KS, ... (lane holds rows 4*(lane/16)+r of each 16x16
-  // tile, column lane%16).  Scales are loaded before any store.
-  float sxv[TM][4];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sxv[i][r] = I32OUT ? 0.0f : row_scale(a, m0 + i * 16 + 4 * j + r);
+  // tile, column lane%16).  The scales were loaded before the main loop.
   if constexpr (KS > 1) {
     __syncthreads();  // every wave is done with its activation buffers
+    // [wave][strip][row tile][lane] 16-byte records: one 128-bit LDS write
+    // per accumulator tile and one 128-bit read per partial
+    v4i* red4 = reinterpret_cast<v4i*>(smem);
 #pragma unroll
     for (int t = 0; t < TN; ++t)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) red[(((wave * TN + t) * TM + i) * 4 + r) * 64 + lane] = acc[i][t][r];
+      for (int i = 0; i < TM; ++i) red4[((wave * TN + t) * TM + i) * 64 + lane] = acc[i][t];
     __syncthreads();
-    float sc[(TN + KS - 1) / KS];
-#pragma unroll
-    for (int u = 0; u < (TN + KS - 1) / KS; ++u) {
-      const int t = wave + u * KS;
-      sc[u] = (I32OUT || t >= TN) ? 0.0f : col_scale(a, (sbase + t) * 16 + c16);
-    }
 #pragma unroll
     for (int u = 0; u < (TN + KS - 1) / KS; ++u) {
       const int t = wave + u * KS;
       if (t < TN && sbase + t < a.n_strips) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i) {
+          v4i v = red4[(t * TM + i) * 64 + lane];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            int v = 0;
+          for (int w = 1; w < KS; ++w) v += red4[((w * TN + t) * TM + i) * 64 + lane];
 #pragma unroll
-            for (int w = 0; w < KS; ++w) v += red[(((w * TN + t) * TM + i) * 4 + r) * 64 + lane];
-            store_out<I32OUT>(a, m0 + i * 16 + 4 * j + r, (sbase + t) * 16 + c16, v, sxv[i][r], sc[u]);
-          }
+          for (int r = 0; r < 4; ++r)
+            store_out<I32OUT>(a, m0 + i * 16 + 4 * j + r, (sbase + t) * 16 + c16, v[r], fp16(sxh[i][r]), fp16(sch[u]));
+        }
       }
     }
   } else {
-    float sc[TN];
-#pragma unroll
-    for (int t = 0; t < TN; ++t) sc[t] = I32OUT ? 0.0f : col_scale(a, (sbase + t) * 16 + c16);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int t = 0; t < TN; ++t)
-          if (sbase + t < a.n_strips) store_out<I32OUT>(a, m0 + i * 16 + 4 * j + r, (sbase + t) * 16 + c16, acc[i][t][r], sxv[i][r], sc[t]);
+          if (sbase + t < a.n_strips)
+            store_out<I32OUT>(a, m0 + i * 16 + 4 * j + r, (sbase + t) * 16 + c16, acc[i][t][r], fp16(sxh[i][r]), fp16(sch[t]));
   }
 }
 
