@@ -66,10 +66,42 @@ __device__ __forceinline__ uint32_t quant4(uint32_t h01, uint32_t h23, float s, 
          ((uint32_t(q3) & 0xffu) << 24);
 }
 
+// Wave-wide reductions of a uint32 (every lane active).  Inside each row of
+// 16 lanes four DPP permutations (lane xor 1, lane xor 2, mirror within 8,
+// mirror within 16) leave every lane holding its row's result; the four rows
+// are then combined from one lane each, so the result is wave-uniform.
+// DPP moves are plain VALU operations, far cheaper than cross-lane permutes
+// through the LDS crossbar.
+constexpr int kDppXor1 = 0xb1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4e;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ uint32_t lane_u32(uint32_t v, int l) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp<kDppXor1>(v));
+  v = max(v, dpp<kDppXor2>(v));
+  v = max(v, dpp<kDppHalfMirror>(v));
+  v = max(v, dpp<kDppMirror>(v));
+  return max(max(lane_u32(v, 0), lane_u32(v, 16)), max(lane_u32(v, 32), lane_u32(v, 48)));
+}
+// Sum; the caller guarantees that the 64 addends sum below 2^32.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppMirror>(v);
+  return (lane_u32(v, 0) + lane_u32(v, 16)) + (lane_u32(v, 32) + lane_u32(v, 48));
+}
+
 // Block-wide max of a uint32 value; every thread gets the result.
 __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, 64)));
+  v = wave_max_u32(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) red[wave] = v;
   __syncthreads();
@@ -205,20 +237,26 @@ struct SumSq {
   }
 };
 
-// Block-wide sum of a 128-bit integer; every thread gets the result.
-__device__ __forceinline__ u128 block_sum_u128(u128 v, u128* red) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const unsigned long long lo = static_cast<unsigned long long>(v);
-    const unsigned long long hi = static_cast<unsigned long long>(v >> 64);
-    v += (u128(__shfl_xor(hi, off, 64)) << 64) | u128(__shfl_xor(lo, off, 64));
-  }
+// Block-wide sum of a 128-bit integer below 2^96 (a thread's sum of squares
+// holds at most K / 256 <= 2^10 squares below 2^80 each); every thread gets
+// the result.  The value is cut into four 24-bit limbs: 256 limbs sum below
+// 2^32, so each limb is reduced exactly in 32-bit lanes and the limbs are
+// recombined in 128-bit arithmetic at the end.
+__device__ __forceinline__ u128 block_sum_u128(u128 v, uint32_t (*red)[4]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  u128 r = red[0];
+  uint32_t s[4];
 #pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) r += red[w];
+  for (int k = 0; k < 4; ++k) s[k] = wave_sum_u32(static_cast<uint32_t>(v >> (24 * k)) & 0xffffffu);
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) red[wave][k] = s[k];
+  }
+  __syncthreads();
+  u128 r = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r += u128(red[w][k]) << (24 * k);
   return r;
 }
 
@@ -257,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_reg_kernel(const uint4
                                                                       int k_vec, const uint4* __restrict__ gamma,
                                                                       float eps, uint2* __restrict__ x8,
                                                                       unsigned short* __restrict__ sx) {
-  __shared__ u128 red_sum[kThreads / 64];
+  __shared__ uint32_t red_sum[kThreads / 64][4];
   __shared__ uint32_t red[kThreads / 64];
   const int64_t m = blockIdx.x;
   const uint4* row = x + m * ldx_vec;
@@ -308,7 +346,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_stream_kernel(const ui
                                                                          int k_vec, const uint4* __restrict__ gamma,
                                                                          float eps, uint2* __restrict__ x8,
                                                                          unsigned short* __restrict__ sx) {
-  __shared__ u128 red_sum[kThreads / 64];
+  __shared__ uint32_t red_sum[kThreads / 64][4];
   __shared__ uint32_t red[kThreads / 64];
   const int64_t m = blockIdx.x;
   const uint4* row = x + m * ldx_vec;
@@ -346,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_scalar_kernel(const un
                                                                          const unsigned short* __restrict__ gamma,
                                                                          float eps, int8_t* __restrict__ x8,
                                                                          unsigned short* __restrict__ sx) {
-  __shared__ u128 red_sum[kThreads / 64];
+  __shared__ uint32_t red_sum[kThreads / 64][4];
   __shared__ uint32_t red[kThreads / 64];
   const int64_t m = blockIdx.x;
   const unsigned short* row = x + m * ldx;
