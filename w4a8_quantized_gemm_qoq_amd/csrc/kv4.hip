@@ -42,6 +42,18 @@ constexpr int kRowBytes = kHeadDim / 2;
 constexpr int kAttnThreads = 256;
 constexpr int kMaxCacheLen = 32768;
 
+// DPP lane permutations (VALU operations, no trip through the LDS crossbar):
+// quad_perm [1,0,3,2] and [2,3,0,1] pair lanes as xor 1 and xor 2 do, and
+// row_ror:4 / row_ror:8 rotate each row of 16 lanes, keeping lane % 4.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xb1;
+constexpr int kDppXor2 = 0x4e;
+constexpr int kDppRor4 = 0x124;
+constexpr int kDppRor8 = 0x128;
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
@@ -240,8 +252,8 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       float v = s[u] * (dot32(q, c[u]) - float(z[u]) * qsum);
-      v += __shfl_xor(v, 1, 64);
-      v += __shfl_xor(v, 2, 64);
+      v += dppf<kDppXor1>(v);
+      v += dppf<kDppXor2>(v);
       const int t = base + 16 * u + tq;
       if (t < L) {
         mx = fmaxf(mx, v);
@@ -292,9 +304,17 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
       zacc = fmaf(w[u], float(z[u]), zacc);
     }
   }
-  // sum over the 16 token slots of the wave (lanes with equal p)
+  // sum over the 16 token slots of the wave (lanes with equal p): the four
+  // slots of a row by two rotations, then the four rows
 #pragma unroll
-  for (int off = 4; off < 64; off <<= 1) {
+  for (int i = 0; i < 32; ++i) {
+    acc[i] += dppf<kDppRor4>(acc[i]);
+    acc[i] += dppf<kDppRor8>(acc[i]);
+  }
+  zacc += dppf<kDppRor4>(zacc);
+  zacc += dppf<kDppRor8>(zacc);
+#pragma unroll
+  for (int off = 16; off < 64; off <<= 1) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] += __shfl_xor(acc[i], off, 64);
     zacc += __shfl_xor(zacc, off, 64);
