@@ -140,6 +140,9 @@ SMALL = [
     (256, 512, 4096, 128),  # up to 256 rows in one round of skinny blocks (4 strips, K split in LDS)
     (200, 384, 4000, 0),    # ... per-channel, ragged M and N (252 blocks)
     (40, 256, 32768, 128),  # skinny 64-row tiles at most 7 strips per block; rows past M read as zeros
+    (192, 640, 4096, 128),  # 3 row blocks of 4 strips (192 blocks): strip count from the activation-aware cost
+    (161, 384, 2000, 0),    # ... per-channel, 2 strips per block, ragged last row block and last strip block
+    (250, 1024, 160, 128),  # ... one strip per block, 4 row blocks, rows past M in the last
     (50, 384, 30000, 0),    # ... per-channel, ragged N
 ]
 

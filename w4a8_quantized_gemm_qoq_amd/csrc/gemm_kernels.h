@@ -701,16 +701,6 @@ struct ATile {
 };
 
 template <int NA, int THREADS>
-__device__ __forceinline__ void a_load(u32x4 (&r)[NA], const GemmArgs& a, int64_t K, int m0, int g) {
-#pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int ch = threadIdx.x + i * THREADS;
-    const int row = min(m0 + (ch >> 3), a.M - 1);  // rows past M read a valid row; results are masked
-    r[i] = *reinterpret_cast<const u32x4*>(a.x8 + int64_t(row) * K + int64_t(g) * 128 + (ch & 7) * 16);
-  }
-}
-
-template <int NA, int THREADS>
 __device__ __forceinline__ void a_store(const u32x4 (&r)[NA], int8_t* lds) {
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
@@ -723,25 +713,6 @@ __device__ __forceinline__ void a_store(const u32x4 (&r)[NA], int8_t* lds) {
 // (c16, hh) and (c16, 2+hh) hold K steps {0, 2} and {1, 3}; INT8 slots hold
 // one K step each.
 constexpr int wf_large_vec(int wf) { return wf == kWfW8 ? 4 : 2; }
-
-template <int TN, int WF>
-__device__ __forceinline__ void b_load(u32x4 (&b)[TN][wf_large_vec(WF)], uint32_t (&m)[TN], const GemmArgs& a,
-                                       const int (&strip)[TN], int c16, int hh, int g) {
-#pragma unroll
-  for (int t = 0; t < TN; ++t) {
-    if constexpr (WF == kWfW8) {
-      // K step s of lane (c32, hh) is K chunk 2s + hh = 16j + 64h of slot c16 + 16j + 64h
-      const u32x4* blk = a.qw + (int64_t(strip[t]) * a.G + g) * 128;
-#pragma unroll
-      for (int st = 0; st < 4; ++st) b[t][st] = blk[c16 + 16 * ((2 * st + hh) & 3) + 64 * ((2 * st + hh) >> 2)];
-    } else {
-      const u32x4* blk = a.qw + (int64_t(strip[t]) * a.G + g) * 64;
-      b[t][0] = blk[c16 + 16 * hh];
-      b[t][1] = blk[c16 + 16 * (2 + hh)];
-    }
-    if constexpr (wf_group_meta(WF)) m[t] = a.meta[(int64_t(strip[t]) * a.G4q + (g >> 2)) * 16 + c16];
-  }
-}
 
 // 32x32x32 B operand of K step s from one lane's loads of a group.
 template <int WF>
@@ -802,7 +773,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
   __shared__ __align__(16) int8_t As0[BM * 128];
   __shared__ __align__(16) int8_t As1[BM * 128];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
   // Tile order.  Workgroups are dispatched round-robin over the 8 XCDs, each
   // with its own L2.  Remap so that each XCD gets a contiguous run of tiles,
@@ -859,12 +830,66 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
   const int n = ge - gb;
   auto gcl = [&](int l) { return gb + min(l, n - 1); };
 
-  a_load<NA, THREADS>(ra[0], a, K, m0, gb);
+  // Global loads go through buffer descriptors: the per-lane offsets below
+  // are loop-invariant and the group is a wave-uniform soffset, so a round of
+  // loads costs no vector ALU work.  Every offset is clamped into the
+  // operands (rows past M read row M-1, strips past N the last strip, and
+  // groups past the range the last group), so no load leaves its buffer.
+  // Activations: chunk ch of the tile is row ch / 8, 16-byte chunk ch % 8.
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x8 + int64_t(m0) * K, int(min(BM, a.M - m0) * K));
+  int aoff[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int ch = threadIdx.x + i * THREADS;
+    aoff[i] = (min(m0 + (ch >> 3), a.M - 1) - m0) * int(K) + (ch & 7) * 16;
+  }
+  auto a_ld = [&](u32x4 (&r)[NA], int g) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) r[i] = buf_load16s<0>(xr, aoff[i], g * 128);
+  };
+  // Weights and group metadata: one descriptor over the (at most 2 TN)
+  // strips of this wave's columns.  UINT4 blocks: lane (c32, hh) loads slots
+  // c16 + 16 hh and c16 + 16 (2 + hh), K steps {0, 2} and {1, 3}; INT8 blocks:
+  // K step st is K chunk 2 st + hh = 16 j + 64 h, slot c16 + 16 j + 64 h.
+  constexpr int kBlk = wf_block_bytes(WF);
+  constexpr int kVec = wf_large_vec(WF);
+  const int sfirst = min(n0 >> 4, a.n_strips - 1);
+  const int nws = min(2 * TN, a.n_strips - sfirst);
+  const __amdgpu_buffer_rsrc_t wr =
+      make_rsrc(reinterpret_cast<const int8_t*>(a.qw) + int64_t(sfirst) * a.G * kBlk, nws * a.G * kBlk);
+  int woff[TN][kVec];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    const int sb = (strip[t] - sfirst) * a.G * kBlk;
+#pragma unroll
+    for (int v = 0; v < kVec; ++v) {
+      const int slot = WF == kWfW8 ? c16 + 16 * ((2 * v + hh) & 3) + 64 * ((2 * v + hh) >> 2) : c16 + 16 * (2 * v + hh);
+      woff[t][v] = sb + slot * 16;
+    }
+  }
+  // (formats without group metadata get an empty descriptor that is never used)
+  const __amdgpu_buffer_rsrc_t mr =
+      wf_group_meta(WF)
+          ? make_rsrc(reinterpret_cast<const int8_t*>(a.meta) + int64_t(sfirst) * a.G4q * 64, nws * a.G4q * 64)
+          : make_rsrc(a.qw, 0);
+  int moff[TN];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) moff[t] = ((strip[t] - sfirst) * a.G4q * 16 + c16) * 4;
+  auto b_ld = [&](u32x4 (&b)[TN][kVec], uint32_t (&m)[TN], int g) {
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) b[t][v] = buf_load16s<0>(wr, woff[t][v], g * kBlk);
+      if constexpr (wf_group_meta(WF)) m[t] = buf_load4s(mr, moff[t], (g >> 2) * 64);
+    }
+  };
+
+  a_ld(ra[0], gb);
   a_store<NA, THREADS>(ra[0], As0);
 #pragma unroll
-  for (int d = 1; d <= DA; ++d) a_load<NA, THREADS>(ra[d % DA], a, K, m0, gcl(d));
+  for (int d = 1; d <= DA; ++d) a_ld(ra[d % DA], gcl(d));
 #pragma unroll
-  for (int d = 0; d < D; ++d) b_load<TN, WF>(rb[d], rm[d], a, strip, c16, hh, gcl(d));
+  for (int d = 0; d < D; ++d) b_ld(rb[d], rm[d], gcl(d));
   __syncthreads();
 
   int l0 = 0;
@@ -873,11 +898,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
     for (int u = 0; u < D; ++u) {
       const int l = l0 + u;
       a_store<NA, THREADS>(ra[(u + 1) % DA], (u & 1) ? As0 : As1);
-      a_load<NA, THREADS>(ra[(u + 1) % DA], a, K, m0, gcl(l + 1 + DA));
+      a_ld(ra[(u + 1) % DA], gcl(l + 1 + DA));
       QOQ_COMPILER_FENCE();
       large_group<TM, TN, WF>(acc, (u & 1) ? As1 : As0, rb[u], rm[u], S, C, gb + l, row0, c32, hh);
       __syncthreads();
-      b_load<TN, WF>(rb[u], rm[u], a, strip, c16, hh, gcl(l + D));
+      b_ld(rb[u], rm[u], gcl(l + D));
       QOQ_COMPILER_FENCE();
     }
   }
