@@ -217,6 +217,40 @@ def test_extreme_valid_bytes(M):
     assert np.array_equal(acc.astype(np.int64), x8.astype(np.int64) @ w8.T)
 
 
+# largest multiple of 128 with 127 * 127 * K below 2^31 (the INT32 bound the packer enforces)
+KMAX = 133120
+
+
+@pytest.mark.parametrize("M,N", [(1, 40),     # strip kernel, activations and metadata fill 147 KB of LDS
+                                 (16, 48),    # activations exceed LDS: 16-row skinny kernel
+                                 (64, 40),    # 64-row skinny kernel, 260 groups per wave
+                                 (300, 64)])  # large kernel, 128x128 tile, K split 64 ways + reduction
+def test_max_k_near_int32_bound(M, N):
+    # K at the INT32 limit through every launch plan.  Row 0 of the weights is
+    # w8 = 121 throughout and row 0 of the activations 127, so accumulator
+    # (0, 0) is 127 * 121 * K, 95% of 2^31.  Sampled rows against an int64
+    # matmul of the reconstructed INT8 weights.
+    K = KMAX
+    G = K // 128
+    rng = np.random.default_rng(M + N)
+    q4 = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    s1 = rng.integers(1, 9, size=(N, G)).astype(np.uint8)   # |w8| <= 120, bytes in [8, 248]
+    z = rng.integers(0, 16, size=(N, G)).astype(np.uint8)
+    q4[0] = 11
+    s1[0] = 11
+    z[0] = 0
+    p = q.qoq_pack_codes(q4, s1, z, np.ones(N, np.float16), 128).to("cuda")
+    x8 = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    x8[0] = 127
+    print(f"[max K] M={M} N={N} K={K}", flush=True)
+    acc = q.qoq_w4a8_gemm_i32(dev(x8), p).cpu().numpy()
+    rows = sorted({0, M // 2, M - 1})
+    w8 = (q4.astype(np.int64) - np.repeat(z, 128, 1)) * np.repeat(s1, 128, 1).astype(np.int64)
+    ref = x8[rows].astype(np.int64) @ w8.T
+    assert ref[0, 0] == 127 * 121 * K
+    assert np.array_equal(acc[rows].astype(np.int64), ref)
+
+
 def test_output_canaries_and_determinism():
     M, K, N = 70, 512, 100
     X = synthetic.make_x(M, K, "frac", seed=1)
