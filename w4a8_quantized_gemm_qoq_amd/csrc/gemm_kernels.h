@@ -276,19 +276,20 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int row, int col, i
 }
 
 // ---------------------------------------------------------------------------
-// skinny: M <= 64 (decode).  A block is KS waves that split the K groups of
-// the same TN strips between them, so every wave streams different weight
-// bytes.  Each wave keeps its activation operand in registers, loaded straight
-// from L2 (the INT8 activations of a decode batch are small and shared by all
-// blocks), and streams its weights through a PF-deep register ring of 128-bit
-// loads so that enough bytes are in flight to cover HBM latency.  The KS
-// partial INT32 accumulators are summed exactly through LDS at the end.
+// skinny: M <= 64 (decode), and up to 256 rows when one round of blocks
+// covers the problem.  A block is KS waves that split the K groups of the
+// same TN strips between them, so every wave streams different weight bytes.
+// Each wave passes its activations (whole 128-byte rows, shared by all blocks
+// and mostly served from L2) through a wave-private LDS buffer into the MFMA
+// operand layout, and streams its weights through a PF-deep register ring of
+// 128-bit loads so that enough bytes are in flight to cover HBM latency.  The
+// KS partial INT32 accumulators are summed exactly through LDS at the end.
 template <int TM, int TN, int KS, int PF, int AD, int WF, bool I32OUT>
 __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
   static_assert(PF % AD == 0 && PF % 2 == 0, "the activation ring and the LDS ping-pong must tile the weight ring");
   // LDS: while multiplying, each wave stages its own activations in two
   // buffers of TM*16 rows x 128 B; afterwards the same memory holds the
-  // partial sums of every wave, [KS][TN][TM][4][64 lanes].
+  // partial sums of every wave, [KS][TN][TM][64 lanes] records of 4 INT32.
   constexpr int kStageBytes = 2 * TM * 16 * 128;
   constexpr int kRedBytes = KS > 1 ? KS * TN * TM * 4 * 64 * 4 : 0;
   constexpr int kSmemBytes = KS * kStageBytes > kRedBytes ? KS * kStageBytes : kRedBytes;
