@@ -113,6 +113,10 @@ def check_attention(Q, kk, vv, lengths):
     (3, 8, 2, 200, [200, 1, 0], 1.0),      # GQA, a single token, an empty sequence
     (1, 2, 1, 1000, [999], 4.0),           # sharp softmax, T not a multiple of 64
     (4, 4, 4, 256, [256, 255, 129, 64], 1.0),
+    (4, 16, 2, 96, [96, 50, 1, 33], 1.0),  # 8 heads per kv head: two 4-head blocks each, XCD-paired
+    (1, 6, 2, 128, [128], 1.0),            # 3 heads per kv head: one head per block
+    (1, 8, 2, 9000, [9000], 1.0),          # 4 heads per kv head, but 4 score rows exceed LDS: 2 per block
+    (1, 4, 1, 20000, [19999], 1.0),        # ... and one per block
 ])
 def test_kv4_attention_matches_oracle(B, H, Hkv, T, lengths, peak):
     kk, vv = make_cache(B, Hkv, T, seed=T + H)

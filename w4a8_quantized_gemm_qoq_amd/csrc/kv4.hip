@@ -140,40 +140,41 @@ __device__ __forceinline__ float ubyte(unsigned v) {
   return static_cast<float>((v >> (8 * k)) & 0xffu);
 }
 
-// <q[0..32), codes of 32 dims> for one 16-byte load: dword w holds dims
-// 8w..8w+7 (byte b: dims 8w+2b (low) and 8w+2b+1 (high)).
-__device__ __forceinline__ float dot32(const float (&q)[32], uint4 c) {
+// The R query heads of a block share every conversion of a code to float:
+// one v_cvt_f32_ubyte feeds R FMAs.  Codes of one 16-byte load: dword w holds
+// dims 8w..8w+7 (byte b: dims 8w+2b (low nibble) and 8w+2b+1 (high)).
+//
+// out[r] = <q[r][0..32), codes of 32 dims>
+template <int R>
+__device__ __forceinline__ void dot32(const float (&q)[R][32], uint4 c, float (&out)[R]) {
   const unsigned w[4] = {c.x, c.y, c.z, c.w};
-  float acc = 0.0f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) out[r] = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const unsigned lo = w[i] & 0x0f0f0f0fu, hi = (w[i] >> 4) & 0x0f0f0f0fu;
-    acc = fmaf(q[8 * i + 0], ubyte<0>(lo), acc);
-    acc = fmaf(q[8 * i + 1], ubyte<0>(hi), acc);
-    acc = fmaf(q[8 * i + 2], ubyte<1>(lo), acc);
-    acc = fmaf(q[8 * i + 3], ubyte<1>(hi), acc);
-    acc = fmaf(q[8 * i + 4], ubyte<2>(lo), acc);
-    acc = fmaf(q[8 * i + 5], ubyte<2>(hi), acc);
-    acc = fmaf(q[8 * i + 6], ubyte<3>(lo), acc);
-    acc = fmaf(q[8 * i + 7], ubyte<3>(hi), acc);
+    const float x[8] = {ubyte<0>(lo), ubyte<0>(hi), ubyte<1>(lo), ubyte<1>(hi),
+                        ubyte<2>(lo), ubyte<2>(hi), ubyte<3>(lo), ubyte<3>(hi)};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int r = 0; r < R; ++r) out[r] = fmaf(q[r][8 * i + e], x[e], out[r]);
   }
-  return acc;
 }
 
-// acc[d] += w * code[d] over the 32 dims of one 16-byte load.
-__device__ __forceinline__ void axpy32(float (&acc)[32], float w, uint4 c) {
+// acc[r][d] += w[r] * code[d] over the 32 dims of one 16-byte load.
+template <int R>
+__device__ __forceinline__ void axpy32(float (&acc)[R][32], const float (&w)[R], uint4 c) {
   const unsigned v[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const unsigned lo = v[i] & 0x0f0f0f0fu, hi = (v[i] >> 4) & 0x0f0f0f0fu;
-    acc[8 * i + 0] = fmaf(w, ubyte<0>(lo), acc[8 * i + 0]);
-    acc[8 * i + 1] = fmaf(w, ubyte<0>(hi), acc[8 * i + 1]);
-    acc[8 * i + 2] = fmaf(w, ubyte<1>(lo), acc[8 * i + 2]);
-    acc[8 * i + 3] = fmaf(w, ubyte<1>(hi), acc[8 * i + 3]);
-    acc[8 * i + 4] = fmaf(w, ubyte<2>(lo), acc[8 * i + 4]);
-    acc[8 * i + 5] = fmaf(w, ubyte<2>(hi), acc[8 * i + 5]);
-    acc[8 * i + 6] = fmaf(w, ubyte<3>(lo), acc[8 * i + 6]);
-    acc[8 * i + 7] = fmaf(w, ubyte<3>(hi), acc[8 * i + 7]);
+    const float x[8] = {ubyte<0>(lo), ubyte<0>(hi), ubyte<1>(lo), ubyte<1>(hi),
+                        ubyte<2>(lo), ubyte<2>(hi), ubyte<3>(lo), ubyte<3>(hi)};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r][8 * i + e] = fmaf(w[r], x[e], acc[r][8 * i + e]);
   }
 }
 
@@ -190,53 +191,67 @@ struct AttnArgs {
 
 // Tokens in flight per wave and pass: U loads of 16 tokens each.
 constexpr int kUnroll = 4;
+// Query heads per block, at most: the heads of one kv group share the
+// block's cache reads and code conversions; their scores sit side by side
+// in LDS ([R][T_max] floats, at most kAttnScoreLds bytes).
+constexpr int kMaxHeadsPerBlock = 4;
+constexpr size_t kAttnScoreLds = size_t(kMaxCacheLen) * sizeof(float);
 
+template <int R>
 __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(AttnArgs a) {
-  extern __shared__ float sc[];  // [T] scores, then weights
-  __shared__ float red[kAttnThreads / 64];
-  __shared__ float part[kAttnThreads / 64][kHeadDim + 1];
+  extern __shared__ float sc[];  // [R][T] scores, then weights
+  __shared__ float red[R][kAttnThreads / 64];
+  __shared__ float part[kAttnThreads / 64][R][kHeadDim + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int p = lane & 3;          // which 32 dims of the head
   const int tq = lane >> 2;        // token slot within the wave's 16
-  // Block -> (b, h).  Workgroups are dealt round-robin to the 8 XCDs, each
-  // with its own L2; the query heads that share a kv head are given
-  // consecutive slots on one XCD, so that the cache rows they all read come
-  // from that L2 after the first.  (Plain order when the grid does not tile.)
-  const int rep = a.H / a.Hkv;
-  int h = blockIdx.x, b = blockIdx.y;
+  // Block -> (b, R consecutive query heads of one kv head).  Workgroups are
+  // dealt round-robin to the 8 XCDs, each with its own L2; when a kv head
+  // has several blocks, they are given consecutive slots on one XCD, so that
+  // the cache rows they all read come from that L2 after the first.  (Plain
+  // order when the grid does not tile.)
+  const int rep = a.H / a.Hkv;     // query heads per kv head
+  const int bpg = rep / R;         // blocks per kv head
+  int hb = blockIdx.x, b = blockIdx.y;
   {
     const int nb = gridDim.x * gridDim.y;
     const int d = blockIdx.y * gridDim.x + blockIdx.x;
-    if (rep > 1 && nb % (8 * rep) == 0) {
+    if (bpg > 1 && nb % (8 * bpg) == 0) {
       const int xcd = d % 8, slot = d / 8;
-      const int pair = (slot / rep) * 8 + xcd;  // (b, kv head) index
+      const int pair = (slot / bpg) * 8 + xcd;  // (b, kv head) index
       b = pair / a.Hkv;
-      h = (pair % a.Hkv) * rep + slot % rep;
+      hb = (pair % a.Hkv) * bpg + slot % bpg;
     }
   }
-  const int g = h / rep;
+  const int h0 = hb * R;           // first query head of the block
+  const int g = h0 / rep;
   const int L = min(max(a.lengths[b], 0), a.T);
-  const int64_t row0 = (int64_t(b) * a.Hkv + g) * a.T;  // first cache row of this head
+  const int64_t row0 = (int64_t(b) * a.Hkv + g) * a.T;  // first cache row of this kv head
 
-  // q' = scale * q for this lane's 32 dims, and their sum
-  float q[32];
-  const uint4* qv = reinterpret_cast<const uint4*>(a.q + (int64_t(b) * a.H + h) * kHeadDim + 32 * p);
-  float qsum = 0.0f;
+  // q' = scale * q for this lane's 32 dims of each head, and their sums
+  float q[R][32], qsum[R];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 u = qv[i];
-    const unsigned w[4] = {u.x, u.y, u.z, u.w};
+  for (int r = 0; r < R; ++r) {
+    const uint4* qv = reinterpret_cast<const uint4*>(a.q + (int64_t(b) * a.H + h0 + r) * kHeadDim + 32 * p);
+    qsum[r] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      q[8 * i + 2 * j] = a.scale * __half2float(__ushort_as_half(static_cast<unsigned short>(w[j] & 0xffffu)));
-      q[8 * i + 2 * j + 1] = a.scale * __half2float(__ushort_as_half(static_cast<unsigned short>(w[j] >> 16)));
+    for (int i = 0; i < 4; ++i) {
+      const uint4 u = qv[i];
+      const unsigned w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        q[r][8 * i + 2 * j] = a.scale * __half2float(__ushort_as_half(static_cast<unsigned short>(w[j] & 0xffffu)));
+        q[r][8 * i + 2 * j + 1] = a.scale * __half2float(__ushort_as_half(static_cast<unsigned short>(w[j] >> 16)));
+      }
     }
-  }
 #pragma unroll
-  for (int i = 0; i < 32; ++i) qsum += q[i];
+    for (int i = 0; i < 32; ++i) qsum[r] += q[r][i];
+  }
 
   // pass 1: scores
-  float mx = -INFINITY;
+  float mx[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) mx[r] = -INFINITY;
   const uint4* kc = reinterpret_cast<const uint4*>(a.kc + row0 * kRowBytes);
   for (int base = wave * 16 * kUnroll; base < L; base += kAttnThreads / 4 * kUnroll) {
     uint4 c[kUnroll];
@@ -251,84 +266,110 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      float v = s[u] * (dot32(q, c[u]) - float(z[u]) * qsum);
-      v += dppf<kDppXor1>(v);
-      v += dppf<kDppXor2>(v);
+      float v[R];
+      dot32<R>(q, c[u], v);
       const int t = base + 16 * u + tq;
-      if (t < L) {
-        mx = fmaxf(mx, v);
-        if (p == 0) sc[t] = v;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        v[r] = s[u] * (v[r] - float(z[u]) * qsum[r]);
+        v[r] += dppf<kDppXor1>(v[r]);
+        v[r] += dppf<kDppXor2>(v[r]);
+        if (t < L) {
+          mx[r] = fmaxf(mx[r], v[r]);
+          if (p == 0) sc[r * a.T + t] = v[r];
+        }
       }
     }
   }
-  mx = wave_max(mx);
-  if (lane == 0) red[wave] = mx;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    mx[r] = wave_max(mx[r]);
+    if (lane == 0) red[r][wave] = mx[r];
+  }
   __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+#pragma unroll
+  for (int r = 0; r < R; ++r) mx[r] = fmaxf(fmaxf(red[r][0], red[r][1]), fmaxf(red[r][2], red[r][3]));
   __syncthreads();
 
-  // weights and their sum
-  float lsum = 0.0f;
-  for (int t = threadIdx.x; t < L; t += kAttnThreads) {
-    const float e = __expf(sc[t] - mx);
-    sc[t] = e;
-    lsum += e;
+  // weights and their sums
+  float lsum[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    lsum[r] = 0.0f;
+    for (int t = threadIdx.x; t < L; t += kAttnThreads) {
+      const float e = __expf(sc[r * a.T + t] - mx[r]);
+      sc[r * a.T + t] = e;
+      lsum[r] += e;
+    }
+    lsum[r] = wave_sum(lsum[r]);
+    if (lane == 0) red[r][wave] = lsum[r];
   }
-  lsum = wave_sum(lsum);
-  if (lane == 0) red[wave] = lsum;
   __syncthreads();
-  lsum = red[0] + red[1] + red[2] + red[3];
+#pragma unroll
+  for (int r = 0; r < R; ++r) lsum[r] = red[r][0] + red[r][1] + red[r][2] + red[r][3];
 
   // pass 2: o = sum_t a_t s_t (c_t - z_t), accumulated as
   // sum (a_t s_t) c_t - sum (a_t s_t z_t)
-  float acc[32];
+  float acc[R][32], zacc[R];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) acc[i] = 0.0f;
-  float zacc = 0.0f;
+  for (int r = 0; r < R; ++r) {
+    zacc[r] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[r][i] = 0.0f;
+  }
   const uint4* vc = reinterpret_cast<const uint4*>(a.vc + row0 * kRowBytes);
   for (int base = wave * 16 * kUnroll; base < L; base += kAttnThreads / 4 * kUnroll) {
     uint4 c[kUnroll];
-    float w[kUnroll];
+    float w[kUnroll][R];
     int z[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int t = base + 16 * u + tq;
       const int tc = min(t, L - 1);
       c[u] = vc[int64_t(tc) * 4 + p];
-      w[u] = t < L ? sc[tc] * __half2float(__ushort_as_half(a.vs[row0 + tc])) : 0.0f;
+      const float vs = __half2float(__ushort_as_half(a.vs[row0 + tc]));
+#pragma unroll
+      for (int r = 0; r < R; ++r) w[u][r] = t < L ? sc[r * a.T + tc] * vs : 0.0f;
       z[u] = a.vz[row0 + tc];
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      axpy32(acc, w[u], c[u]);
-      zacc = fmaf(w[u], float(z[u]), zacc);
+      axpy32<R>(acc, w[u], c[u]);
+#pragma unroll
+      for (int r = 0; r < R; ++r) zacc[r] = fmaf(w[u][r], float(z[u]), zacc[r]);
     }
   }
   // sum over the 16 token slots of the wave (lanes with equal p): the four
   // slots of a row by two rotations, then the four rows
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    acc[i] += dppf<kDppRor4>(acc[i]);
-    acc[i] += dppf<kDppRor8>(acc[i]);
-  }
-  zacc += dppf<kDppRor4>(zacc);
-  zacc += dppf<kDppRor8>(zacc);
+  for (int r = 0; r < R; ++r) {
 #pragma unroll
-  for (int off = 16; off < 64; off <<= 1) {
+    for (int i = 0; i < 32; ++i) {
+      acc[r][i] += dppf<kDppRor4>(acc[r][i]);
+      acc[r][i] += dppf<kDppRor8>(acc[r][i]);
+    }
+    zacc[r] += dppf<kDppRor4>(zacc[r]);
+    zacc[r] += dppf<kDppRor8>(zacc[r]);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) acc[i] += __shfl_xor(acc[i], off, 64);
-    zacc += __shfl_xor(zacc, off, 64);
-  }
-  if (tq == 0) {
+    for (int off = 16; off < 64; off <<= 1) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) part[wave][32 * p + i] = acc[i] - zacc;
+      for (int i = 0; i < 32; ++i) acc[r][i] += __shfl_xor(acc[r][i], off, 64);
+      zacc[r] += __shfl_xor(zacc[r], off, 64);
+    }
+    if (tq == 0) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) part[wave][r][32 * p + i] = acc[r][i] - zacc[r];
+    }
   }
   __syncthreads();
-  if (threadIdx.x < kHeadDim) {
-    const int d = threadIdx.x;
-    const float v = part[0][d] + part[1][d] + part[2][d] + part[3][d];
-    const float o = L > 0 ? v / lsum : 0.0f;
-    a.o[(int64_t(b) * a.H + h) * kHeadDim + d] = __half_as_ushort(__float2half_rn(o));
+  for (int idx = threadIdx.x; idx < R * kHeadDim; idx += kAttnThreads) {
+    const int r = idx / kHeadDim, d = idx % kHeadDim;
+    const float v = part[0][r][d] + part[1][r][d] + part[2][r][d] + part[3][r][d];
+    float ls = lsum[0];
+#pragma unroll
+    for (int k = 1; k < R; ++k) ls = r == k ? lsum[k] : ls;
+    const float o = L > 0 ? v / ls : 0.0f;
+    a.o[(int64_t(b) * a.H + h0 + r) * kHeadDim + d] = __half_as_ushort(__float2half_rn(o));
   }
 }
 
@@ -391,16 +432,31 @@ extern "C" int qoq_kv4_decode_attention(const void* q_fp16, const uint8_t* k_cod
   a.Hkv = Hkv;
   a.T = T_max;
   a.scale = softmax_scale;
-  const size_t lds = size_t(T_max) * sizeof(float);
-  auto* fn = kv4_decode_attention_kernel;
+  // heads per block: the largest of 4, 2, 1 that divides the group and
+  // whose scores fit the block's LDS budget
+  const int rep = H / Hkv;
+  int R = 1;
+  for (int r = kMaxHeadsPerBlock; r > 1; r >>= 1)
+    if (rep % r == 0 && size_t(r) * size_t(T_max) * sizeof(float) <= kAttnScoreLds) {
+      R = r;
+      break;
+    }
+  const size_t lds = size_t(R) * size_t(T_max) * sizeof(float);
+  const void* fn = R == 4 ? reinterpret_cast<const void*>(kv4_decode_attention_kernel<4>)
+                   : R == 2 ? reinterpret_cast<const void*>(kv4_decode_attention_kernel<2>)
+                            : reinterpret_cast<const void*>(kv4_decode_attention_kernel<1>);
   if (lds > 48 * 1024) {
-    const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                                hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxCacheLen * 4));
+    const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(kAttnScoreLds));
     if (attr != hipSuccess)
       return fail(QOQ_ERR_HIP, "qoq_kv4_decode_attention: LDS attribute: %s", hipGetErrorString(attr));
   }
-  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(H), static_cast<unsigned>(B)), dim3(kAttnThreads), lds,
-                     static_cast<hipStream_t>(stream), a);
+  const dim3 grid(static_cast<unsigned>(H / R), static_cast<unsigned>(B));
+  if (R == 4)
+    hipLaunchKernelGGL(kv4_decode_attention_kernel<4>, grid, dim3(kAttnThreads), lds, static_cast<hipStream_t>(stream), a);
+  else if (R == 2)
+    hipLaunchKernelGGL(kv4_decode_attention_kernel<2>, grid, dim3(kAttnThreads), lds, static_cast<hipStream_t>(stream), a);
+  else
+    hipLaunchKernelGGL(kv4_decode_attention_kernel<1>, grid, dim3(kAttnThreads), lds, static_cast<hipStream_t>(stream), a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(QOQ_ERR_HIP, "qoq_kv4_decode_attention: launch failed: %s", hipGetErrorString(e));
   return QOQ_OK;
