@@ -297,6 +297,17 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
   // wave-uniform by construction; readfirstlane lets the compiler keep
   // everything derived from it (K range, group indices) in SGPRs
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // (S, C) dequantization operands of every metadata byte, filled once per
+  // block: one LDS lookup replaces the per-(strip, group) decode arithmetic
+  __shared__ uint2 mtab[wf_group_meta(WF) ? 256 : 1];
+  if constexpr (wf_group_meta(WF)) {
+    for (int e = threadIdx.x; e < 256; e += 64 * KS) {
+      uint32_t s0, c0;
+      meta_g128<WF>(uint32_t(e), s0, c0);
+      mtab[e] = make_uint2(s0, c0);
+    }
+    __syncthreads();
+  }
   int8_t* stage = smem + wave * kStageBytes;
   const int c16 = lane & 15, j = lane >> 4;
   const int sbase = blockIdx.x * TN;
@@ -406,7 +417,11 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
         af[i][h] = *reinterpret_cast<const v4i*>(stage + ((g - g0) & 1) * (TM * 16 * 128) + lds_off(16 * i + c16, j + 4 * h));
     if constexpr (wf_group_meta(WF)) {
 #pragma unroll
-      for (int t = 0; t < TN; ++t) meta_g128<WF>((mc[t] >> (8 * (g & 3))) & 0xffu, S[t], C[t]);
+      for (int t = 0; t < TN; ++t) {
+        const uint2 e = mtab[(mc[t] >> (8 * (g & 3))) & 0xffu];
+        S[t] = e.x;
+        C[t] = e.y;
+      }
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
