@@ -127,8 +127,8 @@ SMALL = [
     (16, 512, 9615, 128),   # strip kernel: 3 strips x 2 K parts per block, dead waves past N
     (1, 256, 27990, 0),     # strip kernel: 7 strips per block, per-channel, ragged N
     (12, 384, 200, 128),    # strip kernel: odd row count, K split in 8 with empty parts
-    (16, 10240, 40, 128),   # strip kernel: activations fill the whole 160 KB of LDS
-    (16, 10368, 40, 128),   # activations exceed LDS: K-split skinny kernel instead
+    (16, 10112, 40, 128),   # strip kernel: activations and metadata fill all 160 KB of LDS
+    (16, 10240, 40, 128),   # one group more exceeds LDS: K-split skinny kernel instead
     (16, 2048, 20000, 128), # strip kernel, 5 strips per block: second activation copy after the barrier
     (7, 1664, 17000, 0),    # ... per-channel, odd row count, copies running into padding
     (512, 256, 24576, 128), # 256x256 tiles (192 of them), 2 groups
