@@ -217,6 +217,30 @@ def test_extreme_valid_bytes(M):
     assert np.array_equal(acc.astype(np.int64), x8.astype(np.int64) @ w8.T)
 
 
+@pytest.mark.parametrize("M", [1, 24, 64, 300])  # strip, 32-row skinny, 64-row skinny, large kernel
+def test_every_valid_metadata_byte(M):
+    # Every (s1, z) pair whose dequantized bytes q4*s1 + 128 - z*s1 stay in
+    # [0, 255] for all q4 (the condition of the carry-free packed form), cycled
+    # over 48 channels x 8 groups, through each kernel's metadata decode;
+    # INT32 accumulators against an int64 matmul.
+    N, K = 48, 1024
+    G = K // 128
+    pairs = [(s, zz) for s in range(1, 17) for zz in range(16) if zz * s <= 128 and s * (15 - zz) <= 127]
+    assert len(pairs) == 177
+    rng = np.random.default_rng(M)
+    idx = (np.arange(N * G) + M) % len(pairs)
+    s1 = np.array([pairs[i][0] for i in idx], np.uint8).reshape(N, G)
+    z = np.array([pairs[i][1] for i in idx], np.uint8).reshape(N, G)
+    q4 = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    p = q.qoq_pack_codes(q4, s1, z, np.ones(N, np.float16), 128).to("cuda")
+    x8 = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    print(f"[meta bytes] M={M}", flush=True)
+    acc = q.qoq_w4a8_gemm_i32(dev(x8), p).cpu().numpy()
+    w8 = (q4.astype(np.int64) - np.repeat(z, 128, 1)) * np.repeat(s1, 128, 1).astype(np.int64)
+    assert w8.min() >= -128 and w8.max() <= 127
+    assert np.array_equal(acc.astype(np.int64), x8.astype(np.int64) @ w8.T)
+
+
 # largest multiple of 128 with 127 * 127 * K below 2^31 (the INT32 bound the packer enforces)
 KMAX = 133120
 
