@@ -155,7 +155,8 @@ def measure_comparators(torch, q, w, W, x8, sx, y, ws, t_g, reps: int):
     return r
 
 
-KV4_SHAPES = [("llama2_7b_mha", 64, 32, 32, 1024), ("llama3_8b_gqa", 64, 32, 8, 1024)]
+KV4_SHAPES = [("llama2_7b_mha", 64, 32, 32, 1024), ("llama3_8b_gqa", 64, 32, 8, 1024),
+              ("llama2_7b_mha_b4_t8k", 4, 32, 32, 8192), ("llama3_8b_gqa_b1_t32k", 1, 32, 8, 32768)]
 
 
 def kv4_bytes(B, H, Hkv, T) -> int:
@@ -166,7 +167,8 @@ def kv4_bytes(B, H, Hkv, T) -> int:
 
 def measure_kv4(torch, q, reps: int):
     """KV4 decode attention and KV quantization at 64 sequences x 1024 cached
-    tokens (the pages' 64 x 1024 attention input), head_dim 128."""
+    tokens (the pages' 64 x 1024 attention input), head_dim 128; and at two
+    small-batch long-cache shapes, where the token-split entry is timed too."""
     import numpy as np
     dev = torch.device("cuda")
     out = []
@@ -192,11 +194,24 @@ def measure_kv4(torch, q, reps: int):
                                                                          caches[i % copies][1], lengths, scale, o=o),
                              reps)
         nb = kv4_bytes(B, H, Hkv, T)
-        out.append({"shape": name, "B": B, "H": H, "Hkv": Hkv, "T": T, "attention_us": round(t_attn, 3),
-                    "attention_gbs": round(nb / t_attn / 1e3, 1),
-                    "attention_frac_hbm": round(nb / t_attn / 1e3 / PEAK_HBM_GBS, 4),
-                    "cache_copies": copies, "kv_quant_us": round(t_quant, 3),
-                    "kv_quant_gbs": round((2 * B * Hkv * T * (256 + 67)) / t_quant / 1e3, 1)})
+        rec = {"shape": name, "B": B, "H": H, "Hkv": Hkv, "T": T, "attention_us": round(t_attn, 3),
+               "attention_gbs": round(nb / t_attn / 1e3, 1),
+               "attention_frac_hbm": round(nb / t_attn / 1e3 / PEAK_HBM_GBS, 4),
+               "cache_copies": copies, "kv_quant_us": round(t_quant, 3),
+               "kv_quant_gbs": round((2 * B * Hkv * T * (256 + 67)) / t_quant / 1e3, 1)}
+        need = q.qoq_kv4_decode_attention_workspace_size(B, H, Hkv, T)
+        if need:
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+            def split(i):
+                c = caches[i % copies]
+                q.qoq_kv4_decode_attention(qq, c[0], c[1], lengths, scale, o=o, split=True, workspace=ws)
+            for i in range(copies):
+                split(i)
+            t_split = time_kernel(torch, split, reps)
+            rec.update({"split_attention_us": round(t_split, 3), "split_attention_gbs": round(nb / t_split / 1e3, 1),
+                        "split_attention_frac_hbm": round(nb / t_split / 1e3 / PEAK_HBM_GBS, 4)})
+        out.append(rec)
         del caches
         torch.cuda.empty_cache()
     return out

@@ -283,6 +283,33 @@ QOQ_API int qoq_kv4_decode_attention(const void* q_fp16, const uint8_t* k_codes,
                              const uint8_t* v_zero, const int32_t* lengths, int32_t B, int32_t H, int32_t Hkv,
                              int32_t T_max, int32_t head_dim, float softmax_scale, void* o_fp16, void* stream);
 
+/*
+ * Workspace (bytes) qoq_kv4_decode_attention_split needs for this shape; 0
+ * when the shape is not split (then that entry runs the single-pass kernel).
+ * 0 also for arguments qoq_kv4_decode_attention would reject.
+ */
+QOQ_API size_t qoq_kv4_decode_attention_workspace_size(int32_t B, int32_t H, int32_t Hkv, int32_t T_max);
+
+/*
+ * The same decode attention with the cached tokens cut into chunks spread
+ * over more workgroups, for batches too small to fill the GPU with one
+ * workgroup per (sequence, kv-head group).  Each chunk keeps its own softmax
+ * statistics (the chunk's largest score m_c, l_c = sum exp(s_t - m_c), and
+ * the unnormalized sum of exp(s_t - m_c) v_t) in FP32 in the workspace; a
+ * second kernel rescales them to the overall largest score M and writes
+ * o = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c.  The result equals
+ * qoq_kv4_decode_attention's up to FP32 rounding order.  Arguments as
+ * there, plus workspace: device, 16-byte aligned, at least
+ * qoq_kv4_decode_attention_workspace_size(B, H, Hkv, T_max) bytes, owned by
+ * the caller and overwritten (QOQ_ERR_INVALID_ARG if too small).  Calls
+ * that share a workspace must be ordered on one stream.
+ */
+QOQ_API int qoq_kv4_decode_attention_split(const void* q_fp16, const uint8_t* k_codes, const void* k_scale_fp16,
+                                   const uint8_t* k_zero, const uint8_t* v_codes, const void* v_scale_fp16,
+                                   const uint8_t* v_zero, const int32_t* lengths, int32_t B, int32_t H,
+                                   int32_t Hkv, int32_t T_max, int32_t head_dim, float softmax_scale,
+                                   void* o_fp16, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Comparators of the W4A8 GEMM.  They run the same kernels, launch plans and
  * epilogue, so that the cost of the weight format is measured on its own.

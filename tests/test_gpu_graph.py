@@ -59,19 +59,23 @@ def test_quant_gemm_graph_replays(M, K, N):
         torch.cuda.synchronize()
 
 
-def test_kv4_graph_replays():
-    B, H, Hkv, T = 4, 8, 2, 300
+@pytest.mark.parametrize("split", [False, True])
+def test_kv4_graph_replays(split):
+    B, H, Hkv, T = 4, 8, 2, 600
     rng = np.random.default_rng(0)
     kv = torch.from_numpy(rng.standard_normal((2, B, Hkv, T, 128)).astype(np.float16)).cuda()
     qq = torch.from_numpy(rng.standard_normal((B, H, 128)).astype(np.float16)).cuda()
-    lengths = torch.tensor([300, 1, 0, 157], dtype=torch.int32, device="cuda")
+    lengths = torch.tensor([600, 1, 0, 357], dtype=torch.int32, device="cuda")
     o = torch.empty((B, H, 128), dtype=torch.float16, device="cuda")
+    need = q.qoq_kv4_decode_attention_workspace_size(B, H, Hkv, T)
+    assert need > 0                  # this shape is split when asked
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
     caches = [q.qoq_kv4_quant(kv[0]), q.qoq_kv4_quant(kv[1])]
 
     def step():
         for i, c in enumerate(caches):
             q.qoq_kv4_quant(kv[i], *c)
-        q.qoq_kv4_decode_attention(qq, caches[0], caches[1], lengths, 0.0883883476, o=o)
+        q.qoq_kv4_decode_attention(qq, caches[0], caches[1], lengths, 0.0883883476, o=o, split=split, workspace=ws)
 
     step()
     torch.cuda.synchronize()

@@ -79,15 +79,15 @@ def make_cache(B, Hkv, T, seed, peak=1.0):
     return O.kv4_quant_per_head(K), O.kv4_quant_per_head(V)
 
 
-def run_attention(Q, kk, vv, lengths):
+def run_attention(Q, kk, vv, lengths, split=False):
     k = (dev(pack_codes(kk[0])), dev(kk[1]), dev(kk[2]))
     v = (dev(pack_codes(vv[0])), dev(vv[1]), dev(vv[2]))
-    o = q.qoq_kv4_decode_attention(dev(Q), k, v, dev(np.asarray(lengths, np.int32)), SCALE)
+    o = q.qoq_kv4_decode_attention(dev(Q), k, v, dev(np.asarray(lengths, np.int32)), SCALE, split=split)
     return o.cpu().numpy()
 
 
-def check_attention(Q, kk, vv, lengths):
-    o = run_attention(Q, kk, vv, lengths).astype(np.float64)
+def check_attention(Q, kk, vv, lengths, split=False):
+    o = run_attention(Q, kk, vv, lengths, split).astype(np.float64)
     ref = O.kv4_decode_attention(Q, *kk, *vv, lengths, SCALE).astype(np.float64)
     B, H, _ = Q.shape
     Hkv = kk[0].shape[1]
@@ -100,7 +100,7 @@ def check_attention(Q, kk, vv, lengths):
     tol = ulp16(ref) + 2.0 ** -12 * vmax[..., None]
     err = np.abs(o - ref)
     worst = float((err / tol).max())
-    print(f"[kv4 attn] B={B} H={H} Hkv={Hkv} worst err/tol = {worst:.3f}", flush=True)
+    print(f"[kv4 attn] B={B} H={H} Hkv={Hkv} split={split} worst err/tol = {worst:.3f}", flush=True)
     assert np.all(np.isfinite(o))
     assert np.all(err <= tol), f"worst err/tol {worst}"
     for b in range(B):
@@ -141,3 +141,49 @@ def test_kv4_attention_bench_shape(H, Hkv):
     kk, vv = make_cache(B, Hkv, T, seed=H + Hkv)
     Q = np.random.default_rng(7).standard_normal((B, H, 128)).astype(np.float16)
     check_attention(Q, kk, vv, [T] * B)
+
+
+# Token-split attention: chunks of the cache over more workgroups, their
+# softmax partials combined afterwards.  Same oracle, same tolerance.
+@pytest.mark.parametrize("B,H,Hkv,T,lengths,peak", [
+    (1, 32, 8, 4096, [4096], 1.0),             # 16 chunks of 256 tokens, four heads a workgroup
+    (2, 32, 32, 3000, [3000, 1], 1.0),         # MHA, 12 chunks of 256; one token: 11 empty chunks
+    (4, 32, 32, 4096, [4096, 3000, 1025, 0], 1.0),  # 4 chunks of 1024; 1025: a one-token chunk
+    (3, 8, 2, 1000, [1000, 0, 513], 1.0),      # empty sequence; 513 = two chunks and one token
+    (1, 2, 1, 1000, [999], 4.0),               # sharp softmax across chunks
+    (1, 6, 2, 2000, [1777], 1.0),              # 3 heads per kv head: one a workgroup
+    (1, 4, 1, 32768, [32768], 1.0),            # the longest cache: 128 chunks
+    (1, 32, 8, 32768, [30001], 1.0),           # 512-token chunks; the last six partial or empty
+    (2, 8, 1, 20000, [20000, 8191], 1.0),      # 8-head groups, chunk ends inside a sequence
+])
+def test_kv4_attention_split_matches_oracle(B, H, Hkv, T, lengths, peak):
+    assert q.qoq_kv4_decode_attention_workspace_size(B, H, Hkv, T) > 0
+    kk, vv = make_cache(B, Hkv, T, seed=T + 3 * H)
+    Q = (np.random.default_rng(B + 11).standard_normal((B, H, 128)) * peak).astype(np.float16)
+    check_attention(Q, kk, vv, lengths, split=True)
+
+
+def test_kv4_attention_split_entry_without_split_is_the_plain_kernel():
+    """Shapes that are not split (here 64 x 32 heads: 512 workgroups already)
+    run the single-pass kernel through the split entry: identical bits."""
+    B, H, Hkv, T = 64, 32, 8, 600
+    assert q.qoq_kv4_decode_attention_workspace_size(B, H, Hkv, T) == 0
+    kk, vv = make_cache(B, Hkv, T, seed=5)
+    Q = np.random.default_rng(5).standard_normal((B, H, 128)).astype(np.float16)
+    lengths = np.random.default_rng(6).integers(0, T + 1, B).astype(np.int32)
+    a = run_attention(Q, kk, vv, lengths, split=False)
+    b = run_attention(Q, kk, vv, lengths, split=True)
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def test_kv4_attention_split_agrees_with_single_pass():
+    """Split and single-pass results differ only by FP32 summation order, so
+    by at most the attention tolerance: one FP16 ulp plus 2^-12 of the
+    largest |v| (outputs near cancellation lose relative accuracy)."""
+    B, H, Hkv, T = 1, 32, 8, 8192
+    kk, vv = make_cache(B, Hkv, T, seed=9)
+    Q = np.random.default_rng(9).standard_normal((B, H, 128)).astype(np.float16)
+    a = run_attention(Q, kk, vv, [T], split=False).astype(np.float64)
+    b = run_attention(Q, kk, vv, [T], split=True).astype(np.float64)
+    vmax = float(np.abs(O.kv4_dequant(*vv)).max())
+    assert np.all(np.abs(a - b) <= ulp16(a) + 2.0 ** -12 * vmax)

@@ -25,7 +25,7 @@ def header_symbols():
 def test_library_exports_every_header_symbol():
     lib = q.load_library()
     syms = header_symbols()
-    assert len(syms) == 22, syms
+    assert len(syms) == 24, syms
     assert sorted(_native.EXPORTS) == syms
     for s in syms:
         assert hasattr(lib, s), s
@@ -343,6 +343,44 @@ def test_kv4_entry_points_validate_before_launch():
     assert lib.qoq_kv4_decode_attention(*args, 2, 4, 2, 16, 128, float("nan"), d, None) == 1
     assert lib.qoq_kv4_decode_attention(d + 8, *args[1:], 2, 4, 2, 16, 128, 0.1, d, None) == 3
     assert lib.qoq_kv4_decode_attention(None, *args[1:], 2, 4, 2, 16, 128, 0.1, d, None) == 1
+    # the token-split entry: same checks, plus its workspace
+    assert lib.qoq_kv4_decode_attention_split(*args, 2, 4, 3, 16, 128, 0.1, d, d, 1 << 20, None) == 2
+    need = lib.qoq_kv4_decode_attention_workspace_size(1, 32, 8, 4096)
+    assert need > 0
+    assert lib.qoq_kv4_decode_attention_split(*args, 1, 32, 8, 4096, 128, 0.1, d, d, need - 1, None) == 1
+    assert lib.qoq_kv4_decode_attention_split(*args, 1, 32, 8, 4096, 128, 0.1, d, None, need, None) == 1
+    assert lib.qoq_kv4_decode_attention_split(*args, 1, 32, 8, 4096, 128, 0.1, d, d + 4, need, None) == 3
+
+
+def test_kv4_attention_split_plan():
+    """Workspace of the token-split attention: nc chunks x B x H x (128 outputs
+    + max + sum) FP32.  Nothing is split once (sequence, head group)
+    workgroups alone reach 256, or below 512 cached tokens; otherwise chunks
+    are 1024 tokens, halved (down to 256) while fewer than 512 workgroups
+    would result."""
+    ws = q.load_library().qoq_kv4_decode_attention_workspace_size
+
+    def chunks(B, H, Hkv, T):
+        n = ws(B, H, Hkv, T)
+        assert n % (B * H * 130 * 4) == 0
+        return n // (B * H * 130 * 4)
+
+    # 1 x 32 heads over 8 kv heads: 8 four-head workgroups; 256-token chunks
+    # still give only 128 workgroups
+    assert chunks(1, 32, 8, 4096) == 16
+    assert chunks(1, 32, 8, 32768) == 64       # 512-token chunks: 512 workgroups
+    # MHA, 2 x 32 one-head workgroups: 1024 -> 192, 512 -> 384, 256 -> 768
+    assert chunks(2, 32, 32, 3000) == 12
+    assert chunks(4, 32, 32, 4096) == 4        # 128 workgroups x 4 chunks of 1024
+    assert chunks(1, 4, 1, 32768) == 128       # one four-head workgroup: 256-token chunks
+    assert chunks(1, 4, 1, 511) == 0           # too short to split
+    assert chunks(1, 4, 1, 512) == 2
+    assert chunks(64, 32, 8, 1024) == 0        # 512 workgroups already
+    assert chunks(32, 32, 8, 1024) == 0        # 256: one per CU
+    assert chunks(8, 32, 1, 4096) == 8         # 8 x 8 four-head workgroups x 8 chunks of 512
+    assert chunks(1, 6, 2, 2000) == 8          # 3 heads per kv head: one a workgroup
+    assert ws(2, 4, 3, 4096) == 0              # invalid shapes: 0
+    assert ws(1, 4, 1, 40000) == 0
 
 
 # ------------------------------------------------- offline transforms (f4)

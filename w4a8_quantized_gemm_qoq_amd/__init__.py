@@ -14,6 +14,7 @@ from ._native import (  # noqa: F401
     load_library,
     qoq_hadamard_rotate,
     qoq_kv4_decode_attention,
+    qoq_kv4_decode_attention_workspace_size,
     qoq_kv4_quant,
     qoq_pack_codes,
     qoq_pack_weights,

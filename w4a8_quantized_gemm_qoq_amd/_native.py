@@ -39,6 +39,8 @@ EXPORTS = [
     "qoq_w4a8_gemm_saturating_i32",
     "qoq_kv4_quant",
     "qoq_kv4_decode_attention",
+    "qoq_kv4_decode_attention_workspace_size",
+    "qoq_kv4_decode_attention_split",
     "qoq_hadamard_rotate",
     "qoq_smoothing_factors",
     "qoq_scale_columns",
@@ -106,6 +108,9 @@ def load_library():
         "qoq_kv4_quant": (ctypes.c_int, [vp, i64, i32, i64, vp, vp, vp, vp]),
         "qoq_kv4_decode_attention": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                                     ctypes.c_float, vp, vp]),
+        "qoq_kv4_decode_attention_workspace_size": (sz, [i32, i32, i32, i32]),
+        "qoq_kv4_decode_attention_split": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                                          ctypes.c_float, vp, vp, sz, vp]),
         "qoq_hadamard_rotate": (ctypes.c_int, [vp, i64, i64, i64, vp]),
         "qoq_smoothing_factors": (ctypes.c_int, [vp, vp, i64, ctypes.c_float, vp]),
         "qoq_scale_columns": (ctypes.c_int, [vp, i64, i64, i64, vp, i32, vp]),
@@ -486,9 +491,19 @@ def qoq_kv4_quant(x, codes=None, scale=None, zero=None, stream=None):
     return codes, scale, zero
 
 
-def qoq_kv4_decode_attention(q, k, v, lengths, softmax_scale, o=None, stream=None):
+def qoq_kv4_decode_attention_workspace_size(B: int, H: int, Hkv: int, T: int) -> int:
+    """Bytes of workspace the token-split attention needs (0: that shape is not split)."""
+    return int(load_library().qoq_kv4_decode_attention_workspace_size(B, H, Hkv, T))
+
+
+def qoq_kv4_decode_attention(q, k, v, lengths, softmax_scale, o=None, stream=None, split=False, workspace=None):
     """Decode attention of q [B, H, 128] FP16 over KV4 caches k, v = (codes
-    [B, Hkv, T, 64], scale [B, Hkv, T], zero [B, Hkv, T]); lengths int32 [B]."""
+    [B, Hkv, T, 64], scale [B, Hkv, T], zero [B, Hkv, T]); lengths int32 [B].
+
+    split=True calls the token-split entry (chunks of the cache over more
+    workgroups, for small batches); its workspace is allocated here unless a
+    uint8 device tensor of at least the queried size is given.
+    """
     import torch
     kc, ks, kz = k
     vc, vs, vz = v
@@ -507,9 +522,17 @@ def qoq_kv4_decode_attention(q, k, v, lengths, softmax_scale, o=None, stream=Non
         raise ValueError("lengths must be int32 [B]")
     o = torch.empty((B, H, HEAD_DIM), dtype=torch.float16, device=q.device) if o is None else o
     lib = load_library()
-    _check(lib.qoq_kv4_decode_attention(_t_ptr(q), _t_ptr(kc), _t_ptr(ks), _t_ptr(kz), _t_ptr(vc), _t_ptr(vs),
-                                        _t_ptr(vz), _t_ptr(lengths), B, H, Hkv, T, HEAD_DIM, float(softmax_scale),
-                                        _t_ptr(o), _stream(stream)), "qoq_kv4_decode_attention")
+    args = (_t_ptr(q), _t_ptr(kc), _t_ptr(ks), _t_ptr(kz), _t_ptr(vc), _t_ptr(vs), _t_ptr(vz), _t_ptr(lengths),
+            B, H, Hkv, T, HEAD_DIM, float(softmax_scale), _t_ptr(o))
+    if not split:
+        _check(lib.qoq_kv4_decode_attention(*args, _stream(stream)), "qoq_kv4_decode_attention")
+        return o
+    if workspace is None:
+        need = int(lib.qoq_kv4_decode_attention_workspace_size(B, H, Hkv, T))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _require_cuda(workspace)
+    _check(lib.qoq_kv4_decode_attention_split(*args, _t_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                              _stream(stream)), "qoq_kv4_decode_attention_split")
     return o
 
 

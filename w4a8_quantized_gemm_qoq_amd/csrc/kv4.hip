@@ -30,6 +30,7 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "qoq_internal.h"
@@ -182,6 +183,8 @@ struct AttnArgs {
   unsigned short* o;
   int H, Hkv, T;
   float scale;
+  int Tc;     // tokens per chunk when the tokens are split over blocks
+  float* ws;  // per-chunk partials: o [nc][B][H][128], max [nc][B][H], sum [nc][B][H]
 };
 
 // Tokens in flight per wave and pass: U loads of 16 tokens each.
@@ -192,9 +195,14 @@ constexpr int kUnroll = 4;
 constexpr int kMaxHeadsPerBlock = 4;
 constexpr size_t kAttnScoreLds = size_t(kMaxCacheLen) * sizeof(float);
 
-template <int R>
+// SPLIT: block (x, y, z) takes only tokens [z Tc, (z + 1) Tc) of its
+// sequence and writes that chunk's softmax partials (running max m, sum of
+// exp(s - m), unnormalized output) to the workspace; a second kernel combines
+// the chunks.  Used when (sequence, head group) pairs alone would leave most
+// CUs idle (small batches, long caches).
+template <int R, bool SPLIT>
 __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(AttnArgs a) {
-  extern __shared__ float sc[];  // [R][T] scores, then weights
+  extern __shared__ float sc[];  // [R][Ts] scores, then weights
   __shared__ float red[R][kAttnThreads / 64];
   __shared__ float part[kAttnThreads / 64][R][kHeadDim + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -222,6 +230,10 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
   const int g = h0 / rep;
   const int L = min(max(a.lengths[b], 0), a.T);
   const int64_t row0 = (int64_t(b) * a.Hkv + g) * a.T;  // first cache row of this kv head
+  // this block's tokens [t0, t1), and the stride of a score row in LDS
+  const int t0 = SPLIT ? int(blockIdx.z) * a.Tc : 0;
+  const int t1 = SPLIT ? min(L, t0 + a.Tc) : L;
+  const int Ts = SPLIT ? a.Tc : a.T;
 
   // q' = scale * q for this lane's 32 dims of each head, and their sums
   float q[R][32], qsum[R];
@@ -248,13 +260,13 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
 #pragma unroll
   for (int r = 0; r < R; ++r) mx[r] = -INFINITY;
   const uint4* kc = reinterpret_cast<const uint4*>(a.kc + row0 * kRowBytes);
-  for (int base = wave * 16 * kUnroll; base < L; base += kAttnThreads / 4 * kUnroll) {
+  for (int base = t0 + wave * 16 * kUnroll; base < t1; base += kAttnThreads / 4 * kUnroll) {
     uint4 c[kUnroll];
     float s[kUnroll];
     int z[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int t = min(base + 16 * u + tq, L - 1);  // past L: a valid token, result dropped
+      const int t = min(base + 16 * u + tq, t1 - 1);  // past t1: a valid token, result dropped
       c[u] = kc[int64_t(t) * 4 + p];
       s[u] = __half2float(__ushort_as_half(a.ks[row0 + t]));
       z[u] = a.kz[row0 + t];
@@ -269,9 +281,9 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
         v[r] = s[u] * (v[r] - float(z[u]) * qsum[r]);
         v[r] += dppf<kDppXor1>(v[r]);
         v[r] += dppf<kDppXor2>(v[r]);
-        if (t < L) {
+        if (t < t1) {
           mx[r] = fmaxf(mx[r], v[r]);
-          if (p == 0) sc[r * a.T + t] = v[r];
+          if (p == 0) sc[r * Ts + (t - t0)] = v[r];
         }
       }
     }
@@ -291,9 +303,9 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     lsum[r] = 0.0f;
-    for (int t = threadIdx.x; t < L; t += kAttnThreads) {
-      const float e = __expf(sc[r * a.T + t] - mx[r]);
-      sc[r * a.T + t] = e;
+    for (int t = threadIdx.x; t < t1 - t0; t += kAttnThreads) {
+      const float e = __expf(sc[r * Ts + t] - mx[r]);
+      sc[r * Ts + t] = e;
       lsum[r] += e;
     }
     lsum[r] = wave_sum(lsum[r]);
@@ -313,18 +325,18 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
     for (int i = 0; i < 32; ++i) acc[r][i] = 0.0f;
   }
   const uint4* vc = reinterpret_cast<const uint4*>(a.vc + row0 * kRowBytes);
-  for (int base = wave * 16 * kUnroll; base < L; base += kAttnThreads / 4 * kUnroll) {
+  for (int base = t0 + wave * 16 * kUnroll; base < t1; base += kAttnThreads / 4 * kUnroll) {
     uint4 c[kUnroll];
     float w[kUnroll][R];
     int z[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int t = base + 16 * u + tq;
-      const int tc = min(t, L - 1);
+      const int tc = min(t, t1 - 1);
       c[u] = vc[int64_t(tc) * 4 + p];
       const float vs = __half2float(__ushort_as_half(a.vs[row0 + tc]));
 #pragma unroll
-      for (int r = 0; r < R; ++r) w[u][r] = t < L ? sc[r * a.T + tc] * vs : 0.0f;
+      for (int r = 0; r < R; ++r) w[u][r] = t < t1 ? sc[r * Ts + (tc - t0)] * vs : 0.0f;
       z[u] = a.vz[row0 + tc];
     }
 #pragma unroll
@@ -357,14 +369,82 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
     }
   }
   __syncthreads();
+  const int64_t BH = int64_t(gridDim.y) * a.H;  // (sequence, query head) pairs
   for (int idx = threadIdx.x; idx < R * kHeadDim; idx += kAttnThreads) {
     const int r = idx / kHeadDim, d = idx % kHeadDim;
     const float v = part[0][r][d] + part[1][r][d] + part[2][r][d] + part[3][r][d];
-    float ls = lsum[0];
+    float ls = lsum[0], m = mx[0];
 #pragma unroll
-    for (int k = 1; k < R; ++k) ls = r == k ? lsum[k] : ls;
-    const float o = L > 0 ? v / ls : 0.0f;
-    a.o[(int64_t(b) * a.H + h0 + r) * kHeadDim + d] = __half_as_ushort(__float2half_rn(o));
+    for (int k = 1; k < R; ++k) {
+      ls = r == k ? lsum[k] : ls;
+      m = r == k ? mx[k] : m;
+    }
+    const int64_t bh = int64_t(b) * a.H + h0 + r;
+    if constexpr (SPLIT) {
+      const int64_t cbh = int64_t(blockIdx.z) * BH + bh;
+      a.ws[cbh * kHeadDim + d] = v;
+      if (d == 0) {
+        a.ws[int64_t(gridDim.z) * BH * kHeadDim + cbh] = t1 > t0 ? m : -INFINITY;
+        a.ws[int64_t(gridDim.z) * BH * (kHeadDim + 1) + cbh] = ls;
+      }
+    } else {
+      const float o = L > 0 ? v / ls : 0.0f;
+      a.o[bh * kHeadDim + d] = __half_as_ushort(__float2half_rn(o));
+    }
+  }
+}
+
+// Combines the nc chunk partials of every (sequence, head): with M the
+// largest chunk max, o = sum_c o_c e^(m_c - M) / sum_c l_c e^(m_c - M).
+// Empty chunks carry m = -inf and contribute nothing; a sequence with no
+// tokens gets zeros.  One block per (head, sequence): a thread per chunk
+// finds M and the weights, then 8 groups of 32 threads each sum every 8th
+// chunk's output, 4 dims a thread, so that the chunk loads are independent.
+constexpr int kCombineThreads = 256;
+constexpr int kMaxChunks = kMaxCacheLen / kAttnThreads;  // a chunk is at least one 256-token pass
+static_assert(kMaxChunks <= kCombineThreads, "one thread per chunk");
+
+__global__ __launch_bounds__(kCombineThreads) void kv4_attention_combine_kernel(const float* __restrict__ ws, int nc,
+                                                                               int64_t BH, int H,
+                                                                               unsigned short* __restrict__ o) {
+  __shared__ float wgt[kMaxChunks];
+  __shared__ float red[2][kCombineThreads / 64];
+  __shared__ float4 part[kCombineThreads / 32][kHeadDim / 4];
+  const int64_t bh = int64_t(blockIdx.y) * H + blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const float* wm = ws + int64_t(nc) * BH * kHeadDim;
+  const float* wl = wm + int64_t(nc) * BH;
+  const float m = t < nc ? wm[t * BH + bh] : -INFINITY;
+  const float l = t < nc ? wl[t * BH + bh] : 0.0f;
+  float M = wave_max(m);
+  if (lane == 0) red[0][wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+  const float e = t < nc && M > -INFINITY ? __expf(m - M) : 0.0f;  // m = -inf: 0
+  if (t < nc) wgt[t] = e;
+  float L = wave_sum(l * e);
+  if (lane == 0) red[1][wave] = L;
+  __syncthreads();
+  L = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  const int d4 = t & 31, cg = t >> 5;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 4
+  for (int c = cg; c < nc; c += kCombineThreads / 32) {
+    const float4 v = *reinterpret_cast<const float4*>(ws + (c * BH + bh) * kHeadDim + 4 * d4);
+    const float w = wgt[c];
+    acc.x = fmaf(v.x, w, acc.x);
+    acc.y = fmaf(v.y, w, acc.y);
+    acc.z = fmaf(v.z, w, acc.z);
+    acc.w = fmaf(v.w, w, acc.w);
+  }
+  part[cg][d4] = acc;
+  __syncthreads();
+  if (t < kHeadDim) {
+    const float* pf = reinterpret_cast<const float*>(&part[0][0]);
+    float v = 0.0f;
+#pragma unroll
+    for (int g = 0; g < kCombineThreads / 32; ++g) v += pf[g * kHeadDim + t];
+    o[bh * kHeadDim + t] = __half_as_ushort(__float2half_rn(L > 0.0f ? v / L : 0.0f));
   }
 }
 
@@ -394,25 +474,112 @@ extern "C" int qoq_kv4_quant(const void* x_fp16, int64_t n_rows, int32_t head_di
   return QOQ_OK;
 }
 
-extern "C" int qoq_kv4_decode_attention(const void* q_fp16, const uint8_t* k_codes, const void* k_scale_fp16,
-                                        const uint8_t* k_zero, const uint8_t* v_codes, const void* v_scale_fp16,
-                                        const uint8_t* v_zero, const int32_t* lengths, int32_t B, int32_t H,
-                                        int32_t Hkv, int32_t T_max, int32_t head_dim, float softmax_scale,
-                                        void* o_fp16, void* stream) {
-  clear_error();
+namespace {
+
+// Launch plan of the decode attention: R query heads per block; with
+// nc > 1 the tokens are cut into nc chunks of Tc whose partials are combined
+// afterwards.
+struct AttnPlan {
+  int R = 1, Tc = 0, nc = 1;
+};
+
+// Tokens are split only while (sequence, head group) workgroups alone number
+// fewer than kSplitBelowBlocks (one per CU).  A chunk is 1024 tokens, four
+// passes of the block's token loop, which amortizes the block's fixed work
+// (query load, cross-lane reductions, partial write); it is halved, down to
+// one pass, while there would be fewer than kSplitTargetBlocks workgroups
+// (two per CU: a lone 4-wave block per CU leaves each SIMD one wave and
+// nothing to hide its load latency behind).
+constexpr int64_t kSplitBelowBlocks = 256;
+constexpr int64_t kSplitTargetBlocks = 512;
+constexpr int kSplitChunkMax = 1024;
+constexpr int kSplitChunkMin = kAttnThreads;  // 16 tokens x kUnroll per wave, 4 waves
+static_assert(kSplitChunkMin == kAttnThreads / 64 * 16 * kUnroll, "one pass of the token loop");
+static_assert(kMaxHeadsPerBlock * kSplitChunkMax <= kMaxCacheLen, "chunk scores fit the LDS budget");
+
+int heads_per_block(int rep, int64_t tokens) {
+  for (int r = kMaxHeadsPerBlock; r > 1; r >>= 1)
+    if (rep % r == 0 && size_t(r) * size_t(tokens) * sizeof(float) <= kAttnScoreLds) return r;
+  return 1;
+}
+
+AttnPlan attn_plan(int B, int H, int Hkv, int T_max, bool allow_split) {
+  AttnPlan p;
+  const int rep = H / Hkv;
+  p.R = heads_per_block(rep, T_max);
+  if (!allow_split) return p;
+  const int Rs = heads_per_block(rep, kSplitChunkMax);
+  const int64_t blocks = int64_t(B) * H / Rs;
+  if (blocks >= kSplitBelowBlocks || T_max < 2 * kSplitChunkMin) return p;
+  int64_t Tc = kSplitChunkMax;
+  while (Tc > kSplitChunkMin && blocks * ((T_max + Tc - 1) / Tc) < kSplitTargetBlocks) Tc /= 2;
+  const int64_t nc = (T_max + Tc - 1) / Tc;
+  if (nc < 2) return p;
+  p.R = Rs;
+  p.Tc = int(Tc);
+  p.nc = int(nc);
+  return p;
+}
+
+size_t attn_workspace_bytes(const AttnPlan& p, int B, int H) {
+  return p.nc > 1 ? size_t(p.nc) * size_t(B) * size_t(H) * (kHeadDim + 2) * sizeof(float) : 0;
+}
+
+int check_attn_args(const char* fn, const void* q_fp16, const uint8_t* k_codes, const void* k_scale_fp16,
+                    const uint8_t* k_zero, const uint8_t* v_codes, const void* v_scale_fp16, const uint8_t* v_zero,
+                    const int32_t* lengths, int32_t B, int32_t H, int32_t Hkv, int32_t T_max, int32_t head_dim,
+                    float softmax_scale, void* o_fp16) {
   if (!q_fp16 || !k_codes || !k_scale_fp16 || !k_zero || !v_codes || !v_scale_fp16 || !v_zero || !lengths || !o_fp16)
-    return fail(QOQ_ERR_INVALID_ARG, "qoq_kv4_decode_attention: null pointer argument");
-  if (head_dim != kHeadDim)
-    return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "qoq_kv4_decode_attention: head_dim must be 128, got %d", head_dim);
+    return fail(QOQ_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (head_dim != kHeadDim) return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "%s: head_dim must be 128, got %d", fn, head_dim);
   if (B < 1 || H < 1 || Hkv < 1 || H % Hkv || B > 65535 || H > 65535)
-    return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "qoq_kv4_decode_attention: need B, H, Hkv >= 1 and H a multiple of Hkv");
+    return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "%s: need B, H, Hkv >= 1 and H a multiple of Hkv", fn);
   if (T_max < 1 || T_max > kMaxCacheLen)
-    return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "qoq_kv4_decode_attention: T_max must be in [1, %d]", kMaxCacheLen);
-  if (!std::isfinite(softmax_scale)) return fail(QOQ_ERR_INVALID_ARG, "qoq_kv4_decode_attention: scale not finite");
+    return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "%s: T_max must be in [1, %d]", fn, kMaxCacheLen);
+  if (!std::isfinite(softmax_scale)) return fail(QOQ_ERR_INVALID_ARG, "%s: scale not finite", fn);
   const auto al = [](const void* p, uintptr_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; };
   if (!al(q_fp16, 16) || !al(k_codes, 16) || !al(v_codes, 16) || !al(k_scale_fp16, 2) || !al(v_scale_fp16, 2) ||
       !al(lengths, 4) || !al(o_fp16, 2))
-    return fail(QOQ_ERR_ALIGNMENT, "qoq_kv4_decode_attention: q and codes need 16-byte alignment");
+    return fail(QOQ_ERR_ALIGNMENT, "%s: q and codes need 16-byte alignment", fn);
+  return QOQ_OK;
+}
+
+template <bool SPLIT>
+int launch_attention(const char* fn, const AttnArgs& a, const AttnPlan& p, int B, int64_t lds, hipStream_t stream) {
+  using Kernel = void (*)(AttnArgs);
+  const Kernel k = p.R == 4   ? kv4_decode_attention_kernel<4, SPLIT>
+                   : p.R == 2 ? kv4_decode_attention_kernel<2, SPLIT>
+                              : kv4_decode_attention_kernel<1, SPLIT>;
+  if (lds > 48 * 1024) {
+    const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, int(kAttnScoreLds));
+    if (attr != hipSuccess) return fail(QOQ_ERR_HIP, "%s: LDS attribute: %s", fn, hipGetErrorString(attr));
+  }
+  const dim3 grid(static_cast<unsigned>(a.H / p.R), static_cast<unsigned>(B), static_cast<unsigned>(p.nc));
+  hipLaunchKernelGGL(k, grid, dim3(kAttnThreads), size_t(lds), stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(QOQ_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return QOQ_OK;
+}
+
+int run_attention(const char* fn, bool allow_split, const void* q_fp16, const uint8_t* k_codes,
+                  const void* k_scale_fp16, const uint8_t* k_zero, const uint8_t* v_codes, const void* v_scale_fp16,
+                  const uint8_t* v_zero, const int32_t* lengths, int32_t B, int32_t H, int32_t Hkv, int32_t T_max,
+                  int32_t head_dim, float softmax_scale, void* o_fp16, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  clear_error();
+  const int st = check_attn_args(fn, q_fp16, k_codes, k_scale_fp16, k_zero, v_codes, v_scale_fp16, v_zero, lengths,
+                                 B, H, Hkv, T_max, head_dim, softmax_scale, o_fp16);
+  if (st != QOQ_OK) return st;
+  const AttnPlan p = attn_plan(B, H, Hkv, T_max, allow_split);
+  const size_t need = attn_workspace_bytes(p, B, H);
+  if (need) {
+    if (!workspace || workspace_bytes < need)
+      return fail(QOQ_ERR_INVALID_ARG, "%s: workspace of %zu bytes required (got %zu); see the workspace-size query", fn, need,
+                  workspace ? workspace_bytes : size_t(0));
+    if (reinterpret_cast<uintptr_t>(workspace) % 16)
+      return fail(QOQ_ERR_ALIGNMENT, "%s: workspace needs 16-byte alignment", fn);
+  }
   AttnArgs a;
   a.q = static_cast<const unsigned short*>(q_fp16);
   a.kc = k_codes;
@@ -427,32 +594,44 @@ extern "C" int qoq_kv4_decode_attention(const void* q_fp16, const uint8_t* k_cod
   a.Hkv = Hkv;
   a.T = T_max;
   a.scale = softmax_scale;
-  // heads per block: the largest of 4, 2, 1 that divides the group and
-  // whose scores fit the block's LDS budget
-  const int rep = H / Hkv;
-  int R = 1;
-  for (int r = kMaxHeadsPerBlock; r > 1; r >>= 1)
-    if (rep % r == 0 && size_t(r) * size_t(T_max) * sizeof(float) <= kAttnScoreLds) {
-      R = r;
-      break;
-    }
-  const size_t lds = size_t(R) * size_t(T_max) * sizeof(float);
-  const void* fn = R == 4 ? reinterpret_cast<const void*>(kv4_decode_attention_kernel<4>)
-                   : R == 2 ? reinterpret_cast<const void*>(kv4_decode_attention_kernel<2>)
-                            : reinterpret_cast<const void*>(kv4_decode_attention_kernel<1>);
-  if (lds > 48 * 1024) {
-    const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(kAttnScoreLds));
-    if (attr != hipSuccess)
-      return fail(QOQ_ERR_HIP, "qoq_kv4_decode_attention: LDS attribute: %s", hipGetErrorString(attr));
-  }
-  const dim3 grid(static_cast<unsigned>(H / R), static_cast<unsigned>(B));
-  if (R == 4)
-    hipLaunchKernelGGL(kv4_decode_attention_kernel<4>, grid, dim3(kAttnThreads), lds, static_cast<hipStream_t>(stream), a);
-  else if (R == 2)
-    hipLaunchKernelGGL(kv4_decode_attention_kernel<2>, grid, dim3(kAttnThreads), lds, static_cast<hipStream_t>(stream), a);
-  else
-    hipLaunchKernelGGL(kv4_decode_attention_kernel<1>, grid, dim3(kAttnThreads), lds, static_cast<hipStream_t>(stream), a);
+  a.Tc = p.Tc;
+  a.ws = static_cast<float*>(workspace);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.nc == 1) return launch_attention<false>(fn, a, p, B, int64_t(p.R) * T_max * int64_t(sizeof(float)), s);
+  const int st2 = launch_attention<true>(fn, a, p, B, int64_t(p.R) * p.Tc * int64_t(sizeof(float)), s);
+  if (st2 != QOQ_OK) return st2;
+  hipLaunchKernelGGL(kv4_attention_combine_kernel, dim3(static_cast<unsigned>(H), static_cast<unsigned>(B)),
+                     dim3(kCombineThreads), 0, s, static_cast<const float*>(workspace), p.nc, int64_t(B) * H, int(H),
+                     static_cast<unsigned short*>(o_fp16));
   const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(QOQ_ERR_HIP, "qoq_kv4_decode_attention: launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(QOQ_ERR_HIP, "%s: combine launch failed: %s", fn, hipGetErrorString(e));
   return QOQ_OK;
+}
+
+}  // namespace
+
+extern "C" int qoq_kv4_decode_attention(const void* q_fp16, const uint8_t* k_codes, const void* k_scale_fp16,
+                                        const uint8_t* k_zero, const uint8_t* v_codes, const void* v_scale_fp16,
+                                        const uint8_t* v_zero, const int32_t* lengths, int32_t B, int32_t H,
+                                        int32_t Hkv, int32_t T_max, int32_t head_dim, float softmax_scale,
+                                        void* o_fp16, void* stream) {
+  return run_attention("qoq_kv4_decode_attention", false, q_fp16, k_codes, k_scale_fp16, k_zero, v_codes,
+                       v_scale_fp16, v_zero, lengths, B, H, Hkv, T_max, head_dim, softmax_scale, o_fp16, nullptr, 0,
+                       stream);
+}
+
+extern "C" size_t qoq_kv4_decode_attention_workspace_size(int32_t B, int32_t H, int32_t Hkv, int32_t T_max) {
+  if (B < 1 || H < 1 || Hkv < 1 || H % Hkv || B > 65535 || H > 65535 || T_max < 1 || T_max > kMaxCacheLen) return 0;
+  return attn_workspace_bytes(attn_plan(B, H, Hkv, T_max, true), B, H);
+}
+
+extern "C" int qoq_kv4_decode_attention_split(const void* q_fp16, const uint8_t* k_codes, const void* k_scale_fp16,
+                                              const uint8_t* k_zero, const uint8_t* v_codes,
+                                              const void* v_scale_fp16, const uint8_t* v_zero,
+                                              const int32_t* lengths, int32_t B, int32_t H, int32_t Hkv,
+                                              int32_t T_max, int32_t head_dim, float softmax_scale, void* o_fp16,
+                                              void* workspace, size_t workspace_bytes, void* stream) {
+  return run_attention("qoq_kv4_decode_attention_split", true, q_fp16, k_codes, k_scale_fp16, k_zero, v_codes,
+                       v_scale_fp16, v_zero, lengths, B, H, Hkv, T_max, head_dim, softmax_scale, o_fp16, workspace,
+                       workspace_bytes, stream);
 }
