@@ -271,12 +271,16 @@ QOQ_API int qoq_kv4_quant(const void* x_fp16, int64_t n_rows, int32_t head_dim, 
  * [0, T_max]) cached tokens:
  *   k_t = (kc_t - kz_t) * ks_t, v_t = (vc_t - vz_t) * vs_t,
  *   a = softmax_t(softmax_scale * <q[b,h], k_t>),  o[b,h] = fp16(sum_t a_t v_t),
- * in FP32 (scores as ks_t * (<q', kc_t> - kz_t * sum(q')) with
- * q' = softmax_scale * q); L = 0 gives o = 0.  q_fp16: device [B][H][128];
- * the k and v arrays: cache rows [B][Hkv][T_max]; lengths: device int32 [B];
- * o_fp16: device [B][H][128].  1 <= T_max <= 32768; q and the code arrays
- * 16-byte aligned.  Accuracy: see the parity tolerance in the design notes
- * (FP32 arithmetic, exp to a few FP32 ulp).
+ * with scores ks_t * <q', kc_t - kz_t>, q' = softmax_scale * q: q' is split
+ * into three INT8 pieces (q' ~ S0 b0 + S1 b1 + S2 b2, S0 = max|q'| / 127,
+ * S_{p+1} = S_p / 254, within about 2^-23 max|q'|), whose dot products with
+ * the codes are exact INT32 on the matrix cores, combined in FP32; the
+ * softmax and the weighted sum of values are FP32.  L = 0 gives o = 0.
+ * q_fp16: device [B][H][128]; the k and v arrays: cache rows
+ * [B][Hkv][T_max]; lengths: device int32 [B]; o_fp16: device [B][H][128].
+ * 1 <= T_max <= 32768; q and the code arrays 16-byte aligned.  Accuracy:
+ * each output within one FP16 ulp plus 2^-12 max_t |v_t| of the exact
+ * attention over the dequantized cache.
  */
 QOQ_API int qoq_kv4_decode_attention(const void* q_fp16, const uint8_t* k_codes, const void* k_scale_fp16,
                              const uint8_t* k_zero, const uint8_t* v_codes, const void* v_scale_fp16,

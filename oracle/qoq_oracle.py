@@ -17,15 +17,15 @@ weights (output x input channels), Y[M,N] = X W^T.  The [PL §2] summary calls
 the token count N; this file uses M for tokens and N for output channels.
 
 Precision.  The pages fix FP16 for the per-channel weight scale
-([PL §4, progressive group quantization]: "channel-wise FP16 scales").  Every
+([PL §4, progressive group quantization]).  Every
 step that decides an integer code (activation and weight quantization) is
 taken in IEEE FP32 with round-half-to-even, the precision the GPU kernel uses;
 the epilogue is evaluated exactly in FP64 and rounded once to FP16.
 
-Readings where the pages are silent or garbled are listed in the design notes
-shipped with the repository; the ones that shape arithmetic here are:
-  * group scale stored as an 8-bit integer in [1, 16] (the summary says "INT4
-    scales", which cannot hold 16), rounded to nearest;
+Readings taken where the pages are silent or garbled, those that shape the
+arithmetic here:
+  * group scale stored as an 8-bit integer in [1, 16] (one page calls the
+    group scales 4-bit, which cannot hold 16), rounded to nearest;
   * round half to even everywhere;
   * level-1 code = round(q8 / s1) + z, rounding before adding the zero;
   * plain min/max group range (0 not forced in), zero clamped to [0, 15];

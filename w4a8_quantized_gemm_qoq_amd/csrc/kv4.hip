@@ -42,6 +42,7 @@ constexpr int kHeadDim = 128;
 constexpr int kRowBytes = kHeadDim / 2;
 constexpr int kAttnThreads = 256;
 constexpr int kMaxCacheLen = 32768;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // DPP lane permutations (VALU operations, no trip through the LDS crossbar):
 // quad_perm [1,0,3,2] and [2,3,0,1] pair lanes as xor 1 and xor 2 do, and
@@ -136,29 +137,9 @@ __device__ __forceinline__ float ubyte(unsigned v) {
   return static_cast<float>((v >> (8 * k)) & 0xffu);
 }
 
-// The R query heads of a block share every conversion of a code to float:
-// one v_cvt_f32_ubyte feeds R FMAs.  Codes of one 16-byte load: dword w holds
-// dims 8w..8w+7 (byte b: dims 8w+2b (low nibble) and 8w+2b+1 (high)).
-//
-// out[r] = <q[r][0..32), codes of 32 dims>
-template <int R>
-__device__ __forceinline__ void dot32(const float (&q)[R][32], uint4 c, float (&out)[R]) {
-  const unsigned w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-  for (int r = 0; r < R; ++r) out[r] = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const unsigned lo = w[i] & 0x0f0f0f0fu, hi = (w[i] >> 4) & 0x0f0f0f0fu;
-    const float x[8] = {ubyte<0>(lo), ubyte<0>(hi), ubyte<1>(lo), ubyte<1>(hi),
-                        ubyte<2>(lo), ubyte<2>(hi), ubyte<3>(lo), ubyte<3>(hi)};
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int r = 0; r < R; ++r) out[r] = fmaf(q[r][8 * i + e], x[e], out[r]);
-  }
-}
-
-// acc[r][d] += w[r] * code[d] over the 32 dims of one 16-byte load.
+// acc[r][d] += w[r] * code[d] over the 32 dims of one 16-byte load (dword
+// w holds dims 8w..8w+7; byte b: dims 8w+2b (low nibble) and 8w+2b+1 (high)).
+// The R query heads of a block share each conversion of a code to float.
 template <int R>
 __device__ __forceinline__ void axpy32(float (&acc)[R][32], const float (&w)[R], uint4 c) {
   const unsigned v[4] = {c.x, c.y, c.z, c.w};
@@ -235,62 +216,138 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
   const int t1 = SPLIT ? min(L, t0 + a.Tc) : L;
   const int Ts = SPLIT ? a.Tc : a.T;
 
-  // q' = scale * q for this lane's 32 dims of each head, and their sums
-  float q[R][32], qsum[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const uint4* qv = reinterpret_cast<const uint4*>(a.q + (int64_t(b) * a.H + h0 + r) * kHeadDim + 32 * p);
-    qsum[r] = 0.0f;
+  // Pass 1, the scores, on the matrix cores in exact integer arithmetic.
+  // Each query row q' = scale * q is split into three signed-byte pieces,
+  //   q' ~= S0 b0 + S1 b1 + S2 b2,  S0 = max|q'| / 127,  S1 = S0 / 254,  S2 = S1 / 254,
+  // each piece the rounded remainder left by the ones before (the sum is
+  // within about 2^-23 max|q'| of q'), so that
+  //   <q', c_t - z_t> = sum_p S_p (<b_p, c_t> - z_t sum(b_p))
+  // takes only exact INT8 products.  One v_mfma_i32_16x16x64_i8 multiplies
+  // 16 rows (M: 4 heads x (3 pieces + an empty row)) by 16 tokens (N); the
+  // 128 dims are two K steps.  Lane (l16 = lane % 16, jq = lane / 16) holds,
+  // for K step h, the 16 K values of quarter jq: dims 32 jq + 16 h + o(k),
+  // o = 0,2,4,6, 1,3,5,7, 8,10,12,14, 9,11,13,15 -- the order in which a
+  // 16-byte load of codes (dims 32 jq .. 32 jq + 31) comes out of the
+  // nibble split below.  The A operand (row l16 = 4 r + p) is piece p of
+  // head r; the B operand (column l16) is a token's codes; the result lane
+  // (token l16, jq) holds the three piece products of head jq in elements
+  // 0..2.
+  const int l16 = lane & 15, jq = lane >> 4;
+  i32x4 qa[2];
+  float spc;  // step S_p of this lane's row
+  int bsum;   // sum of its piece over the 128 dims
+  {
+    const int r = l16 >> 2, pc = l16 & 3;
+    const bool on = r < R && pc < 3;
+    const uint4* qv = reinterpret_cast<const uint4*>(a.q + (int64_t(b) * a.H + h0 + min(r, R - 1)) * kHeadDim + 32 * jq);
+    float x[32];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint4 u = qv[i];
       const unsigned w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        q[r][8 * i + 2 * j] = a.scale * __half2float(__ushort_as_half(static_cast<unsigned short>(w[j] & 0xffffu)));
-        q[r][8 * i + 2 * j + 1] = a.scale * __half2float(__ushort_as_half(static_cast<unsigned short>(w[j] >> 16)));
+      for (int e = 0; e < 4; ++e) {
+        x[8 * i + 2 * e] = a.scale * half_lo(w[e]);
+        x[8 * i + 2 * e + 1] = a.scale * half_hi(w[e]);
       }
     }
+    float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) qsum[r] += q[r][i];
+    for (int d = 0; d < 32; ++d) amax = fmaxf(amax, fabsf(x[d]));
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    const float s0 = amax / 127.0f, s1 = s0 / 254.0f, s2 = s1 / 254.0f;
+    const float i0 = amax > 0.0f ? 127.0f / amax : 0.0f, i1 = 254.0f * i0, i2 = 254.0f * i1;
+    const auto clamp127 = [](float v) { return fminf(127.0f, fmaxf(-127.0f, v)); };
+    int bp[32];
+    int sum = 0;
+#pragma unroll
+    for (int d = 0; d < 32; ++d) {
+      const float b0 = clamp127(rintf(x[d] * i0));
+      const float r1 = fmaf(-b0, s0, x[d]);
+      const float b1 = clamp127(rintf(r1 * i1));
+      const float r2 = fmaf(-b1, s1, r1);
+      const float b2 = clamp127(rintf(r2 * i2));
+      bp[d] = on ? int(pc == 0 ? b0 : pc == 1 ? b1 : b2) : 0;
+      sum += bp[d];
+    }
+    sum += __shfl_xor(sum, 16, 64);
+    sum += __shfl_xor(sum, 32, 64);
+    bsum = sum;
+    spc = pc == 0 ? s0 : pc == 1 ? s1 : s2;
+    // byte 4 w + e of K step h: dim 16 h + 8 (w / 2) + 2 e + w % 2
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        unsigned v = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v |= (unsigned(bp[16 * h + 8 * (w >> 1) + 2 * e + (w & 1)]) & 0xffu) << (8 * e);
+        qa[h][w] = int(v);
+      }
+  }
+  // steps and piece sums of head jq (rows 4 jq + p), for the lanes that
+  // combine its scores
+  float sp[3];
+  int bs[3];
+#pragma unroll
+  for (int pc = 0; pc < 3; ++pc) {
+    sp[pc] = __shfl(spc, 4 * jq + pc, 64);
+    bs[pc] = __shfl(bsum, 4 * jq + pc, 64);
   }
 
-  // pass 1: scores
-  float mx[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) mx[r] = -INFINITY;
+  // Both passes load the next round's cache rows before working on the
+  // current one, so each wave has a round of loads in flight while it computes.
+  constexpr int kStride = kAttnThreads / 4 * kUnroll;  // tokens per block round
+  float mown = -INFINITY;  // largest score of head jq seen by this lane
   const uint4* kc = reinterpret_cast<const uint4*>(a.kc + row0 * kRowBytes);
-  for (int base = t0 + wave * 16 * kUnroll; base < t1; base += kAttnThreads / 4 * kUnroll) {
+  uint4 kn[kUnroll];
+  unsigned short sn[kUnroll];
+  int zn[kUnroll];
+  auto kload = [&](int base) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int t = min(base + 16 * u + l16, t1 - 1);  // past t1: a valid token, result dropped
+      kn[u] = kc[int64_t(t) * 4 + jq];
+      sn[u] = a.ks[row0 + t];
+      zn[u] = a.kz[row0 + t];
+    }
+  };
+  if (t0 + wave * 16 * kUnroll < t1) kload(t0 + wave * 16 * kUnroll);
+  for (int base = t0 + wave * 16 * kUnroll; base < t1; base += kStride) {
     uint4 c[kUnroll];
     float s[kUnroll];
     int z[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int t = min(base + 16 * u + tq, t1 - 1);  // past t1: a valid token, result dropped
-      c[u] = kc[int64_t(t) * 4 + p];
-      s[u] = __half2float(__ushort_as_half(a.ks[row0 + t]));
-      z[u] = a.kz[row0 + t];
+      c[u] = kn[u];
+      s[u] = __half2float(__ushort_as_half(sn[u]));
+      z[u] = zn[u];
     }
+    if (base + kStride < t1) kload(base + kStride);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      float v[R];
-      dot32<R>(q, c[u], v);
-      const int t = base + 16 * u + tq;
+      const unsigned w[4] = {c[u].x, c[u].y, c[u].z, c[u].w};
+      i32x4 d = {0, 0, 0, 0};
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        v[r] = s[u] * (v[r] - float(z[u]) * qsum[r]);
-        v[r] += dppf<kDppXor1>(v[r]);
-        v[r] += dppf<kDppXor2>(v[r]);
-        if (t < t1) {
-          mx[r] = fmaxf(mx[r], v[r]);
-          if (p == 0) sc[r * Ts + (t - t0)] = v[r];
-        }
+      for (int h = 0; h < 2; ++h) {
+        const i32x4 cb = {int(w[2 * h] & 0x0f0f0f0fu), int((w[2 * h] >> 4) & 0x0f0f0f0fu),
+                          int(w[2 * h + 1] & 0x0f0f0f0fu), int((w[2 * h + 1] >> 4) & 0x0f0f0f0fu)};
+        d = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[h], cb, d, 0, 0, 0);
+      }
+      const int t = base + 16 * u + l16;
+      const float v = s[u] * (sp[0] * float(d[0] - z[u] * bs[0]) + sp[1] * float(d[1] - z[u] * bs[1]) +
+                              sp[2] * float(d[2] - z[u] * bs[2]));
+      if (jq < R && t < t1) {
+        mown = fmaxf(mown, v);
+        sc[jq * Ts + (t - t0)] = v;
       }
     }
   }
+  float mx[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    mx[r] = wave_max(mx[r]);
+    mx[r] = wave_max(jq == r ? mown : -INFINITY);
     if (lane == 0) red[r][wave] = mx[r];
   }
   __syncthreads();
@@ -325,7 +382,20 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
     for (int i = 0; i < 32; ++i) acc[r][i] = 0.0f;
   }
   const uint4* vc = reinterpret_cast<const uint4*>(a.vc + row0 * kRowBytes);
-  for (int base = t0 + wave * 16 * kUnroll; base < t1; base += kAttnThreads / 4 * kUnroll) {
+  uint4 vn[kUnroll];
+  unsigned short vsn[kUnroll];
+  int vzn[kUnroll];
+  auto vload = [&](int base) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int tc = min(base + 16 * u + tq, t1 - 1);
+      vn[u] = vc[int64_t(tc) * 4 + p];
+      vsn[u] = a.vs[row0 + tc];
+      vzn[u] = a.vz[row0 + tc];
+    }
+  };
+  if (t0 + wave * 16 * kUnroll < t1) vload(t0 + wave * 16 * kUnroll);
+  for (int base = t0 + wave * 16 * kUnroll; base < t1; base += kStride) {
     uint4 c[kUnroll];
     float w[kUnroll][R];
     int z[kUnroll];
@@ -333,12 +403,13 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
     for (int u = 0; u < kUnroll; ++u) {
       const int t = base + 16 * u + tq;
       const int tc = min(t, t1 - 1);
-      c[u] = vc[int64_t(tc) * 4 + p];
-      const float vs = __half2float(__ushort_as_half(a.vs[row0 + tc]));
+      c[u] = vn[u];
+      const float vs = __half2float(__ushort_as_half(vsn[u]));
 #pragma unroll
       for (int r = 0; r < R; ++r) w[u][r] = t < t1 ? sc[r * Ts + (tc - t0)] * vs : 0.0f;
-      z[u] = a.vz[row0 + tc];
+      z[u] = vzn[u];
     }
+    if (base + kStride < t1) vload(base + kStride);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       axpy32<R>(acc, w[u], c[u]);
