@@ -113,7 +113,7 @@ def check_attention(Q, kk, vv, lengths, split=False):
     (3, 8, 2, 200, [200, 1, 0], 1.0),      # GQA, a single token, an empty sequence
     (1, 2, 1, 1000, [999], 4.0),           # sharp softmax, T not a multiple of 64
     (4, 4, 4, 256, [256, 255, 129, 64], 1.0),
-    (4, 16, 2, 96, [96, 50, 1, 33], 1.0),  # 8 heads per kv head: two 4-head blocks each, XCD-paired
+    (4, 16, 2, 96, [96, 50, 1, 33], 1.0),  # 8 heads per kv head: four 2-head blocks each, XCD-grouped
     (1, 6, 2, 128, [128], 1.0),            # 3 heads per kv head: one head per block
     (1, 8, 2, 9000, [9000], 1.0),          # 4 heads per kv head, but 4 score rows exceed LDS: 2 per block
     (1, 4, 1, 20000, [19999], 1.0),        # ... and one per block
@@ -146,14 +146,15 @@ def test_kv4_attention_bench_shape(H, Hkv):
 # Token-split attention: chunks of the cache over more workgroups, their
 # softmax partials combined afterwards.  Same oracle, same tolerance.
 @pytest.mark.parametrize("B,H,Hkv,T,lengths,peak", [
-    (1, 32, 8, 4096, [4096], 1.0),             # 16 chunks of 256 tokens, four heads a workgroup
+    (1, 32, 8, 4096, [4096], 1.0),             # 16 chunks of 256 tokens, two heads a workgroup
     (2, 32, 32, 3000, [3000, 1], 1.0),         # MHA, 12 chunks of 256; one token: 11 empty chunks
     (4, 32, 32, 4096, [4096, 3000, 1025, 0], 1.0),  # 4 chunks of 1024; 1025: a one-token chunk
     (3, 8, 2, 1000, [1000, 0, 513], 1.0),      # empty sequence; 513 = two chunks and one token
     (1, 2, 1, 1000, [999], 4.0),               # sharp softmax across chunks
     (1, 6, 2, 2000, [1777], 1.0),              # 3 heads per kv head: one a workgroup
     (1, 4, 1, 32768, [32768], 1.0),            # the longest cache: 128 chunks
-    (1, 32, 8, 32768, [30001], 1.0),           # 512-token chunks; the last six partial or empty
+    (1, 32, 8, 32768, [30001], 1.0),           # 1024-token chunks; the last three partial or empty
+    (4, 64, 8, 8192, [8192, 5000, 8191, 1], 1.0),  # four heads a workgroup, 1024-token chunks
     (2, 8, 1, 20000, [20000, 8191], 1.0),      # 8-head groups, chunk ends inside a sequence
 ])
 def test_kv4_attention_split_matches_oracle(B, H, Hkv, T, lengths, peak):

@@ -357,7 +357,9 @@ def test_kv4_attention_split_plan():
     + max + sum) FP32.  Nothing is split once (sequence, head group)
     workgroups alone reach 256, or below 512 cached tokens; otherwise chunks
     are 1024 tokens, halved (down to 256) while fewer than 512 workgroups
-    would result."""
+    would result.  A GQA group is taken 4 or 2 heads a workgroup: of the plans
+    that reach 512 workgroups the one with the longest chunks, else the one
+    with the most workgroups."""
     ws = q.load_library().qoq_kv4_decode_attention_workspace_size
 
     def chunks(B, H, Hkv, T):
@@ -365,10 +367,12 @@ def test_kv4_attention_split_plan():
         assert n % (B * H * 130 * 4) == 0
         return n // (B * H * 130 * 4)
 
-    # 1 x 32 heads over 8 kv heads: 8 four-head workgroups; 256-token chunks
-    # still give only 128 workgroups
-    assert chunks(1, 32, 8, 4096) == 16
-    assert chunks(1, 32, 8, 32768) == 64       # 512-token chunks: 512 workgroups
+    # 1 x 32 heads over 8 kv heads: 16 two-head workgroups; 256-token chunks
+    # still give only 256 workgroups (128 with four heads)
+    assert chunks(1, 32, 8, 32768 // 8) == 16
+    # 512 workgroups either way: four heads with 512-token chunks, two heads
+    # with 1024-token chunks (longer, chosen)
+    assert chunks(1, 32, 8, 32768) == 32
     # MHA, 2 x 32 one-head workgroups: 1024 -> 192, 512 -> 384, 256 -> 768
     assert chunks(2, 32, 32, 3000) == 12
     assert chunks(4, 32, 32, 4096) == 4        # 128 workgroups x 4 chunks of 1024
@@ -377,7 +381,8 @@ def test_kv4_attention_split_plan():
     assert chunks(1, 4, 1, 512) == 2
     assert chunks(64, 32, 8, 1024) == 0        # 512 workgroups already
     assert chunks(32, 32, 8, 1024) == 0        # 256: one per CU
-    assert chunks(8, 32, 1, 4096) == 8         # 8 x 8 four-head workgroups x 8 chunks of 512
+    assert chunks(8, 32, 1, 4096) == 4         # 8 x 16 two-head workgroups x 4 chunks of 1024
+    assert chunks(4, 64, 8, 8192) == 8         # 64 four-head workgroups x 8 chunks of 1024
     assert chunks(1, 6, 2, 2000) == 8          # 3 heads per kv head: one a workgroup
     assert ws(2, 4, 3, 4096) == 0              # invalid shapes: 0
     assert ws(1, 4, 1, 40000) == 0

@@ -170,9 +170,10 @@ struct AttnArgs {
 
 // Tokens in flight per wave and pass: U loads of 16 tokens each.
 constexpr int kUnroll = 4;
-// Query heads per block, at most: the heads of one kv group share the
-// block's cache reads and code conversions; their scores sit side by side
-// in LDS ([R][T_max] floats, at most kAttnScoreLds bytes).
+// Query heads per block, at most.  The heads of one kv group in a block
+// share its cache reads and code conversions; their scores sit side by side
+// in LDS ([R][rows] floats, at most kAttnScoreLds bytes).  The launch plan
+// picks 4 or 2, or 1 when neither divides the group or fits.
 constexpr int kMaxHeadsPerBlock = 4;
 constexpr size_t kAttnScoreLds = size_t(kMaxCacheLen) * sizeof(float);
 
@@ -568,28 +569,49 @@ constexpr int kSplitChunkMin = kAttnThreads;  // 16 tokens x kUnroll per wave, 4
 static_assert(kSplitChunkMin == kAttnThreads / 64 * 16 * kUnroll, "one pass of the token loop");
 static_assert(kMaxHeadsPerBlock * kSplitChunkMax <= kMaxCacheLen, "chunk scores fit the LDS budget");
 
-int heads_per_block(int rep, int64_t tokens) {
-  for (int r = kMaxHeadsPerBlock; r > 1; r >>= 1)
-    if (rep % r == 0 && size_t(r) * size_t(tokens) * sizeof(float) <= kAttnScoreLds) return r;
-  return 1;
-}
-
-AttnPlan attn_plan(int B, int H, int Hkv, int T_max, bool allow_split) {
+// Chunks for R heads per block (nc = 1: the whole cache in one block).
+AttnPlan plan_with(int B, int H, int T_max, int R, bool allow_split) {
   AttnPlan p;
-  const int rep = H / Hkv;
-  p.R = heads_per_block(rep, T_max);
-  if (!allow_split) return p;
-  const int Rs = heads_per_block(rep, kSplitChunkMax);
-  const int64_t blocks = int64_t(B) * H / Rs;
-  if (blocks >= kSplitBelowBlocks || T_max < 2 * kSplitChunkMin) return p;
+  p.R = R;
+  const int64_t blocks = int64_t(B) * H / R;
+  if (!allow_split || blocks >= kSplitBelowBlocks || T_max < 2 * kSplitChunkMin) return p;
   int64_t Tc = kSplitChunkMax;
   while (Tc > kSplitChunkMin && blocks * ((T_max + Tc - 1) / Tc) < kSplitTargetBlocks) Tc /= 2;
   const int64_t nc = (T_max + Tc - 1) / Tc;
   if (nc < 2) return p;
-  p.R = Rs;
   p.Tc = int(Tc);
   p.nc = int(nc);
   return p;
+}
+
+// Heads per block: 4 or 2 of a kv group (1 only when neither divides the
+// group or fits the LDS budget).  More heads per block share each code's
+// conversion among more FMAs, fewer heads give more blocks: among the plans
+// that reach kSplitTargetBlocks blocks the one with the longest chunks wins
+// (then the most heads); if none does, the one with the most blocks.
+AttnPlan attn_plan(int B, int H, int Hkv, int T_max, bool allow_split) {
+  const int rep = H / Hkv;
+  AttnPlan best;
+  bool have = false;
+  int64_t best_blocks = 0, best_tc = 0;
+  for (int r = kMaxHeadsPerBlock; r >= 1; r >>= 1) {
+    if (rep % r) continue;
+    if (r == 1 && have) break;
+    const AttnPlan p = plan_with(B, H, T_max, r, allow_split);
+    const int64_t rows = p.nc > 1 ? p.Tc : T_max;  // score row length in LDS
+    if (size_t(r) * size_t(rows) * sizeof(float) > kAttnScoreLds) continue;
+    const int64_t blocks = int64_t(B) * H / r * p.nc;
+    const int64_t tc = p.nc > 1 ? p.Tc : int64_t(1) << 40;
+    const bool full = blocks >= kSplitTargetBlocks, best_full = best_blocks >= kSplitTargetBlocks;
+    const bool better = !have || (full != best_full ? full : full ? tc > best_tc : blocks > best_blocks);
+    if (better) {
+      best = p;
+      best_blocks = blocks;
+      best_tc = tc;
+      have = true;
+    }
+  }
+  return best;
 }
 
 size_t attn_workspace_bytes(const AttnPlan& p, int B, int H) {
