@@ -124,6 +124,24 @@ def test_kv4_attention_matches_oracle(B, H, Hkv, T, lengths, peak):
     check_attention(Q, kk, vv, lengths)
 
 
+@pytest.mark.parametrize("split", [False, True])
+def test_kv4_attention_query_edge_cases(split):
+    """Queries that stress the three-piece INT8 split of the scaled query: a
+    zero head (all pieces zero: uniform weights), one FP16-max entry, FP16
+    subnormals only, all dims equal, and alternating signs at the FP16 max."""
+    B, H, Hkv, T = 1, 8, 2, 1500
+    kk, vv = make_cache(B, Hkv, T, seed=77)
+    Q = np.random.default_rng(77).standard_normal((B, H, 128)).astype(np.float16)
+    Q[0, 0] = 0
+    Q[0, 1] = 0
+    Q[0, 1, 17] = 65504
+    Q[0, 2] = np.float16(6e-8) * np.sign(np.random.default_rng(1).standard_normal(128)).astype(np.float16)
+    Q[0, 3] = np.float16(0.3)
+    Q[0, 4, ::2] = 65504
+    Q[0, 4, 1::2] = -65504
+    check_attention(Q, kk, vv, [1499], split=split)
+
+
 def test_kv4_attention_lengths_clamped_to_cache():
     kk, vv = make_cache(2, 2, 32, seed=3)
     Q = np.random.default_rng(0).standard_normal((2, 2, 128)).astype(np.float16)
