@@ -145,7 +145,11 @@ __device__ __forceinline__ void axpy32(float (&acc)[R][32], const float (&w)[R],
   const unsigned v[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const unsigned lo = v[i] & 0x0f0f0f0fu, hi = (v[i] >> 4) & 0x0f0f0f0fu;
+    unsigned lo = v[i] & 0x0f0f0f0fu, hi = (v[i] >> 4) & 0x0f0f0f0fu;
+    // Opaque to the optimizer, so that it cannot fold the masks into a
+    // 4-bit field extract per code: each byte then converts with one
+    // v_cvt_f32_ubyte{0..3}.
+    asm volatile("" : "+v"(lo), "+v"(hi));
     const float x[8] = {ubyte<0>(lo), ubyte<0>(hi), ubyte<1>(lo), ubyte<1>(hi),
                         ubyte<2>(lo), ubyte<2>(hi), ubyte<3>(lo), ubyte<3>(hi)};
 #pragma unroll
@@ -289,19 +293,22 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
   }
   // steps and piece sums of head jq (rows 4 jq + p), for the lanes that
   // combine its scores
-  float sp[3];
-  int bs[3];
+  float sp[3], bs[3];
 #pragma unroll
   for (int pc = 0; pc < 3; ++pc) {
     sp[pc] = __shfl(spc, 4 * jq + pc, 64);
-    bs[pc] = __shfl(bsum, 4 * jq + pc, 64);
+    bs[pc] = float(__shfl(bsum, 4 * jq + pc, 64));
   }
 
   // Both passes load the next round's cache rows before working on the
   // current one, so each wave has a round of loads in flight while it computes.
   constexpr int kStride = kAttnThreads / 4 * kUnroll;  // tokens per block round
+  const int first = t0 + wave * 16 * kUnroll;          // this wave's first token
   float mown = -INFINITY;  // largest score of head jq seen by this lane
+  // this kv head's rows: block-uniform bases, 32-bit token offsets
   const uint4* kc = reinterpret_cast<const uint4*>(a.kc + row0 * kRowBytes);
+  const unsigned short* ksb = a.ks + row0;
+  const uint8_t* kzb = a.kz + row0;
   uint4 kn[kUnroll];
   unsigned short sn[kUnroll];
   int zn[kUnroll];
@@ -309,13 +316,13 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int t = min(base + 16 * u + l16, t1 - 1);  // past t1: a valid token, result dropped
-      kn[u] = kc[int64_t(t) * 4 + jq];
-      sn[u] = a.ks[row0 + t];
-      zn[u] = a.kz[row0 + t];
+      kn[u] = kc[unsigned(t * 4 + jq)];
+      sn[u] = ksb[unsigned(t)];
+      zn[u] = kzb[unsigned(t)];
     }
   };
-  if (t0 + wave * 16 * kUnroll < t1) kload(t0 + wave * 16 * kUnroll);
-  for (int base = t0 + wave * 16 * kUnroll; base < t1; base += kStride) {
+  if (first < t1) kload(first);
+  for (int base = first; base < t1; base += kStride) {
     uint4 c[kUnroll];
     float s[kUnroll];
     int z[kUnroll];
@@ -337,8 +344,11 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
         d = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[h], cb, d, 0, 0, 0);
       }
       const int t = base + 16 * u + l16;
-      const float v = s[u] * (sp[0] * float(d[0] - z[u] * bs[0]) + sp[1] * float(d[1] - z[u] * bs[1]) +
-                              sp[2] * float(d[2] - z[u] * bs[2]));
+      // <b_p, c_t> - z_t sum(b_p): integers below 2^24 in magnitude, so the
+      // FMA is exact
+      const float zf = float(z[u]);
+      const float v = s[u] * (sp[0] * fmaf(-zf, bs[0], float(d[0])) + sp[1] * fmaf(-zf, bs[1], float(d[1])) +
+                              sp[2] * fmaf(-zf, bs[2], float(d[2])));
       if (jq < R && t < t1) {
         mown = fmaxf(mown, v);
         sc[jq * Ts + (t - t0)] = v;
@@ -383,6 +393,8 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
     for (int i = 0; i < 32; ++i) acc[r][i] = 0.0f;
   }
   const uint4* vc = reinterpret_cast<const uint4*>(a.vc + row0 * kRowBytes);
+  const unsigned short* vsb = a.vs + row0;
+  const uint8_t* vzb = a.vz + row0;
   uint4 vn[kUnroll];
   unsigned short vsn[kUnroll];
   int vzn[kUnroll];
@@ -390,13 +402,13 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int tc = min(base + 16 * u + tq, t1 - 1);
-      vn[u] = vc[int64_t(tc) * 4 + p];
-      vsn[u] = a.vs[row0 + tc];
-      vzn[u] = a.vz[row0 + tc];
+      vn[u] = vc[unsigned(tc * 4 + p)];
+      vsn[u] = vsb[unsigned(tc)];
+      vzn[u] = vzb[unsigned(tc)];
     }
   };
-  if (t0 + wave * 16 * kUnroll < t1) vload(t0 + wave * 16 * kUnroll);
-  for (int base = t0 + wave * 16 * kUnroll; base < t1; base += kStride) {
+  if (first < t1) vload(first);
+  for (int base = first; base < t1; base += kStride) {
     uint4 c[kUnroll];
     float w[kUnroll][R];
     int z[kUnroll];
