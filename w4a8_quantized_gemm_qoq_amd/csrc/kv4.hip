@@ -131,31 +131,65 @@ __global__ __launch_bounds__(256) void kv4_quant_kernel(const uint4* __restrict_
   }
 }
 
+// acc += w * (FP16 value in the low / high half of x), the conversion done
+// inside the FMA (v_fma_mix_f32).  A code c enters as the FP16 subnormal
+// c * 2^-24 (bit pattern c; exact, the kernel runs with FP16 denormals on),
+// so the caller scales w by 2^24.
+__device__ __forceinline__ float fma_mix_lo(float w, unsigned x, float acc) {
+  asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel_hi:[0,1,0]" : "+v"(acc) : "v"(w), "v"(x));
+  return acc;
+}
+__device__ __forceinline__ float fma_mix_hi(float w, unsigned x, float acc) {
+  asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(acc) : "v"(w), "v"(x));
+  return acc;
+}
+
 // byte k of v as a float (one v_cvt_f32_ubyte{k})
 template <int k>
 __device__ __forceinline__ float ubyte(unsigned v) {
   return static_cast<float>((v >> (8 * k)) & 0xffu);
 }
 
-// acc[r][d] += w[r] * code[d] over the 32 dims of one 16-byte load (dword
-// w holds dims 8w..8w+7; byte b: dims 8w+2b (low nibble) and 8w+2b+1 (high)).
-// The R query heads of a block share each conversion of a code to float.
+// Weights of the V pass carry a factor kVScale(R): 2^24 where the codes enter
+// the FMAs as FP16 subnormals (up to 2 heads a block), 1 where they are
+// converted once and shared by 4 heads' FMAs (there the FMAs dominate and
+// the mixed-precision form measured slower).
+template <int R>
+constexpr float kVScale = R <= 2 ? 16777216.0f : 1.0f;
+
+// acc[r][d] += w[r] / kVScale * code[d] over the 32 dims of one 16-byte load
+// (dword i holds dims 8i..8i+7, dim 8i+k in nibble k).
 template <int R>
 __device__ __forceinline__ void axpy32(float (&acc)[R][32], const float (&w)[R], uint4 c) {
   const unsigned v[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    unsigned lo = v[i] & 0x0f0f0f0fu, hi = (v[i] >> 4) & 0x0f0f0f0fu;
-    // Opaque to the optimizer, so that it cannot fold the masks into a
-    // 4-bit field extract per code: each byte then converts with one
-    // v_cvt_f32_ubyte{0..3}.
-    asm volatile("" : "+v"(lo), "+v"(hi));
-    const float x[8] = {ubyte<0>(lo), ubyte<0>(hi), ubyte<1>(lo), ubyte<1>(hi),
-                        ubyte<2>(lo), ubyte<2>(hi), ubyte<3>(lo), ubyte<3>(hi)};
+    if constexpr (R <= 2) {
+      // a masked shift puts the codes of dims 8i+j and 8i+j+4 in the two
+      // halves of one register, which the heads' FMAs read directly
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+      for (int j = 0; j < 4; ++j) {
+        const unsigned x = (v[i] >> (4 * j)) & 0x000f000fu;
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[r][8 * i + e] = fmaf(w[r], x[e], acc[r][8 * i + e]);
+        for (int r = 0; r < R; ++r) {
+          acc[r][8 * i + j] = fma_mix_lo(w[r], x, acc[r][8 * i + j]);
+          acc[r][8 * i + j + 4] = fma_mix_hi(w[r], x, acc[r][8 * i + j + 4]);
+        }
+      }
+    } else {
+      unsigned lo = v[i] & 0x0f0f0f0fu, hi = (v[i] >> 4) & 0x0f0f0f0fu;
+      // Opaque to the optimizer, so that it cannot fold the masks into a
+      // 4-bit field extract per code: each byte then converts with one
+      // v_cvt_f32_ubyte{0..3}.
+      asm volatile("" : "+v"(lo), "+v"(hi));
+      const float x[8] = {ubyte<0>(lo), ubyte<0>(hi), ubyte<1>(lo), ubyte<1>(hi),
+                          ubyte<2>(lo), ubyte<2>(hi), ubyte<3>(lo), ubyte<3>(hi)};
+      // x[e]: the code of dim 8i + e
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r][8 * i + e] = fmaf(w[r], x[e], acc[r][8 * i + e]);
+    }
   }
 }
 
@@ -384,7 +418,8 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
   for (int r = 0; r < R; ++r) lsum[r] = red[r][0] + red[r][1] + red[r][2] + red[r][3];
 
   // pass 2: o = sum_t a_t s_t (c_t - z_t), accumulated as
-  // sum (a_t s_t) c_t - sum (a_t s_t z_t)
+  // sum (a_t s_t) c_t - sum (a_t s_t z_t); the weights carry kVScale<R>,
+  // taken off the second sum at the end (exact)
   float acc[R][32], zacc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -417,7 +452,7 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
       const int t = base + 16 * u + tq;
       const int tc = min(t, t1 - 1);
       c[u] = vn[u];
-      const float vs = __half2float(__ushort_as_half(vsn[u]));
+      const float vs = __half2float(__ushort_as_half(vsn[u])) * kVScale<R>;  // exact
 #pragma unroll
       for (int r = 0; r < R; ++r) w[u][r] = t < t1 ? sc[r * Ts + (tc - t0)] * vs : 0.0f;
       z[u] = vzn[u];
@@ -449,7 +484,7 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
     }
     if (tq == 0) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) part[wave][r][32 * p + i] = acc[r][i] - zacc[r];
+      for (int i = 0; i < 32; ++i) part[wave][r][32 * p + i] = acc[r][i] - zacc[r] * (1.0f / kVScale<R>);
     }
   }
   __syncthreads();
