@@ -45,14 +45,11 @@ constexpr int kMaxCacheLen = 32768;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // DPP lane permutations (VALU operations, no trip through the LDS crossbar):
-// quad_perm [1,0,3,2] and [2,3,0,1] pair lanes as xor 1 and xor 2 do, and
 // row_ror:4 / row_ror:8 rotate each row of 16 lanes, keeping lane % 4.
 template <int CTRL>
 __device__ __forceinline__ float dppf(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
 }
-constexpr int kDppXor1 = 0xb1;
-constexpr int kDppXor2 = 0x4e;
 constexpr int kDppRor4 = 0x124;
 constexpr int kDppRor8 = 0x128;
 
