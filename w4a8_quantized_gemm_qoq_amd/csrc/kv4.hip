@@ -154,13 +154,12 @@ __device__ __forceinline__ float ubyte(unsigned v) {
 template <int R>
 constexpr float kVScale = R <= 2 ? 16777216.0f : 1.0f;
 
-// acc[r][d] += w[r] / kVScale * code[d] over the 32 dims of one 16-byte load
-// (dword i holds dims 8i..8i+7, dim 8i+k in nibble k).
-template <int R>
-__device__ __forceinline__ void axpy32(float (&acc)[R][32], const float (&w)[R], uint4 c) {
-  const unsigned v[4] = {c.x, c.y, c.z, c.w};
+// acc[r][d] += w[r] / kVScale * code[d] over the 8 NW dims of one lane's
+// load (dword i holds dims 8i..8i+7, dim 8i+k in nibble k).
+template <int R, int NW>
+__device__ __forceinline__ void axpy_codes(float (&acc)[R][8 * NW], const float (&w)[R], const unsigned (&v)[NW]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NW; ++i) {
     if constexpr (R <= 2) {
       // a masked shift puts the codes of dims 8i+j and 8i+j+4 in the two
       // halves of one register, which the heads' FMAs read directly
@@ -223,8 +222,6 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
   __shared__ float red[R][kAttnThreads / 64];
   __shared__ float part[kAttnThreads / 64][R][kHeadDim + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int p = lane & 3;          // which 32 dims of the head
-  const int tq = lane >> 2;        // token slot within the wave's 16
   // Block -> (b, R consecutive query heads of one kv head).  Workgroups are
   // dealt round-robin to the 8 XCDs, each with its own L2; when a kv head
   // has several blocks, they are given consecutive slots on one XCD, so that
@@ -416,39 +413,60 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
 
   // pass 2: o = sum_t a_t s_t (c_t - z_t), accumulated as
   // sum (a_t s_t) c_t - sum (a_t s_t z_t); the weights carry kVScale<R>,
-  // taken off the second sum at the end (exact)
-  float acc[R][32], zacc[R];
+  // taken off the second sum at the end (exact).  LPT lanes share a token,
+  // DPT dims each: 4 x 32 for up to 2 heads, 8 x 16 for 4 heads, whose
+  // R x DPT accumulators would otherwise leave room for only 2 waves per SIMD.
+  constexpr int LPT = R >= 4 ? 8 : 4;
+  constexpr int DPT = kHeadDim / LPT;
+  constexpr int NW = DPT / 8;     // code dwords per lane and token
+  constexpr int SLOTS = 64 / LPT; // tokens per wave-wide load
+  constexpr int U = LPT;          // loads per round: 64 tokens a wave
+  static_assert(SLOTS * U == 16 * kUnroll, "both passes take the same tokens per round");
+  const int vp = lane % LPT;      // which DPT dims of the head
+  const int vt = lane / LPT;      // token slot within the wave's SLOTS
+  float acc[R][DPT], zacc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     zacc[r] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) acc[r][i] = 0.0f;
+    for (int i = 0; i < DPT; ++i) acc[r][i] = 0.0f;
   }
-  const uint4* vc = reinterpret_cast<const uint4*>(a.vc + row0 * kRowBytes);
+  const uint8_t* vrow = a.vc + row0 * kRowBytes;
   const unsigned short* vsb = a.vs + row0;
   const uint8_t* vzb = a.vz + row0;
-  uint4 vn[kUnroll];
-  unsigned short vsn[kUnroll];
-  int vzn[kUnroll];
+  unsigned vn[U][NW];
+  unsigned short vsn[U];
+  int vzn[U];
   auto vload = [&](int base) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int tc = min(base + 16 * u + tq, t1 - 1);
-      vn[u] = vc[unsigned(tc * 4 + p)];
+    for (int u = 0; u < U; ++u) {
+      const int tc = min(base + SLOTS * u + vt, t1 - 1);
+      if constexpr (NW == 4) {
+        const uint4 q = reinterpret_cast<const uint4*>(vrow)[unsigned(tc * 4 + vp)];
+        vn[u][0] = q.x;
+        vn[u][1] = q.y;
+        vn[u][2] = q.z;
+        vn[u][3] = q.w;
+      } else {
+        const uint2 q = reinterpret_cast<const uint2*>(vrow)[unsigned(tc * 8 + vp)];
+        vn[u][0] = q.x;
+        vn[u][1] = q.y;
+      }
       vsn[u] = vsb[unsigned(tc)];
       vzn[u] = vzb[unsigned(tc)];
     }
   };
   if (first < t1) vload(first);
   for (int base = first; base < t1; base += kStride) {
-    uint4 c[kUnroll];
-    float w[kUnroll][R];
-    int z[kUnroll];
+    unsigned c[U][NW];
+    float w[U][R];
+    int z[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int t = base + 16 * u + tq;
+    for (int u = 0; u < U; ++u) {
+      const int t = base + SLOTS * u + vt;
       const int tc = min(t, t1 - 1);
-      c[u] = vn[u];
+#pragma unroll
+      for (int i = 0; i < NW; ++i) c[u][i] = vn[u][i];
       const float vs = __half2float(__ushort_as_half(vsn[u])) * kVScale<R>;  // exact
 #pragma unroll
       for (int r = 0; r < R; ++r) w[u][r] = t < t1 ? sc[r * Ts + (tc - t0)] * vs : 0.0f;
@@ -456,32 +474,32 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_decode_attention_kernel(Attn
     }
     if (base + kStride < t1) vload(base + kStride);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      axpy32<R>(acc, w[u], c[u]);
+    for (int u = 0; u < U; ++u) {
+      axpy_codes<R, NW>(acc, w[u], c[u]);
 #pragma unroll
       for (int r = 0; r < R; ++r) zacc[r] = fmaf(w[u][r], float(z[u]), zacc[r]);
     }
   }
-  // sum over the 16 token slots of the wave (lanes with equal p): the four
-  // slots of a row by two rotations, then the four rows
+  // sum over the token slots of the wave (lanes with equal vp): the slots
+  // of a row of 16 lanes by rotations (by 4 and 8, or by 8), then the rows
 #pragma unroll
   for (int r = 0; r < R; ++r) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      acc[r][i] += dppf<kDppRor4>(acc[r][i]);
+    for (int i = 0; i < DPT; ++i) {
+      if constexpr (LPT == 4) acc[r][i] += dppf<kDppRor4>(acc[r][i]);
       acc[r][i] += dppf<kDppRor8>(acc[r][i]);
     }
-    zacc[r] += dppf<kDppRor4>(zacc[r]);
+    if constexpr (LPT == 4) zacc[r] += dppf<kDppRor4>(zacc[r]);
     zacc[r] += dppf<kDppRor8>(zacc[r]);
 #pragma unroll
     for (int off = 16; off < 64; off <<= 1) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) acc[r][i] += __shfl_xor(acc[r][i], off, 64);
+      for (int i = 0; i < DPT; ++i) acc[r][i] += __shfl_xor(acc[r][i], off, 64);
       zacc[r] += __shfl_xor(zacc[r], off, 64);
     }
-    if (tq == 0) {
+    if (vt == 0) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) part[wave][r][32 * p + i] = acc[r][i] - zacc[r] * (1.0f / kVScale<R>);
+      for (int i = 0; i < DPT; ++i) part[wave][r][DPT * vp + i] = acc[r][i] - zacc[r] * (1.0f / kVScale<R>);
     }
   }
   __syncthreads();
