@@ -110,12 +110,13 @@ def check_attention(Q, kk, vv, lengths, split=False):
 
 @pytest.mark.parametrize("B,H,Hkv,T,lengths,peak", [
     (2, 4, 4, 64, [64, 17], 1.0),          # full and partial unroll rounds
-    (3, 8, 2, 200, [200, 1, 0], 1.0),      # GQA, a single token, an empty sequence
+    (3, 8, 2, 200, [200, 1, 0], 1.0),      # GQA, a single token, an empty sequence (1 head a block)
     (1, 2, 1, 1000, [999], 4.0),           # sharp softmax, T not a multiple of 64
     (4, 4, 4, 256, [256, 255, 129, 64], 1.0),
-    (4, 16, 2, 96, [96, 50, 1, 33], 1.0),  # 8 heads per kv head: four 2-head blocks each, XCD-grouped
+    (4, 16, 2, 96, [96, 50, 1, 33], 1.0),  # 8 heads per kv head: eight 1-head blocks each, XCD-grouped
+    (32, 32, 8, 100, [100, 1, 77, 64] * 8, 1.0),  # 2 heads a block (512 blocks; 4 heads give 256)
     (1, 6, 2, 128, [128], 1.0),            # 3 heads per kv head: one head per block
-    (1, 8, 2, 9000, [9000], 1.0),          # 4 heads per kv head, but 4 score rows exceed LDS: 2 per block
+    (1, 8, 2, 9000, [9000], 1.0),          # 4 heads per kv head, few blocks: one head a block
     (1, 4, 1, 20000, [19999], 1.0),        # ... and one per block
 ])
 def test_kv4_attention_matches_oracle(B, H, Hkv, T, lengths, peak):

@@ -646,11 +646,12 @@ AttnPlan plan_with(int B, int H, int T_max, int R, bool allow_split) {
   return p;
 }
 
-// Heads per block: 4 or 2 of a kv group (1 only when neither divides the
-// group or fits the LDS budget).  More heads per block share each code's
-// conversion among more FMAs, fewer heads give more blocks: among the plans
-// that reach kSplitTargetBlocks blocks the one with the longest chunks wins
-// (then the most heads); if none does, the one with the most blocks.
+// Heads per block: 4, 2 or 1 of a kv group (with token chunks, 1 only when
+// neither 4 nor 2 divides the group or fits the LDS budget: there the chunks
+// supply the blocks).  More heads per block share each code's conversion
+// among more FMAs, fewer heads give more blocks: among the plans that reach
+// kSplitTargetBlocks blocks the one with the longest chunks wins (then the
+// most heads); if none does, the one with the most blocks.
 AttnPlan attn_plan(int B, int H, int Hkv, int T_max, bool allow_split) {
   const int rep = H / Hkv;
   AttnPlan best;
@@ -658,7 +659,7 @@ AttnPlan attn_plan(int B, int H, int Hkv, int T_max, bool allow_split) {
   int64_t best_blocks = 0, best_tc = 0;
   for (int r = kMaxHeadsPerBlock; r >= 1; r >>= 1) {
     if (rep % r) continue;
-    if (r == 1 && have) break;
+    if (r == 1 && have && allow_split) break;
     const AttnPlan p = plan_with(B, H, T_max, r, allow_split);
     const int64_t rows = p.nc > 1 ? p.Tc : T_max;  // score row length in LDS
     if (size_t(r) * size_t(rows) * sizeof(float) > kAttnScoreLds) continue;
