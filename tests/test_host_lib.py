@@ -13,6 +13,7 @@ import oracle as O
 import synthetic
 import w4a8_quantized_gemm_qoq_amd as q
 from w4a8_quantized_gemm_qoq_amd import _native
+from golden_io import read_fixture
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -434,6 +435,28 @@ def test_scale_columns_bit_exact_and_smoothing_factors():
     with np.errstate(over="ignore"):   # 65504 * 2 overflows FP16 to inf on purpose
         ref_e = O.scale_columns(E, f)
     assert np.array_equal(q.qoq_scale_columns(E, f).view(np.uint16), ref_e.view(np.uint16))
+
+
+def test_library_refuses_a_build_of_other_sources(monkeypatch):
+    # load_library() compares the source hash recorded by build() with the
+    # sources in the tree and refuses a library built from anything else
+    import w4a8_quantized_gemm_qoq_amd.build as b
+    monkeypatch.setattr(_native, "_lib", None)
+    monkeypatch.setattr(b, "source_hash", lambda arch="gfx950": "0" * 64)
+    with pytest.raises(RuntimeError, match="not built from the sources"):
+        _native.load_library()
+
+
+def test_scale_columns_hand_worked_cases():
+    # the library against the hand-worked fixture directly (not only against
+    # the oracle)
+    fx = read_fixture("scale_columns.txt")
+    for x, f, d, y in zip(fx["x"], fx["f"], fx["divide"], fx["y"]):
+        got = q.qoq_scale_columns(np.array([[x]], np.float16), np.array([f], np.float32), divide=bool(d))
+        assert got[0, 0].view(np.uint16) == np.float16(y).view(np.uint16), (x, f, d, y, got[0, 0])
+    X = np.array(fx["mat_x"], np.float16).reshape(2, 2)
+    got = q.qoq_scale_columns(X, np.array(fx["mat_f"], np.float32))
+    assert np.array_equal(got, np.array(fx["mat_y"], np.float16).reshape(2, 2))
 
 
 def test_transforms_validate_arguments():

@@ -557,6 +557,24 @@ def test_smoothing_factor_hand_cases():
     assert O.smoothing_factors([8.0], [2.0], 0.0).tolist() == [0.5]   # alpha = 0: 1 / w
 
 
+def test_scale_columns_hand_worked_cases():
+    # tests/golden/scale_columns.txt: orientation (multiply against divide),
+    # one FP16 rounding of the exact FP64 product (case 4 would round to the
+    # other neighbour through FP32), overflow to inf, a subnormal tie, exact
+    # halvings, and the factor running along the last axis
+    fx = read_fixture("scale_columns.txt")
+    for x, f, d, y in zip(fx["x"], fx["f"], fx["divide"], fx["y"]):
+        got = O.scale_columns(np.array([[x]], np.float16), np.array([f]), divide=bool(d))
+        assert got.dtype == np.float16
+        assert got[0, 0].view(np.uint16) == np.float16(y).view(np.uint16), (x, f, d, y, got[0, 0])
+    X = np.array(fx["mat_x"], np.float16).reshape(2, 2)
+    got = O.scale_columns(X, np.array(fx["mat_f"]))
+    assert np.array_equal(got, np.array(fx["mat_y"], np.float16).reshape(2, 2))
+    # divide=True with the same factors undoes it exactly here (powers of two and
+    # small integers)
+    assert np.array_equal(O.scale_columns(got, np.array(fx["mat_f"]), divide=True), X)
+
+
 def test_rotation_spreads_activation_outliers():
     # synthetic rows with x20 outlier channels: after the rotation no channel
     # dominates, so the per-token INT8 step is finer (information about the

@@ -81,6 +81,17 @@ def load_library():
         raise RuntimeError(
             f"{LIB_PATH} is not built; run `python -m w4a8_quantized_gemm_qoq_amd.build` "
             "(there is no fallback implementation)")
+    from .build import HASH_FILE, source_hash
+    try:
+        with open(HASH_FILE) as f:
+            built_from = f.read().strip()
+    except OSError:
+        built_from = None
+    if built_from != source_hash():
+        raise RuntimeError(
+            f"{LIB_PATH} was not built from the sources in this tree (its record {HASH_FILE} is "
+            f"{'missing' if built_from is None else 'different'}); rebuild with "
+            "`python -m w4a8_quantized_gemm_qoq_amd.build`")
     try:
         import torch  # noqa: F401  -- loads torch's libamdhip64 first
     except ImportError:

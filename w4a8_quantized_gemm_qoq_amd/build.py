@@ -10,6 +10,7 @@ division and round-half-to-even.
 
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -20,6 +21,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqoq.so")
+# Written next to the library by build(): the hash of the sources and flags it
+# was built from.  load_library() refuses a library whose record is missing or
+# differs from the sources in the tree.
+HASH_FILE = LIB + ".srchash"
 
 SOURCES = ["status.cpp", "pack.cpp", "transforms.cpp", "act_quant.hip", "kv4.hip", "gemm_w4.hip", "gemm_w8.hip", "gemm_sat.hip"]
 OBJDIR = os.path.join(PKG, "_build")
@@ -48,6 +53,21 @@ def compile_flags(arch: str = "gfx950") -> list[str]:
     ]
 
 
+def source_hash(arch: str = "gfx950") -> str:
+    """SHA-256 of every file under csrc/ and include/ (bytes, sorted by name)
+    and of the compile flags: what the library is built from."""
+    h = hashlib.sha256()
+    for d in (CSRC, INCLUDE):
+        for name in sorted(os.listdir(d)):
+            path = os.path.join(d, name)
+            if os.path.isfile(path):
+                h.update(os.path.relpath(path, ROOT).encode() + b"\0")
+                with open(path, "rb") as f:
+                    h.update(f.read())
+    h.update("\0".join(compile_flags(arch)).replace(ROOT, "").encode())
+    return h.hexdigest()
+
+
 def build_commands(out: str = LIB, arch: str = "gfx950") -> tuple[list[list[str]], list[str]]:
     """One compile command per source (independent, run in parallel), then the link."""
     flags = compile_flags(arch)
@@ -63,6 +83,9 @@ def build_commands(out: str = LIB, arch: str = "gfx950") -> tuple[list[list[str]
 def build(verbose: bool = False) -> str:
     """Compile libqoq.so; returns its path.  Always recompiles."""
     os.makedirs(OBJDIR, exist_ok=True)
+    digest = source_hash()
+    if os.path.exists(HASH_FILE):
+        os.remove(HASH_FILE)
     tmp = LIB + ".tmp"
     compiles, link = build_commands(tmp)
     procs = []
@@ -86,6 +109,8 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc link failed with exit code {res.returncode}")
     os.replace(tmp, LIB)
+    with open(HASH_FILE, "w") as f:
+        f.write(digest + "\n")
     return LIB
 
 
