@@ -213,6 +213,27 @@ QOQ_API int qoq_w4a8_gemm_i32(const int8_t* x8, const void* qweight, const void*
                       int64_t M, int64_t N, int64_t K, int64_t ldacc, int32_t group_size,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* Split-K scratch held by the library for qoq_w4a8_gemm_noalloc, per GPU. */
+#define QOQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * GEMM as qoq_w4a8_gemm, same arguments without the workspace, calling no
+ * allocating routine.  Where the launch plan splits K, the INT32 partials go
+ * to a device array of QOQ_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends.  Shapes whose partials would
+ * exceed it (qoq_w4a8_gemm_workspace_size() > QOQ_NOALLOC_SCRATCH_BYTES) are
+ * rejected with QOQ_ERR_UNSUPPORTED_SHAPE before any launch.  Every call on
+ * one GPU shares that array: calls that overlap on one GPU (concurrent
+ * streams, or threads) race and give wrong results; calls ordered on one
+ * stream are safe.  The GPU is the calling thread's current device, which
+ * must be the stream's.  Results are bit-identical to qoq_w4a8_gemm's.
+ */
+QOQ_API int qoq_w4a8_gemm_noalloc(const int8_t* x8, const void* sx_fp16, const void* qweight, const void* meta,
+                          const void* scale_fp16, void* y_fp16, int64_t M, int64_t N, int64_t K,
+                          int64_t ldy, int32_t group_size, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Offline accuracy transforms (host).  [PL §4, activation optimizations:
  * block inputs are rotated by a unitary matrix absorbed into the preceding

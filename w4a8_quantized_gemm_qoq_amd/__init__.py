@@ -26,6 +26,8 @@ from ._native import (  # noqa: F401
     qoq_w4a8_forward,
     qoq_w4a8_gemm,
     qoq_w4a8_gemm_i32,
+    qoq_w4a8_gemm_noalloc,
+    NOALLOC_SCRATCH_BYTES,
     qoq_w4a8_gemm_saturating,
     qoq_w4a8_gemm_saturating_i32,
     qoq_pack_weights_w8,

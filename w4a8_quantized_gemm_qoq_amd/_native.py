@@ -31,6 +31,7 @@ EXPORTS = [
     "qoq_w4a8_gemm_workspace_size",
     "qoq_w4a8_gemm",
     "qoq_w4a8_gemm_i32",
+    "qoq_w4a8_gemm_noalloc",
     "qoq_pack_weights_w8",
     "qoq_w8a8_gemm_workspace_size",
     "qoq_w8a8_gemm",
@@ -110,6 +111,7 @@ def load_library():
         "qoq_w4a8_gemm_workspace_size": (sz, [i64, i64, i64, i32]),
         "qoq_w4a8_gemm": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]),
         "qoq_w4a8_gemm_i32": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]),
+        "qoq_w4a8_gemm_noalloc": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]),
         "qoq_pack_weights_w8": (ctypes.c_int, [vp, i64, i64, vp, vp]),
         "qoq_w8a8_gemm_workspace_size": (sz, [i64, i64, i64]),
         "qoq_w8a8_gemm": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]),
@@ -314,6 +316,28 @@ def qoq_w4a8_gemm(x8, sx, w: PackedWeight, y=None, workspace=None, stream=None):
     _check(lib.qoq_w4a8_gemm(_t_ptr(x8), _t_ptr(sx), _t_ptr(w.qweight), _t_ptr(w.meta), _t_ptr(w.scale), _t_ptr(y),
                              M, w.N, w.K, y.stride(0), w.group_size, _t_ptr(workspace) if ws_bytes else None,
                              ws_bytes, _stream(stream)), "qoq_w4a8_gemm")
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # QOQ_NOALLOC_SCRATCH_BYTES in qoq.h
+
+
+def qoq_w4a8_gemm_noalloc(x8, sx, w: PackedWeight, y, stream=None):
+    """qoq_w4a8_gemm without a workspace: the library's own per-GPU scratch
+    holds any split-K partials (no device allocation in the call).  y is the
+    caller's float16 [M, N] output."""
+    import torch
+    _check_gemm_inputs(x8, w)
+    M = x8.shape[0]
+    _require_cuda(sx, y)
+    if y.dtype != torch.float16 or y.shape != (M, w.N) or y.stride(1) != 1:
+        raise ValueError("y must be float16 [M, N] with unit column stride")
+    if sx.dtype != torch.float16 or sx.numel() != M or not sx.is_contiguous():
+        raise ValueError("sx must be contiguous float16 [M]")
+    lib = load_library()
+    _check(lib.qoq_w4a8_gemm_noalloc(_t_ptr(x8), _t_ptr(sx), _t_ptr(w.qweight), _t_ptr(w.meta), _t_ptr(w.scale),
+                                     _t_ptr(y), M, w.N, w.K, y.stride(0), w.group_size, _stream(stream)),
+           "qoq_w4a8_gemm_noalloc")
     return y
 
 
