@@ -6,10 +6,14 @@ already resident in HBM: per-token INT8 activation quantization followed by the
 W4A8 GEMM with its fused FP16 epilogue.  The offline weight encode/pack is not
 part of a step (it runs once per weight, on the host).
 
-Default workload: the Llama-2-7B attention-projection shape (M=256 tokens,
-K=4096, N=4096, g128).  Prints ONE JSON line with the headline numbers, the
-roofline of the GEMM kernel, the CPU oracle baseline and a sweep over the
-other workload shapes (kernel-level TOPS / GB/s / roofline fraction).
+Default workload: the largest single-GPU configuration, the Qwen1.5-72B-like
+FFN at large batch (M=4096 tokens, K=8192, N=24576, g128), compute-bound on the
+INT8 matrix cores.  Prints ONE JSON line with the headline numbers, the
+roofline of the GEMM kernel, the CPU oracle baseline (all host cores, plus
+one-thread legs on the smaller workloads and the oracle's weight encode beside
+the library's packer) and a sweep over the other workload shapes
+(kernel-level TOPS / GB/s / roofline fraction; the decode shapes against the
+HBM roofline).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-sweep]
 """
@@ -103,28 +107,104 @@ def time_kernel(torch, launch, reps: int, sleep_ms: float = 20.0) -> float:
     return 1e3 * e0.elapsed_time(e1) / reps
 
 
-def cpu_baseline(w, X, W, seconds: float):
-    """The CPU oracle's online part (per-token quantization, exact GEMM, FP64
-    epilogue) on the same workload, repeated for about `seconds`."""
-    import numpy as np  # noqa: F401
-    import oracle as O
-    enc = O.encode_weight_g128(W) if w.group_size else O.encode_weight_per_channel(W)
+def blas_threads() -> int:
+    """Threads of the BLAS pool the oracle's matrix product runs on."""
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
     except Exception:
-        cores = len(os.sched_getaffinity(0))
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def _time_oracle(O, X, enc, seconds: float):
+    """Repeat the oracle's online part (per-token quantization, exact GEMM,
+    FP64 epilogue) for about `seconds`; returns (seconds per repetition, reps)."""
     reps = 0
     t0 = time.perf_counter()
     while True:
         O.w4a8_forward(X, enc)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= seconds or (reps >= 1 and el * (reps + 1) / reps > 3 * seconds):
+        if el >= seconds:
             break
-    return {"value": w.ops * reps / el / 1e12, "unit": "TOPS", "cores": int(cores), "kind": "oracle",
-            "sample": f"full {w.name} workload (M{w.M} K{w.K} N{w.N}), {reps} repetitions in {el:.1f} s",
-            "seconds_per_step": el / reps}
+    return el / reps, reps
+
+
+def _column_sample(w, W, max_cols: int):
+    """The first `max_cols` output channels of a workload's weight (all tokens,
+    all of K): a bounded sample of the same GEMM for the CPU oracle."""
+    n = min(w.N, max_cols)
+    return W[:n], n
+
+
+def cpu_baseline(w, X, W, seconds: float, max_cols: int = 2048):
+    """The CPU oracle's online part on a bounded sample of the workload (every
+    token row and all of K, the first `max_cols` output channels), repeated for
+    about `seconds` on all of the host's BLAS threads, in TOPS of that sample."""
+    import oracle as O
+    Ws, n = _column_sample(w, W, max_cols)
+    enc = O.encode_weight_g128(Ws) if w.group_size else O.encode_weight_per_channel(Ws)
+    per, reps = _time_oracle(O, X, enc, seconds)
+    ops = 2 * w.M * n * w.K
+    return {"value": round(ops / per / 1e12, 4), "unit": "TOPS", "cores": blas_threads(), "kind": "oracle",
+            "sample": (f"{w.name}: all {w.M} tokens x K={w.K} x the first {n} of {w.N} output channels "
+                       f"({ops / 1e9:.0f} G int ops), {reps} repetitions in {per * reps:.1f} s"),
+            "seconds_per_repetition": round(per, 4)}
+
+
+# One-thread and all-thread legs of the oracle on the smaller workloads (the
+# tiny GEMM, the attention projections, the prefill FFN and the decode
+# shapes), each on at most 1024 output channels.
+CPU_LEG_WORKLOADS = ["tiny", "attn_proj", "attn_qkv", "ffn_gateup_prefill", "ffn_down_prefill", "decode_m1",
+                     "decode_m16", "decode_m64"]
+
+
+def cpu_legs(seconds_per_leg: float, max_cols: int = 1024):
+    import oracle as O
+    import synthetic
+    from threadpoolctl import threadpool_limits
+    out = []
+    for name in CPU_LEG_WORKLOADS:
+        w = synthetic.get_workload(name)
+        n = min(w.N, max_cols)
+        # the first n rows of a workload's weight draw are a draw of n rows
+        X, Ws = synthetic.make_x(w.M, w.K, w.outliers), synthetic.make_w(n, w.K)
+        enc = O.encode_weight_g128(Ws) if w.group_size else O.encode_weight_per_channel(Ws)
+        ops = 2 * w.M * n * w.K
+        rec = {"workload": name, "sample": f"all {w.M} tokens x K={w.K} x the first {n} of {w.N} output channels"}
+        with threadpool_limits(limits=1, user_api="blas"):
+            per1, _ = _time_oracle(O, X, enc, seconds_per_leg)
+        perN, _ = _time_oracle(O, X, enc, seconds_per_leg)
+        rec.update({"tops_1_thread": round(ops / per1 / 1e12, 5), "tops_all_threads": round(ops / perN / 1e12, 5),
+                    "threads": blas_threads(), "ms_1_thread": round(1e3 * per1, 3),
+                    "ms_all_threads": round(1e3 * perN, 3)})
+        out.append(rec)
+    return out
+
+
+def encode_vs_pack(w, W, q, max_cols: int = 2048):
+    """The offline weight encode on the host: the oracle's progressive
+    quantization (levels 0 and 1, NumPy) against the library's packer
+    (quantization + packing, threaded C++), on the same sample of the
+    weight; and the packer on the whole weight."""
+    import oracle as O
+    Ws, n = _column_sample(w, W, max_cols)
+    q.qoq_pack_weights(Ws[:16], w.group_size)  # first call: library load, thread start-up
+    t0 = time.perf_counter()
+    O.encode_weight_g128(Ws) if w.group_size else O.encode_weight_per_channel(Ws)
+    t_o = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    q.qoq_pack_weights(Ws, w.group_size)
+    t_l = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    q.qoq_pack_weights(W, w.group_size)
+    t_full = time.perf_counter() - t0
+    return {"sample": f"{w.name} weight, the first {n} of {w.N} output channels x K={w.K}",
+            "oracle_encode_s": round(t_o, 4), "library_pack_s": round(t_l, 4),
+            "library_pack_full_weight_s": round(t_full, 4), "host_cores": len(os.sched_getaffinity(0))}
 
 
 def _copies(w, wbytes):
@@ -264,7 +344,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="attn_proj")
+    ap.add_argument("--workload", default="ffn_large_g128")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--sweep", default=",".join(SWEEP), help="comma-separated workload names")
     ap.add_argument("--sweep-reps", type=int, default=20)
@@ -274,6 +354,9 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-leg-seconds", type=float, default=0.5,
+                    help="seconds per one-thread / all-thread oracle leg on the smaller workloads")
+    ap.add_argument("--no-cpu-legs", action="store_true")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -359,7 +442,7 @@ def main():
     quant_us = time_kernel(torch, lambda i: q.qoq_quant_act_per_token(x, x8, sx), args.kernel_reps)
     bnd = bound_of(w)
     if bnd == "mfma":
-        achieved, peak, unit = w.ops / gemm_us / 1e6, PEAK_INT8_TOPS, "TFLOP/s"
+        achieved, peak, unit = w.ops / gemm_us / 1e6, PEAK_INT8_TOPS, "TOPS"
         per_unit = "2*M*N*K int8 ops per launch"
     else:
         achieved, peak, unit = algo_bytes(w) / gemm_us / 1e3, PEAK_HBM_GBS, "GB/s"
@@ -446,6 +529,12 @@ def main():
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, X, W, args.cpu_seconds)
+        print(f"[cpu_baseline] {json.dumps(out['cpu_baseline'])}", file=sys.stderr, flush=True)
+        out["host_encode"] = encode_vs_pack(w, W, q)
+        print(f"[host_encode] {json.dumps(out['host_encode'])}", file=sys.stderr, flush=True)
+        if not args.no_cpu_legs:
+            out["cpu_legs"] = cpu_legs(args.cpu_leg_seconds)
+            print(f"[cpu_legs] {json.dumps(out['cpu_legs'])}", file=sys.stderr, flush=True)
     else:
         out["cpu_baseline"] = None
 
