@@ -60,22 +60,13 @@
 #define QOQ_LTM 4
 #define QOQ_LTN 2
 #endif
-// Register-ring depth (groups of weights / activations in flight) of the big
+// Weight-ring depth (groups of weights in flight) of the big
 // and of the 128x128 large-M tile.
 #ifndef QOQ_LD
 #define QOQ_LD 2
 #endif
 #ifndef QOQ_SD
 #define QOQ_SD 4
-#endif
-#ifndef QOQ_LDA
-#define QOQ_LDA 2
-#endif
-#ifndef QOQ_AF_PIN
-#define QOQ_AF_PIN 0
-#endif
-#ifndef QOQ_SDA
-#define QOQ_SDA 2
 #endif
 // 128x128 tile: WM x WN waves, each TM x TN tiles of 32x32
 #ifndef QOQ_SWM
@@ -705,13 +696,23 @@ __global__ __launch_bounds__(512) void gemm_strip_kernel(GemmArgs a, int spb, in
 
 // ---------------------------------------------------------------------------
 // gemm_large: M > 64 (prefill, compute-bound).  Block = WM x WN waves, wave
-// tile = TM*32 rows x TN*32 columns of v_mfma_i32_32x32x32_i8.  The K loop is
-// unrolled by two with explicit ping-pong register buffers: while group g is
-// multiplied from LDS buffer g&1 and weight registers set g&1, the activation
-// chunks and packed weights of group g+1 are already in flight into the other
-// set, and are written to the other LDS buffer after the MFMAs.  There are no
-// loop-carried register copies, so every wait is for data that is actually
-// needed next.
+// tile = TM*32 rows x TN*32 columns of v_mfma_i32_32x32x32_i8.
+//
+// Activations: a ring of kLargeRing tiles of BM rows x 128 bytes in LDS, the
+// tile of group g in slot g % kLargeRing.  Each tile is copied global -> LDS
+// by buffer loads with an LDS destination (no registers, no LDS write
+// instructions), three groups ahead.  Lane i of a copy instruction writes LDS
+// chunk base + i, so every lane fetches the global chunk that the swizzled
+// layout keeps at that position.
+// Weights: global -> VGPR, D groups ahead, dequantized in registers.
+// Step l: copy tile l+3 into the slot of group l-1, multiply group l (the
+// first A fragments of group l+1 are read during its last K step), refill the
+// weight slot of group l with group l+D, wait for tile l+2 and meet the other
+// waves at one barrier.  After that barrier every wave is done with group l's
+// slot (the next copy may overwrite it) and tile l+2 is visible (the next step
+// reads its first fragments).
+constexpr int kLargeRing = 4;
+
 template <int BM, int THREADS>
 struct ATile {
   static constexpr int kChunks = BM * 8;
@@ -719,13 +720,17 @@ struct ATile {
   static_assert(kChunks % THREADS == 0, "A tile must split evenly over the block");
 };
 
-template <int NA, int THREADS>
-__device__ __forceinline__ void a_store(const u32x4 (&r)[NA], int8_t* lds) {
-#pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int ch = threadIdx.x + i * THREADS;
-    *reinterpret_cast<u32x4*>(lds + lds_off(ch >> 3, ch & 7)) = r[i];
-  }
+// Direct global -> LDS copy of 16 bytes per lane: lane i writes lds + 16 i.
+// (Kept in a device function: the builtin is not meaningful to the host pass.)
+__device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, int8_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+// Barrier for LDS traffic only: this wave's LDS operations are complete
+// (lgkmcnt 0) and every wave has arrived.  Global loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
 }
 
 // 16-byte weight loads per lane, per 32-column tile and group: UINT4 slots
@@ -745,52 +750,51 @@ __device__ __forceinline__ v4i b_op32(const u32x4 (&b)[wf_large_vec(WF)], int s,
   }
 }
 
-// Multiply one 128-wide K group: 4 K steps of 32.  Weight slot 0 of a column
-// tile holds K steps 0 and 2 (low / high half), slot 1 holds steps 1 and 3.
+// Multiply one 128-wide K group (4 K steps of 32) from LDS tile `lds`.  A
+// fragments are double-buffered across the steps: the reads of step s+1 are
+// issued before the multiplies of step s, and during the last step the reads
+// are those of step 0 of the next group (tile `lds_next`), left in af0.
+// Weight slot 0 of a column tile holds K steps 0 and 2 (low / high half),
+// slot 1 holds steps 1 and 3.
 template <int TM, int TN, int WF>
-__device__ __forceinline__ void large_group(v16i (&acc)[TM][TN], const int8_t* lds,
-                                            const u32x4 (&b)[TN][wf_large_vec(WF)], const uint32_t (&m)[TN],
-                                            uint32_t (&S)[TN], uint32_t (&C)[TN], int g, int row0, int c32, int hh) {
+__device__ __forceinline__ void large_group(v16i (&acc)[TM][TN], const int8_t* lds, const int8_t* lds_next,
+                                            v4i (&af0)[TM], const u32x4 (&b)[TN][wf_large_vec(WF)],
+                                            const uint32_t (&m)[TN], uint32_t (&S)[TN], uint32_t (&C)[TN], int g,
+                                            int row0, int c32, int hh) {
   if constexpr (wf_group_meta(WF)) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) meta_g128<WF>((m[t] >> (8 * (g & 3))) & 0xffu, S[t], C[t]);
   }
-  // A fragments are double-buffered across the 4 K steps: the reads of step
-  // s+1 are issued before the multiplies of step s, so LDS latency hides
-  // behind them.
-  v4i af[2][TM];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) af[0][i] = *reinterpret_cast<const v4i*>(lds + lds_off(row0 + i * 32 + c32, hh));
+  v4i af1[TM];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    if (s + 1 < 4) {
+    v4i (&cur)[TM] = (s & 1) ? af1 : af0;
+    v4i (&nxt)[TM] = (s & 1) ? af0 : af1;
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[(s + 1) & 1][i] = *reinterpret_cast<const v4i*>(lds + lds_off(row0 + i * 32 + c32, 2 * (s + 1) + hh));
-    }
-#if QOQ_AF_PIN
-    __builtin_amdgcn_sched_barrier(0);
-#endif
+    for (int i = 0; i < TM; ++i)
+      nxt[i] = *reinterpret_cast<const v4i*>((s < 3 ? lds : lds_next) +
+                                             lds_off(row0 + i * 32 + c32, s < 3 ? 2 * (s + 1) + hh : hh));
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       const v4i bf = b_op32<WF>(b[t], s, S[t], C[t]);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[s & 1][i], bf, acc[i][t], 0, 0, 0);
+      for (int i = 0; i < TM; ++i) acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur[i], bf, acc[i][t], 0, 0, 0);
     }
   }
 }
 
+// Dynamic LDS of the large kernel: the activation ring (the epilogue reuses
+// its first BM floats for the row scales).
+constexpr size_t large_lds_bytes(int bm) { return size_t(kLargeRing) * size_t(bm) * 128; }
 
-template <int WM, int WN, int TM, int TN, int D, int DA, int WF, bool I32OUT>
+template <int WM, int WN, int TM, int TN, int D, int WF, bool I32OUT>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
-  static_assert(D % 2 == 0, "ring depth must be even (LDS ping-pong parity)");
-  static_assert(D % DA == 0, "the activation ring must tile the weight ring");
   constexpr int THREADS = 64 * WM * WN;
   constexpr int BM = WM * TM * 32;
   constexpr int BN = WN * TN * 32;
+  constexpr int TILE = BM * 128;
   constexpr int NA = ATile<BM, THREADS>::kPer;
-  __shared__ __align__(16) int8_t As0[BM * 128];
-  __shared__ __align__(16) int8_t As1[BM * 128];
+  extern __shared__ __align__(16) int8_t smem[];
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
@@ -835,41 +839,36 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][t][e] = 0;
 
-  // Register rings.  Weights: D slots, slot l % D holds the packed weights of
-  // group gb+l, refilled right after use, D groups ahead.  Activations: DA
-  // slots; at the start of step l the chunks of group gb+l+1 are written to
-  // the LDS buffer not being read (every wave passed the previous barrier),
-  // and the slot is refilled DA groups ahead.  LDS is double-buffered by
-  // group parity.  Loads retire in issue order, so a step waits for the
-  // activations loaded DA steps earlier: DA steps of work must cover the
-  // load latency.
-  u32x4 ra[DA][NA];
-  u32x4 rb[D][TN][wf_large_vec(WF)];
-  uint32_t rm[D][TN];
+  // Groups past the range are clamped to the last one (their copies and loads
+  // stay inside the operands and are never multiplied).
   const int n = ge - gb;
   auto gcl = [&](int l) { return gb + min(l, n - 1); };
+  auto slot = [&](int l) { return smem + (l % kLargeRing) * TILE; };
 
-  // Global loads go through buffer descriptors: the per-lane offsets below
-  // are loop-invariant and the group is a wave-uniform soffset, so a round of
-  // loads costs no vector ALU work.  Every offset is clamped into the
-  // operands (rows past M read row M-1, strips past N the last strip, and
-  // groups past the range the last group), so no load leaves its buffer.
-  // Activations: chunk ch of the tile is row ch / 8, 16-byte chunk ch % 8.
+  // Activation copies.  Copy instruction i of a thread moves LDS chunk p =
+  // i * THREADS + threadIdx.x of the tile: row p / 8, stored position p % 8,
+  // which holds the row's logical chunk (p % 8) ^ ((row >> 1) & 7).  Rows past
+  // M read row M-1.  One descriptor over the block's rows; the group is a
+  // wave-uniform soffset.
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x8 + int64_t(m0) * K, int(min(BM, a.M - m0) * K));
   int aoff[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
-    const int ch = threadIdx.x + i * THREADS;
-    aoff[i] = (min(m0 + (ch >> 3), a.M - 1) - m0) * int(K) + (ch & 7) * 16;
+    const int p = threadIdx.x + i * THREADS;
+    const int row = p >> 3, kc = (p & 7) ^ ((row >> 1) & 7);
+    aoff[i] = (min(m0 + row, a.M - 1) - m0) * int(K) + kc * 16;
   }
-  auto a_ld = [&](u32x4 (&r)[NA], int g) {
+  auto a_copy = [&](int l) {
+    int8_t* dst = slot(l);
 #pragma unroll
-    for (int i = 0; i < NA; ++i) r[i] = buf_load16s<0>(xr, aoff[i], g * 128);
+    for (int i = 0; i < NA; ++i) buf_load_lds16(xr, dst + (i * THREADS + wave * 64) * 16, aoff[i], gcl(l) * 128);
   };
+
   // Weights and group metadata: one descriptor over the (at most 2 TN)
   // strips of this wave's columns.  UINT4 blocks: lane (c32, hh) loads slots
   // c16 + 16 hh and c16 + 16 (2 + hh), K steps {0, 2} and {1, 3}; INT8 blocks:
   // K step st is K chunk 2 st + hh = 16 j + 64 h, slot c16 + 16 j + 64 h.
+  // Per-lane offsets are loop-invariant; strips past N read the last strip.
   constexpr int kBlk = wf_block_bytes(WF);
   constexpr int kVec = wf_large_vec(WF);
   const int sfirst = min(n0 >> 4, a.n_strips - 1);
@@ -882,8 +881,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
     const int sb = (strip[t] - sfirst) * a.G * kBlk;
 #pragma unroll
     for (int v = 0; v < kVec; ++v) {
-      const int slot = WF == kWfW8 ? c16 + 16 * ((2 * v + hh) & 3) + 64 * ((2 * v + hh) >> 2) : c16 + 16 * (2 * v + hh);
-      woff[t][v] = sb + slot * 16;
+      const int sl = WF == kWfW8 ? c16 + 16 * ((2 * v + hh) & 3) + 64 * ((2 * v + hh) >> 2) : c16 + 16 * (2 * v + hh);
+      woff[t][v] = sb + sl * 16;
     }
   }
   // (formats without group metadata get an empty descriptor that is never used)
@@ -894,6 +893,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
   int moff[TN];
 #pragma unroll
   for (int t = 0; t < TN; ++t) moff[t] = ((strip[t] - sfirst) * a.G4q * 16 + c16) * 4;
+  u32x4 rb[D][TN][kVec];
+  uint32_t rm[D][TN];
   auto b_ld = [&](u32x4 (&b)[TN][kVec], uint32_t (&m)[TN], int g) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
@@ -902,49 +903,56 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
       if constexpr (wf_group_meta(WF)) m[t] = buf_load4s(mr, moff[t], (g >> 2) * 64);
     }
   };
+  // global loads of one b_ld and of one a_copy, for the hand-written waits
+  constexpr int kBLoads = TN * kVec + (wf_group_meta(WF) ? TN : 0);
+  static_assert(NA + 2 * kBLoads <= 63 && NA + D * kBLoads <= 63, "vmcnt holds at most 63");
 
-  a_ld(ra[0], gb);
-  a_store<NA, THREADS>(ra[0], As0);
+  // Prologue: tiles 0 and 1, the weight ring, tile 2.  Tiles 0 and 1 must
+  // have landed before the barrier (step 0 reads the first fragments of both).
+  a_copy(0);
+  a_copy(1);
 #pragma unroll
-  for (int d = 1; d <= DA; ++d) a_ld(ra[d % DA], gcl(d));
+  for (int dd = 0; dd < D; ++dd) b_ld(rb[dd], rm[dd], gcl(dd));
+  a_copy(2);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(NA + D * kBLoads));
+  lds_barrier();
+  v4i af0[TM];
 #pragma unroll
-  for (int d = 0; d < D; ++d) b_ld(rb[d], rm[d], gcl(d));
-  __syncthreads();
+  for (int i = 0; i < TM; ++i) af0[i] = *reinterpret_cast<const v4i*>(slot(0) + lds_off(row0 + i * 32 + c32, hh));
 
+  auto step = [&](int l, int u) {
+    a_copy(l + 3);
+    QOQ_COMPILER_FENCE();
+    large_group<TM, TN, WF>(acc, slot(l), slot(l + 1), af0, rb[u], rm[u], S, C, gb + l, row0, c32, hh);
+    QOQ_COMPILER_FENCE();
+    b_ld(rb[u], rm[u], gcl(l + D));
+    // tile l+2 was issued one step ago; after it come the weights of the last
+    // step, tile l+3 and the weights of this step
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NA + 2 * kBLoads));
+    lds_barrier();
+  };
   int l0 = 0;
   for (; l0 + D <= n; l0 += D) {
 #pragma unroll
-    for (int u = 0; u < D; ++u) {
-      const int l = l0 + u;
-      a_store<NA, THREADS>(ra[(u + 1) % DA], (u & 1) ? As0 : As1);
-      a_ld(ra[(u + 1) % DA], gcl(l + 1 + DA));
-      QOQ_COMPILER_FENCE();
-      large_group<TM, TN, WF>(acc, (u & 1) ? As1 : As0, rb[u], rm[u], S, C, gb + l, row0, c32, hh);
-      __syncthreads();
-      b_ld(rb[u], rm[u], gcl(l + D));
-      QOQ_COMPILER_FENCE();
-    }
+    for (int u = 0; u < D; ++u) step(l0 + u, u);
   }
-  // the last n % D groups are already in the rings
+  // the last n % D groups are already in the weight ring
   const int rem = n - l0;
 #pragma unroll
-  for (int u = 0; u < D; ++u) {
-    if (u < rem) {
-      if (u + 1 < rem) a_store<NA, THREADS>(ra[(u + 1) % DA], (u & 1) ? As0 : As1);
-      large_group<TM, TN, WF>(acc, (u & 1) ? As1 : As0, rb[u], rm[u], S, C, gb + l0 + u, row0, c32, hh);
-      __syncthreads();
-    }
-  }
+  for (int u = 0; u < D; ++u)
+    if (u < rem) step(l0 + u, u);
 
-  // epilogue: lane holds column lane%32 and rows 8*(r/4) + 4*(lane/32) + r%4.
+  // Epilogue: lane holds column lane%32 and rows 8*(r/4) + 4*(lane/32) + r%4.
   // Every scale is fetched before the first store: stores count on the same
   // in-order counter as global loads, so a load issued after a store waits
-  // for it.  The block's row scales go through LDS (free after the last
-  // barrier of the K loop; LDS reads have a counter of their own).
+  // for it.  The block's row scales go through LDS, once the trailing
+  // (clamped) copies have landed.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  lds_barrier();
   float sc[TN];
 #pragma unroll
   for (int t = 0; t < TN; ++t) sc[t] = I32OUT ? 0.0f : col_scale(a, n0 + 32 * t + c32);
-  float* sxs = reinterpret_cast<float*>(As0);
+  float* sxs = reinterpret_cast<float*>(smem);
   if constexpr (!I32OUT) {
     for (int r = threadIdx.x; r < BM; r += THREADS) sxs[r] = row_scale(a, m0 + r);
     __syncthreads();
@@ -1212,22 +1220,25 @@ inline size_t workspace_bytes_of(int64_t M, int64_t N, int64_t K) {
   return p.ksplit > 1 ? size_t(p.ksplit) * size_t(M) * size_t(round_up(N, kStrip)) * sizeof(int) : 0;
 }
 
-template <int WM, int WN, int TM, int TN, int D, int DA, int WF, bool I32>
+template <int WM, int WN, int TM, int TN, int D, int WF, bool I32>
 hipError_t launch_large(const GemmArgs& a, hipStream_t st) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+  constexpr size_t lds = large_lds_bytes(BM);
+  auto* fn = gemm_large_kernel<WM, WN, TM, TN, D, WF, I32>;
+  if (lds > 64 * 1024) {
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (attr != hipSuccess) return attr;
+  }
   const dim3 grid((a.n_strips * 16 + BN - 1) / BN, (a.M + BM - 1) / BM, a.ksplit);
-  hipLaunchKernelGGL((gemm_large_kernel<WM, WN, TM, TN, D, DA, WF, I32>), grid, dim3(64 * WM * WN), 0, st, a);
+  hipLaunchKernelGGL(fn, grid, dim3(64 * WM * WN), lds, st, a);
   return hipGetLastError();
 }
 
 template <int WF, bool I32>
 hipError_t launch_large_tile(int tile, const GemmArgs& a, hipStream_t st) {
-  // On the 256x256 tile the INT8 weight ring and the 16-bit lanes of the
-  // saturating dequantization leave room for one group of activations in
-  // flight instead of two (two would spill).
-  constexpr int kLDA = (WF == kWfW8 || WF == kWfG128Sat) ? 1 : QOQ_LDA;
-  if (tile == 0) return launch_large<QOQ_LWM, QOQ_LWN, QOQ_LTM, QOQ_LTN, QOQ_LD, kLDA, WF, I32>(a, st);
-  return launch_large<QOQ_SWM, QOQ_SWN, QOQ_STM, QOQ_STN, QOQ_SD, QOQ_SDA, WF, I32>(a, st);
+  if (tile == 0) return launch_large<QOQ_LWM, QOQ_LWN, QOQ_LTM, QOQ_LTN, QOQ_LD, WF, I32>(a, st);
+  return launch_large<QOQ_SWM, QOQ_SWN, QOQ_STM, QOQ_STN, QOQ_SD, WF, I32>(a, st);
 }
 
 template <int WF, bool I32>
