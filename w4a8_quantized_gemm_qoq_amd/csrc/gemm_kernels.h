@@ -40,7 +40,7 @@
 //   skinny: v_mfma_i32_16x16x64_i8, 16-row M tiles, K split across the
 //           waves of a block; up to 64 rows (decode, memory-bound), and up
 //           to 256 rows when one round of blocks covers the problem.
-//   large:  v_mfma_i32_32x32x32_i8, 128x128 or 256x256 block tiles, K
+//   large:  v_mfma_i32_32x32x32_i8, 128x512 or 64x256 block tiles, K
 //           optionally split across blocks; above 64 rows (prefill).
 // Weights always go global -> VGPR directly and are dequantized in
 // registers.  Both MFMA operands use the same K order per (lane group, byte),
@@ -53,35 +53,34 @@
 
 #include "qoq_internal.h"
 
-// Large-M tile: WM x WN waves, each TM x TN tiles of 32x32.
+// Large-M tiles: WM x WN waves, each TM x TN tiles of 32x32.  Both are one
+// row of 8 waves side by side: every wave multiplies the block's whole row
+// range by its own columns, so no two waves load or dequantize the same
+// weights, and the block's activation tile (read from LDS by all 8 waves) is
+// BM rows.  Big tile: 128 x 512 (waves of 128 x 64); small tile: 64 x 256
+// (waves of 64 x 32), for problems with too few big tiles.  Both hold 65536
+// outputs, so per-group block times are alike.
 #ifndef QOQ_LWM
-#define QOQ_LWM 2
-#define QOQ_LWN 4
+#define QOQ_LWM 1
+#define QOQ_LWN 8
 #define QOQ_LTM 4
 #define QOQ_LTN 2
 #endif
-// Weight-ring depth (groups of weights in flight) of the big
-// and of the 128x128 large-M tile.
+#ifndef QOQ_SWM
+#define QOQ_SWM 1
+#define QOQ_SWN 8
+#define QOQ_STM 2
+#define QOQ_STN 1
+#endif
+// Weight-ring depth (groups of weights in flight) of the big and of the
+// small large-M tile.
 #ifndef QOQ_LD
 #define QOQ_LD 2
 #endif
 #ifndef QOQ_SD
 #define QOQ_SD 4
 #endif
-// 128x128 tile: WM x WN waves, each TM x TN tiles of 32x32
-#ifndef QOQ_SWM
-#define QOQ_SWM 2
-#endif
-#ifndef QOQ_SWN
-#define QOQ_SWN 4
-#endif
-#ifndef QOQ_STM
-#define QOQ_STM 2
-#endif
-#ifndef QOQ_STN
-#define QOQ_STN 1
-#endif
-static_assert(QOQ_SWM * QOQ_STM * 32 == 128 && QOQ_SWN * QOQ_STN * 32 == 128, "the small large-M tile is 128x128");
+static_assert(QOQ_LWM * QOQ_LWN == 8 && QOQ_SWM * QOQ_SWN == 8, "large-M blocks are 8 waves");
 
 namespace qoq {
 namespace {
@@ -1162,12 +1161,15 @@ hipError_t dispatch_skinny_strip(const GemmArgs& a, hipStream_t st) {
 }
 
 
-// Large-M plans.  Tile 0: 256x256 blocks of 8 waves (each 128 x 64).
-// Tile 1: 128x128 blocks of 4 waves (each 64 x 64), for smaller problems.
+// Large-M plans.  Tile 0: the big tile (128 x 512); tile 1: the small one
+// (64 x 256), for problems with fewer than 192 big tiles.
 struct LargePlan {
   int tile;    // 0 or 1
   int ksplit;  // K splits
 };
+
+constexpr int kBigBM = QOQ_LWM * QOQ_LTM * 32, kBigBN = QOQ_LWN * QOQ_LTN * 32;
+constexpr int kSmallBM = QOQ_SWM * QOQ_STM * 32, kSmallBN = QOQ_SWN * QOQ_STN * 32;
 
 inline int64_t tiles_of(int64_t M, int64_t N_pad, int bm, int bn) { return ((M + bm - 1) / bm) * ((N_pad + bn - 1) / bn); }
 
@@ -1175,15 +1177,15 @@ inline int64_t tiles_of(int64_t M, int64_t N_pad, int bm, int bn) { return ((M +
 // 256) rounds of blocks, each G / ksplit groups long, plus, for a split, the
 // INT32 partials written and read again by the reduction (about 5 TB/s)
 // and its launch.  Per-group block times are the ones measured with every CU
-// busy: about 0.8 us for a 128x128 tile and 2.2 us for a 256x256 one.  Every
-// split keeps at least 4 groups (512 channels).
+// busy: about 0.8 us for a small tile and 2.2 us for a big one.  Every split
+// keeps at least 4 groups (512 channels).
 inline LargePlan plan_large(int64_t M, int64_t N, int64_t K) {
   const int64_t N_pad = round_up(N, kStrip);
   const int64_t G = K / kGroup;
   LargePlan p{0, 1};
-  const int64_t big = tiles_of(M, N_pad, 256, 256);
+  const int64_t big = tiles_of(M, N_pad, kBigBM, kBigBN);
   if (big < 192) p.tile = 1;
-  const int64_t tiles = p.tile ? tiles_of(M, N_pad, 128, 128) : big;
+  const int64_t tiles = p.tile ? tiles_of(M, N_pad, kSmallBM, kSmallBN) : big;
   const int64_t group_ns = p.tile ? 800 : 2200;
   auto cost_ns = [&](int64_t ks) {
     const int64_t run = ((tiles * ks + 255) / 256) * ((G + ks - 1) / ks) * group_ns;
