@@ -18,8 +18,10 @@
  *   - The return value is a qoq_status.  On failure qoq_last_error() gives a
  *     thread-local description; nothing has been written to outputs unless
  *     stated otherwise.
- *   - No function allocates device memory or keeps state between calls apart
- *     from that thread-local error text.  The caller owns every buffer.
+ *   - No function allocates device memory.  The caller owns every buffer.
+ *     Apart from that thread-local error text the library keeps no state
+ *     between calls, except the per-GPU split-K scratch that
+ *     qoq_w4a8_gemm_noalloc uses (declared below).
  *   - Host functions (pack / unpack / layout) run synchronously on the calling
  *     thread and touch host memory only.
  *   - Device functions take device pointers and a `stream` (a hipStream_t, or
@@ -68,9 +70,9 @@ QOQ_API const char* qoq_last_error(void);
 
 /*
  * Packed weight layout (QOQ_LAYOUT_ID 1).  The GEMM reads weights in the order
- * it computes with them ([PL §5, W4A8 GEMM optimization]: compute-aware weight
- * reordering stores weights in computation order so that each thread issues
- * 128-bit loads without runtime reordering).  Here the order follows the INT8
+ * it computes with them ([PL §5, W4A8 GEMM optimization]: the weights are
+ * rearranged offline so that the kernel fetches each thread's operands with
+ * wide loads and no shuffling at run time).  Here the order follows the INT8
  * matrix-core operand fragments of gfx950.
  *
  *   N_pad   = N rounded up to a multiple of 16; padded channels are all-zero.
@@ -165,8 +167,9 @@ QOQ_API int qoq_quant_act_per_token(const void* x_fp16, int64_t M, int64_t K, in
 /*
  * Fused producer (device): RMS normalization of each token row, then the
  * per-token INT8 quantization above, in one kernel that reads x once and
- * writes only x8 and s_x.  [PL §5, runtime and precision mapping: activation
- * quantization is fused into the preceding normalization layer].  Per row m:
+ * writes only x8 and s_x.  [PL §5, runtime and precision mapping: the
+ * quantizer runs inside the normalization kernel that produces the
+ * activations].  Per row m:
  *   S    = sum_k x[m,k]^2, exact (FP16 squares are integers times 2^-48);
  *   ms   = fp32(fp64(S) / K), r = 1 / sqrt(ms + eps) (FP32 IEEE add, sqrt and
  *          divide);
@@ -236,9 +239,10 @@ QOQ_API int qoq_w4a8_gemm_noalloc(const int8_t* x8, const void* sx_fp16, const v
 
 /* ---------------------------------------------------------------------------
  * Offline accuracy transforms (host).  [PL §4, activation optimizations:
- * block inputs are rotated by a unitary matrix absorbed into the preceding
- * weights, and output modules use per-channel smoothing factors]; [PL §4,
- * SmoothAttention: outlier key channels scaled down, alpha = 0.5].  Each is
+ * a unitary rotation of a block's inputs, folded into the weights before it,
+ * and per-channel smoothing for the layers where rotation is not used];
+ * [PL §4, SmoothAttention: the keys' outlier channels are divided down and
+ * the queries take the factor, alpha = 0.5].  Each is
  * an identity of the product, X W^T = (X H)(W H)^T = (X / l)(W * l)^T, so
  * the W4A8 path is run on the transformed tensors.  FP16 in and out, the
  * arithmetic in FP64 with one rounding to FP16 (half to even).
@@ -314,6 +318,17 @@ QOQ_API int qoq_kv4_decode_attention(const void* q_fp16, const uint8_t* k_codes,
  * 0 also for arguments qoq_kv4_decode_attention would reject.
  */
 QOQ_API size_t qoq_kv4_decode_attention_workspace_size(int32_t B, int32_t H, int32_t Hkv, int32_t T_max);
+
+/*
+ * Launch plan the decode attention takes for a shape (host, no GPU work): the
+ * query heads each workgroup serves (4, 2 or 1 of a kv group) and the number
+ * of token chunks (1: not split).  split != 0 asks for the plan of
+ * qoq_kv4_decode_attention_split, 0 for qoq_kv4_decode_attention.  For tests
+ * and tuning: it shows which kernel variant a shape reaches.  Returns
+ * QOQ_ERR_UNSUPPORTED_SHAPE for shapes the attention rejects.
+ */
+QOQ_API int qoq_kv4_decode_attention_plan(int32_t B, int32_t H, int32_t Hkv, int32_t T_max, int32_t split,
+                                  int32_t* heads_per_block, int32_t* token_chunks);
 
 /*
  * The same decode attention with the cached tokens cut into chunks spread

@@ -186,8 +186,8 @@ def group_codes(q8, s1, z):
 def quant_weight_level1(q8, group=GROUP):
     """Progressive quantization, level 1: per-group (g128) asymmetric UINT4.
 
-    [PL §2, integer quantization]: per-group quantization uses a separate
-    scale and zero point for every g columns within each row;
+    [PL §2, integer quantization]: with group quantization each run of g
+    consecutive input channels of a row gets its own scale and zero point;
     [PL §6, experimental setup]: the g128 variant uses group size 128.
 
     Returns (q4 uint8 [N,K], s1 uint8 [N,K/g], z uint8 [N,K/g]).
@@ -387,9 +387,9 @@ def dequant_level1_saturating(q4, s1, z, group=GROUP):
 def rmsnorm_fp16(X, gamma, eps):
     """RMS normalization of FP16 token rows, rounded to FP16.
 
-    [PL §5, runtime and precision mapping]: activation quantization is fused
-    into the preceding normalization layer; what is fused is the RMS
-    normalization of the token (x / rms(x) * gamma, the Llama-family norm)
+    [PL §5, runtime and precision mapping]: the per-token quantizer runs
+    inside the normalization that produces the activations; here that is the
+    RMS normalization of the token (x / rms(x) * gamma, the Llama-family norm)
     followed by the per-token INT8 quantization.  The pages give no
     arithmetic, so the statistic is taken exactly and rounded once:
       S    = sum_k x_k^2, exact (every FP16 value is an integer times 2^-24,

@@ -15,6 +15,7 @@ import pytest
 
 import oracle as O
 import w4a8_quantized_gemm_qoq_amd as q
+from kv4_cases import EDGE, PLAIN, SPLIT
 
 pytestmark = pytest.mark.gpu
 
@@ -108,29 +109,26 @@ def check_attention(Q, kk, vv, lengths, split=False):
             assert not o[b].any()
 
 
-@pytest.mark.parametrize("B,H,Hkv,T,lengths,peak", [
-    (2, 4, 4, 64, [64, 17], 1.0),          # full and partial unroll rounds
-    (3, 8, 2, 200, [200, 1, 0], 1.0),      # GQA, a single token, an empty sequence (1 head a block)
-    (1, 2, 1, 1000, [999], 4.0),           # sharp softmax, T not a multiple of 64
-    (4, 4, 4, 256, [256, 255, 129, 64], 1.0),
-    (4, 16, 2, 96, [96, 50, 1, 33], 1.0),  # 8 heads per kv head: eight 1-head blocks each, XCD-grouped
-    (32, 32, 8, 100, [100, 1, 77, 64] * 8, 1.0),  # 2 heads a block (512 blocks; 4 heads give 256)
-    (1, 6, 2, 128, [128], 1.0),            # 3 heads per kv head: one head per block
-    (1, 8, 2, 9000, [9000], 1.0),          # 4 heads per kv head, few blocks: one head a block
-    (1, 4, 1, 20000, [19999], 1.0),        # ... and one per block
-])
-def test_kv4_attention_matches_oracle(B, H, Hkv, T, lengths, peak):
+def assert_plan(B, H, Hkv, T, split, plan):
+    """The launch plan the shape reaches (pinned in kv4_cases.py)."""
+    assert q.qoq_kv4_decode_attention_plan(B, H, Hkv, T, split=split) == tuple(plan)
+
+
+@pytest.mark.parametrize("B,H,Hkv,T,lengths,peak,plan", PLAIN)
+def test_kv4_attention_matches_oracle(B, H, Hkv, T, lengths, peak, plan):
+    assert_plan(B, H, Hkv, T, False, plan)
     kk, vv = make_cache(B, Hkv, T, seed=T + H)
     Q = (np.random.default_rng(B).standard_normal((B, H, 128)) * peak).astype(np.float16)
     check_attention(Q, kk, vv, lengths)
 
 
-@pytest.mark.parametrize("split", [False, True])
-def test_kv4_attention_query_edge_cases(split):
+@pytest.mark.parametrize("B,H,Hkv,T,split,plan", EDGE)
+def test_kv4_attention_query_edge_cases(B, H, Hkv, T, split, plan):
     """Queries that stress the three-piece INT8 split of the scaled query: a
     zero head (all pieces zero: uniform weights), one FP16-max entry, FP16
-    subnormals only, all dims equal, and alternating signs at the FP16 max."""
-    B, H, Hkv, T = 1, 8, 2, 1500
+    subnormals only, all dims equal, and alternating signs at the FP16 max;
+    once for every kernel family (1, 2 and 4 heads a workgroup, split or not)."""
+    assert_plan(B, H, Hkv, T, split, plan)
     kk, vv = make_cache(B, Hkv, T, seed=77)
     Q = np.random.default_rng(77).standard_normal((B, H, 128)).astype(np.float16)
     Q[0, 0] = 0
@@ -140,7 +138,8 @@ def test_kv4_attention_query_edge_cases(split):
     Q[0, 3] = np.float16(0.3)
     Q[0, 4, ::2] = 65504
     Q[0, 4, 1::2] = -65504
-    check_attention(Q, kk, vv, [1499], split=split)
+    lengths = [T - 1] + [T] * (B - 1)
+    check_attention(Q, kk, vv, lengths, split=split)
 
 
 def test_kv4_attention_lengths_clamped_to_cache():
@@ -164,19 +163,9 @@ def test_kv4_attention_bench_shape(H, Hkv):
 
 # Token-split attention: chunks of the cache over more workgroups, their
 # softmax partials combined afterwards.  Same oracle, same tolerance.
-@pytest.mark.parametrize("B,H,Hkv,T,lengths,peak", [
-    (1, 32, 8, 4096, [4096], 1.0),             # 16 chunks of 256 tokens, two heads a workgroup
-    (2, 32, 32, 3000, [3000, 1], 1.0),         # MHA, 12 chunks of 256; one token: 11 empty chunks
-    (4, 32, 32, 4096, [4096, 3000, 1025, 0], 1.0),  # 4 chunks of 1024; 1025: a one-token chunk
-    (3, 8, 2, 1000, [1000, 0, 513], 1.0),      # empty sequence; 513 = two chunks and one token
-    (1, 2, 1, 1000, [999], 4.0),               # sharp softmax across chunks
-    (1, 6, 2, 2000, [1777], 1.0),              # 3 heads per kv head: one a workgroup
-    (1, 4, 1, 32768, [32768], 1.0),            # the longest cache: 128 chunks
-    (1, 32, 8, 32768, [30001], 1.0),           # 1024-token chunks; the last three partial or empty
-    (4, 64, 8, 8192, [8192, 5000, 8191, 1], 1.0),  # four heads a workgroup, 1024-token chunks
-    (2, 8, 1, 20000, [20000, 8191], 1.0),      # 8-head groups, chunk ends inside a sequence
-])
-def test_kv4_attention_split_matches_oracle(B, H, Hkv, T, lengths, peak):
+@pytest.mark.parametrize("B,H,Hkv,T,lengths,peak,plan", SPLIT)
+def test_kv4_attention_split_matches_oracle(B, H, Hkv, T, lengths, peak, plan):
+    assert_plan(B, H, Hkv, T, True, plan)
     assert q.qoq_kv4_decode_attention_workspace_size(B, H, Hkv, T) > 0
     kk, vv = make_cache(B, Hkv, T, seed=T + 3 * H)
     Q = (np.random.default_rng(B + 11).standard_normal((B, H, 128)) * peak).astype(np.float16)

@@ -575,6 +575,29 @@ def test_scale_columns_hand_worked_cases():
     assert np.array_equal(O.scale_columns(got, np.array(fx["mat_f"]), divide=True), X)
 
 
+def test_smooth_attention_keeps_scores_and_lowers_key_error():
+    # SmoothAttention: keys / lambda, queries * lambda with lambda = max|k|^0.5
+    # per channel (w = 1).  The scores are unchanged before rounding, and on
+    # keys with fixed outlier channels the INT4 key error drops (information
+    # about the transform on synthetic keys)
+    rng = np.random.default_rng(3)
+    K = rng.standard_normal((512, 128)).astype(np.float32)
+    K[:, [5, 40, 77, 100]] *= 20
+    K = K.astype(np.float16)
+    qv = rng.standard_normal(128).astype(np.float16)
+    lam = O.smoothing_factors(np.abs(K.astype(np.float64)).max(0), np.ones(128), 0.5).astype(np.float64)
+    K64, q64 = K.astype(np.float64), qv.astype(np.float64)
+    assert np.allclose((K64 / lam) @ (q64 * lam), K64 @ q64, rtol=0, atol=1e-10)
+
+    def key_err(Kq, factor):
+        d = O.kv4_dequant(*O.kv4_quant_per_head(Kq)) * factor
+        return np.linalg.norm(d - K64) / np.linalg.norm(K64)
+
+    plain = key_err(K, 1.0)
+    smooth = key_err(O.scale_columns(K, lam, divide=True), lam)
+    assert smooth < 0.5 * plain, (plain, smooth)
+
+
 def test_rotation_spreads_activation_outliers():
     # synthetic rows with x20 outlier channels: after the rotation no channel
     # dominates, so the per-token INT8 step is finer (information about the

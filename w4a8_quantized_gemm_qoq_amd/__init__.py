@@ -15,6 +15,7 @@ from ._native import (  # noqa: F401
     qoq_hadamard_rotate,
     qoq_kv4_decode_attention,
     qoq_kv4_decode_attention_workspace_size,
+    qoq_kv4_decode_attention_plan,
     qoq_kv4_quant,
     qoq_pack_codes,
     qoq_pack_weights,

@@ -42,6 +42,7 @@ EXPORTS = [
     "qoq_kv4_decode_attention",
     "qoq_kv4_decode_attention_workspace_size",
     "qoq_kv4_decode_attention_split",
+    "qoq_kv4_decode_attention_plan",
     "qoq_hadamard_rotate",
     "qoq_smoothing_factors",
     "qoq_scale_columns",
@@ -124,6 +125,8 @@ def load_library():
         "qoq_kv4_decode_attention_workspace_size": (sz, [i32, i32, i32, i32]),
         "qoq_kv4_decode_attention_split": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                                           ctypes.c_float, vp, vp, sz, vp]),
+        "qoq_kv4_decode_attention_plan": (ctypes.c_int, [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_int32),
+                                                          ctypes.POINTER(ctypes.c_int32)]),
         "qoq_hadamard_rotate": (ctypes.c_int, [vp, i64, i64, i64, vp]),
         "qoq_smoothing_factors": (ctypes.c_int, [vp, vp, i64, ctypes.c_float, vp]),
         "qoq_scale_columns": (ctypes.c_int, [vp, i64, i64, i64, vp, i32, vp]),
@@ -529,6 +532,15 @@ def qoq_kv4_quant(x, codes=None, scale=None, zero=None, stream=None):
 def qoq_kv4_decode_attention_workspace_size(B: int, H: int, Hkv: int, T: int) -> int:
     """Bytes of workspace the token-split attention needs (0: that shape is not split)."""
     return int(load_library().qoq_kv4_decode_attention_workspace_size(B, H, Hkv, T))
+
+
+def qoq_kv4_decode_attention_plan(B: int, H: int, Hkv: int, T: int, split: bool = False) -> tuple[int, int]:
+    """(query heads per workgroup, token chunks) the attention launches for this shape."""
+    r, nc = ctypes.c_int32(0), ctypes.c_int32(0)
+    lib = load_library()
+    _check(lib.qoq_kv4_decode_attention_plan(B, H, Hkv, T, int(split), ctypes.byref(r), ctypes.byref(nc)),
+           "qoq_kv4_decode_attention_plan")
+    return int(r.value), int(nc.value)
 
 
 def qoq_kv4_decode_attention(q, k, v, lengths, softmax_scale, o=None, stream=None, split=False, workspace=None):

@@ -197,8 +197,8 @@ __global__ __launch_bounds__(kThreads) void act_quant_scalar_kernel(const unsign
 // Fused producer: RMS normalization of each token row, then the per-token
 // quantization above ("QServe: W4A8KV4 Quantization and System Co-design for
 // Efficient LLM Serving", paperlayer.ai summary, §5 runtime and precision
-// mapping: activation quantization is fused into the preceding
-// normalization).  Per row:
+// mapping: the quantizer runs inside the normalization kernel that produces
+// the activations).  Per row:
 //   S   = sum_k x_k^2, exactly: an FP16 value is an integer times 2^-24, so
 //         its square is an integer times 2^-48 below 2^80, and a 128-bit
 //         integer holds the sum of any row;

@@ -781,6 +781,19 @@ extern "C" size_t qoq_kv4_decode_attention_workspace_size(int32_t B, int32_t H, 
   return attn_workspace_bytes(attn_plan(B, H, Hkv, T_max, true), B, H);
 }
 
+extern "C" int qoq_kv4_decode_attention_plan(int32_t B, int32_t H, int32_t Hkv, int32_t T_max, int32_t split,
+                                             int32_t* heads_per_block, int32_t* token_chunks) {
+  clear_error();
+  if (!heads_per_block || !token_chunks)
+    return fail(QOQ_ERR_INVALID_ARG, "qoq_kv4_decode_attention_plan: null pointer argument");
+  if (B < 1 || H < 1 || Hkv < 1 || H % Hkv || B > 65535 || H > 65535 || T_max < 1 || T_max > kMaxCacheLen)
+    return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "qoq_kv4_decode_attention_plan: shape out of range");
+  const AttnPlan p = attn_plan(B, H, Hkv, T_max, split != 0);
+  *heads_per_block = p.R;
+  *token_chunks = p.nc;
+  return QOQ_OK;
+}
+
 extern "C" int qoq_kv4_decode_attention_split(const void* q_fp16, const uint8_t* k_codes, const void* k_scale_fp16,
                                               const uint8_t* k_zero, const uint8_t* v_codes,
                                               const void* v_scale_fp16, const uint8_t* v_zero,
