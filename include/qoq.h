@@ -91,6 +91,10 @@ QOQ_API const char* qoq_last_error(void);
  *   scale (N_pad FP16): the per-channel FP16 scale -- s0 (g128) or s_w
  *     (per-channel); 0 for padded channels.
  *
+ * The metadata of a format lives in one buffer: for g128 the 8-bit group scale
+ * and the UINT4 zero share a byte (s1 <= 16 needs 4 bits), for per-channel
+ * the byte is the zero; the FP16 per-channel scale is the separate `scale`.
+ *
  * Code meaning ([PL §4, progressive group quantization]; [PL §5, W4A8 GEMM
  * optimization: subtraction after multiplication]):
  *   g128:         w8 = (q4 - z) * s1, s1 in [1,16], q4 and z in [0,15];
