@@ -83,6 +83,19 @@ def src_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def stored_traffic(name: str):
+    """HBM bytes per GEMM launch from the counter profile of this workload
+    (profiles/traffic_<name>.json), or None when there is none or the kernel
+    code has changed since it was taken."""
+    tf = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    try:
+        with open(tf) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return rec.get("hbm_bytes_per_launch") if rec.get("src_hash") == src_hash() else None
+
+
 def busy(torch, ms: float):
     """Keep the stream busy so launches queued behind it run back to back."""
     try:
@@ -330,7 +343,8 @@ def measure_gemm(torch, q, w, X, W, reps: int, comparators: bool = False):
     frac = tops / PEAK_INT8_TOPS if bnd == "mfma" else gbs / PEAK_HBM_GBS
     r = {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "group_size": w.group_size,
          "gemm_us": round(t_g, 3), "tops": round(tops, 2), "gbs": round(gbs, 1), "bound": bnd,
-         "frac": round(frac, 4), "weight_copies": copies, "act_quant_us": round(t_q, 3),
+         "frac": round(frac, 4), "traffic": stored_traffic(w.name), "weight_copies": copies,
+         "act_quant_us": round(t_q, 3),
          "act_quant_gbs": round(act_bytes(w) / t_q / 1e3, 1),
          "rmsnorm_quant_us": round(t_n, 3), "rmsnorm_quant_gbs": round(producer_bytes(w) / t_n / 1e3, 1)}
     if comparators:
@@ -448,15 +462,7 @@ def main():
         achieved, peak, unit = algo_bytes(w) / gemm_us / 1e3, PEAK_HBM_GBS, "GB/s"
         per_unit = "algorithmic bytes per launch"
 
-    traffic = None
-    tf = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
-    if os.path.exists(tf):
-        try:
-            rec = json.load(open(tf))
-            if rec.get("src_hash") == src_hash():
-                traffic = rec.get("hbm_bytes_per_launch")
-        except Exception:
-            traffic = None
+    traffic = stored_traffic(w.name)
 
     out = {
         "metric": METRIC,
