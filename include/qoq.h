@@ -220,6 +220,18 @@ QOQ_API int qoq_w4a8_gemm_i32(const int8_t* x8, const void* qweight, const void*
                       int64_t M, int64_t N, int64_t K, int64_t ldacc, int32_t group_size,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Launch plan qoq_w4a8_gemm takes for a shape (host, no GPU work), for tests
+ * and tuning.  kernel: 0 strip kernel (up to 16 rows, activations in LDS),
+ * 1 / 2 / 3 skinny kernel with 16- / 32- / 64-row tiles, 4 large-M kernel.
+ * tile: strips per workgroup (kernels 0-3) or the large-M block tile (0:
+ * 128 x 512, 1: 64 x 256, 2: 128 x 128 with K split inside the block).
+ * ksplit: K parts per workgroup (kernel 0) or K splits across workgroups with
+ * a reduction (kernel 4), else 1.  Same argument checks as qoq_w4a8_gemm.
+ */
+QOQ_API int qoq_w4a8_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t* kernel,
+                       int32_t* tile, int32_t* ksplit);
+
 /* Split-K scratch held by the library for qoq_w4a8_gemm_noalloc, per GPU. */
 #define QOQ_NOALLOC_SCRATCH_BYTES (32u << 20)
 

@@ -16,7 +16,8 @@ torch = pytest.importorskip("torch")
 
 @pytest.mark.parametrize("M,K,N", [(256, 4096, 4096),   # skinny, K split in LDS
                                    (300, 2048, 96),     # large kernel, K split over blocks + reduction
-                                   (520, 512, 24576),   # 256x256 tiles
+                                   (520, 512, 24576),   # big 128x512 tiles
+                                   (1024, 8320, 4096),  # K-set 128x128 tile, odd group count
                                    (16, 2048, 20000)])  # strip kernel
 def test_quant_gemm_graph_replays(M, K, N):
     X = synthetic.make_x(M, K, "frac", seed=M)

@@ -105,50 +105,12 @@ def test_act_quant_strided_rows_and_edge_values():
 
 # ------------------------------------------------------------- GEMM, small shapes
 
-SMALL = [
-    (16, 256, 256, 128),   # the tiny workload shape
-    (1, 128, 16, 128),
-    (17, 384, 40, 128),
-    (63, 256, 200, 128),
-    (64, 512, 96, 128),
-    (65, 256, 130, 128),
-    (130, 640, 72, 128),
-    (257, 384, 300, 128),
-    (5, 256, 48, 0),
-    (70, 384, 100, 0),
-    (200, 2048, 96, 128),   # skinny 64-row tiles: 4 row blocks of one strip, K split over 4 waves
-    (97, 1920, 40, 128),    # ... 15 groups: K parts of 3 and 4 groups per wave
-    (256, 1024, 50, 0),     # ... per-channel, 4 row blocks
-    (300, 2048, 96, 128),   # large-M kernel, K split in 4 (INT32 partials + reduction)
-    (290, 1920, 40, 128),   # ... K split in 2 with an odd group count per split
-    (270, 1024, 50, 0),     # ... per-channel with a K split
-    (300, 640, 520, 128),   # several 128x128 tiles, ragged M and N
-    (520, 512, 300, 128),   # 256x256 tiles (8 waves), ragged M and N
-    (16, 512, 9615, 128),   # strip kernel: 3 strips x 2 K parts per block, dead waves past N
-    (1, 256, 27990, 0),     # strip kernel: 7 strips per block, per-channel, ragged N
-    (12, 384, 200, 128),    # strip kernel: odd row count, K split in 8 with empty parts
-    (16, 10112, 40, 128),   # strip kernel: activations and metadata fill all 160 KB of LDS
-    (16, 10240, 40, 128),   # one group more exceeds LDS: K-split skinny kernel instead
-    (16, 2048, 20000, 128), # strip kernel, 5 strips per block: second activation copy after the barrier
-    (7, 1664, 17000, 0),    # ... per-channel, odd row count, copies running into padding
-    (512, 256, 24576, 128), # 256x256 tiles (192 of them), 2 groups
-    (520, 384, 24400, 0),   # ... per-channel, ragged M and N, 3 groups
-    (768, 640, 16384, 128), # ... 5 groups: the three-stage ring wraps
-    (512, 1024, 24576, 128),# ... 8 groups: 192 tiles fill one round, so no K split
-    (256, 1024, 12288, 128),# 128x128 tiles, 192 of them: no K split (a split would need 2 rounds)
-    (640, 1024, 4096, 0),   # ... per-channel, 160 tiles, ragged last row tile
-    (256, 512, 4096, 128),  # up to 256 rows in one round of skinny blocks (4 strips, K split in LDS)
-    (200, 384, 4000, 0),    # ... per-channel, ragged M and N (252 blocks)
-    (40, 256, 32768, 128),  # skinny 64-row tiles at most 7 strips per block; rows past M read as zeros
-    (192, 640, 4096, 128),  # 3 row blocks of 4 strips (192 blocks): strip count from the activation-aware cost
-    (161, 384, 2000, 0),    # ... per-channel, 2 strips per block, ragged last row block and last strip block
-    (250, 1024, 160, 128),  # ... one strip per block, 4 row blocks, rows past M in the last
-    (50, 384, 30000, 0),    # ... per-channel, ragged N
-]
+from gemm_cases import SMALL  # noqa: E402  (shapes and the launch plan each reaches)
 
 
-@pytest.mark.parametrize("M,K,N,gs", SMALL)
-def test_gemm_small_shapes_match_oracle(M, K, N, gs):
+@pytest.mark.parametrize("M,K,N,gs,plan", SMALL)
+def test_gemm_small_shapes_match_oracle(M, K, N, gs, plan):
+    assert q.qoq_w4a8_gemm_plan(M, N, K, gs) == plan
     X = synthetic.make_x(M, K, "frac", seed=M)
     W = synthetic.make_w(N, K, seed=N)
     x8, sx, acc, y, _ = run_path(X, W, gs)
@@ -248,7 +210,7 @@ KMAX = 133120
 @pytest.mark.parametrize("M,N", [(1, 40),     # strip kernel, activations and metadata fill 147 KB of LDS
                                  (16, 48),    # activations exceed LDS: 16-row skinny kernel
                                  (64, 40),    # 64-row skinny kernel, 260 groups per wave
-                                 (300, 64)])  # large kernel, 128x128 tile, K split 64 ways + reduction
+                                 (300, 64)])  # large kernel, small tile, K split 128 ways + reduction
 def test_max_k_near_int32_bound(M, N):
     # K at the INT32 limit through every launch plan.  Row 0 of the weights is
     # w8 = 121 throughout and row 0 of the activations 127, so accumulator

@@ -28,6 +28,7 @@ from ._native import (  # noqa: F401
     qoq_w4a8_gemm,
     qoq_w4a8_gemm_i32,
     qoq_w4a8_gemm_noalloc,
+    qoq_w4a8_gemm_plan,
     NOALLOC_SCRATCH_BYTES,
     qoq_w4a8_gemm_saturating,
     qoq_w4a8_gemm_saturating_i32,

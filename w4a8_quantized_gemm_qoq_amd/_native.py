@@ -32,6 +32,7 @@ EXPORTS = [
     "qoq_w4a8_gemm",
     "qoq_w4a8_gemm_i32",
     "qoq_w4a8_gemm_noalloc",
+    "qoq_w4a8_gemm_plan",
     "qoq_pack_weights_w8",
     "qoq_w8a8_gemm_workspace_size",
     "qoq_w8a8_gemm",
@@ -113,6 +114,8 @@ def load_library():
         "qoq_w4a8_gemm": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]),
         "qoq_w4a8_gemm_i32": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]),
         "qoq_w4a8_gemm_noalloc": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]),
+        "qoq_w4a8_gemm_plan": (ctypes.c_int, [i64, i64, i64, i32, ctypes.POINTER(ctypes.c_int32),
+                                              ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]),
         "qoq_pack_weights_w8": (ctypes.c_int, [vp, i64, i64, vp, vp]),
         "qoq_w8a8_gemm_workspace_size": (sz, [i64, i64, i64]),
         "qoq_w8a8_gemm": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]),
@@ -320,6 +323,18 @@ def qoq_w4a8_gemm(x8, sx, w: PackedWeight, y=None, workspace=None, stream=None):
                              M, w.N, w.K, y.stride(0), w.group_size, _t_ptr(workspace) if ws_bytes else None,
                              ws_bytes, _stream(stream)), "qoq_w4a8_gemm")
     return y
+
+
+GEMM_KERNELS = {0: "strip", 1: "skinny16", 2: "skinny32", 3: "skinny64", 4: "large"}
+
+
+def qoq_w4a8_gemm_plan(M: int, N: int, K: int, group_size: int = GROUP) -> tuple[str, int, int]:
+    """(kernel family, strips per block or large-M tile, K parts or splits) of a GEMM call."""
+    k, t, s = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    lib = load_library()
+    _check(lib.qoq_w4a8_gemm_plan(M, N, K, group_size, ctypes.byref(k), ctypes.byref(t), ctypes.byref(s)),
+           "qoq_w4a8_gemm_plan")
+    return GEMM_KERNELS[k.value], int(t.value), int(s.value)
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20   # QOQ_NOALLOC_SCRATCH_BYTES in qoq.h

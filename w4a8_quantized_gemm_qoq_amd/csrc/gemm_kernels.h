@@ -40,8 +40,9 @@
 //   skinny: v_mfma_i32_16x16x64_i8, 16-row M tiles, K split across the
 //           waves of a block; up to 64 rows (decode, memory-bound), and up
 //           to 256 rows when one round of blocks covers the problem.
-//   large:  v_mfma_i32_32x32x32_i8, 128x512 or 64x256 block tiles, K
-//           optionally split across blocks; above 64 rows (prefill).
+//   large:  v_mfma_i32_32x32x32_i8, 128x512, 64x256 or 128x128 block tiles, K
+//           optionally split across blocks (and, on the 128x128 tile,
+//           inside the block); above 64 rows (prefill).
 // Weights always go global -> VGPR directly and are dequantized in
 // registers.  Both MFMA operands use the same K order per (lane group, byte),
 // so the contraction is exact whatever order the matrix unit walks K in.
@@ -72,6 +73,20 @@
 #define QOQ_STM 2
 #define QOQ_STN 1
 #endif
+// K-set tile: the small tile's problems when each block has many groups to
+// run: 128 x 128 blocks of two sets of 4 waves (waves of 128 x 32), the sets
+// taking alternate groups.  A weight fragment then feeds 4 MFMAs instead of 2.
+#ifndef QOQ_KWM
+#define QOQ_KWM 1
+#define QOQ_KWN 4
+#define QOQ_KTM 4
+#define QOQ_KTN 1
+#define QOQ_KKI 2
+#endif
+// Fewest groups per block (after any K split) for the K-set tile.
+#ifndef QOQ_KSET_MIN_GROUPS
+#define QOQ_KSET_MIN_GROUPS 64
+#endif
 // Weight-ring depth (groups of weights in flight) of the big and of the
 // small large-M tile.
 #ifndef QOQ_LD
@@ -80,7 +95,8 @@
 #ifndef QOQ_SD
 #define QOQ_SD 4
 #endif
-static_assert(QOQ_LWM * QOQ_LWN == 8 && QOQ_SWM * QOQ_SWN == 8, "large-M blocks are 8 waves");
+static_assert(QOQ_LWM * QOQ_LWN == 8 && QOQ_SWM * QOQ_SWN == 8 && QOQ_KWM * QOQ_KWN * QOQ_KKI == 8,
+              "large-M blocks are 8 waves");
 
 namespace qoq {
 namespace {
@@ -704,12 +720,9 @@ __global__ __launch_bounds__(512) void gemm_strip_kernel(GemmArgs a, int spb, in
 // chunk base + i, so every lane fetches the global chunk that the swizzled
 // layout keeps at that position.
 // Weights: global -> VGPR, D groups ahead, dequantized in registers.
-// Step l: copy tile l+3 into the slot of group l-1, multiply group l (the
-// first A fragments of group l+1 are read during its last K step), refill the
-// weight slot of group l with group l+D, wait for tile l+2 and meet the other
-// waves at one barrier.  After that barrier every wave is done with group l's
-// slot (the next copy may overwrite it) and tile l+2 is visible (the next step
-// reads its first fragments).
+// A step multiplies one group per set of waves (one set unless K is split
+// inside the block); the ring holds four steps' tiles, copied three steps
+// ahead, with one barrier per step (see the kernel).
 constexpr int kLargeRing = 4;
 
 template <int BM, int THREADS>
@@ -786,17 +799,24 @@ __device__ __forceinline__ void large_group(v16i (&acc)[TM][TN], const int8_t* l
 // its first BM floats for the row scales).
 constexpr size_t large_lds_bytes(int bm) { return size_t(kLargeRing) * size_t(bm) * 128; }
 
-template <int WM, int WN, int TM, int TN, int D, int WF, bool I32OUT>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
-  constexpr int THREADS = 64 * WM * WN;
+// KI > 1 splits K inside the block: KI sets of WM x WN waves take the groups
+// of a step in turn (set k multiplies group KI s + k of step s), so each wave
+// can hold a taller tile (fewer dequantizations per MFMA) at the same number
+// of blocks; the sets' INT32 partials are added exactly through LDS at the end.
+template <int WM, int WN, int TM, int TN, int D, int KI, int WF, bool I32OUT>
+__global__ __launch_bounds__(64 * WM * WN * KI) void gemm_large_kernel(GemmArgs a) {
+  constexpr int THREADS = 64 * WM * WN * KI;
   constexpr int BM = WM * TM * 32;
   constexpr int BN = WN * TN * 32;
   constexpr int TILE = BM * 128;
-  constexpr int NA = ATile<BM, THREADS>::kPer;
+  constexpr int NA1 = ATile<BM, THREADS>::kPer;  // copies per thread per tile
+  constexpr int NA = NA1 * KI;                   // copies per thread per step
+  constexpr int NB = kLargeRing * KI;            // ring slots (tiles)
   extern __shared__ __align__(16) int8_t smem[];
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave / WN, wn = wave % WN;
+  const int kset = wave / (WM * WN), wl = wave % (WM * WN);
+  const int wm = wl / WN, wn = wl % WN;
   // Tile order.  Workgroups are dispatched round-robin over the 8 XCDs, each
   // with its own L2.  Remap so that each XCD gets a contiguous run of tiles,
   // and walk that run in bands of up to 8 row tiles, column by column, so the
@@ -823,13 +843,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
   int strip[TN];
 #pragma unroll
   for (int t = 0; t < TN; ++t) strip[t] = min((n0 + 32 * t + c32) >> 4, a.n_strips - 1);
-
   uint32_t S[TN] = {}, C[TN] = {};
   if constexpr (WF == kWfPerChannel) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) meta_perchannel(a.meta8[strip[t] * 16 + c16], S[t], C[t]);
   }
-
   v16i acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -840,27 +858,34 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
 
   // Groups past the range are clamped to the last one (their copies and loads
   // stay inside the operands and are never multiplied).
-  const int n = ge - gb;
+  const int n = ge - gb;               // groups of this split
+  const int nsteps = (n + KI - 1) / KI;
   auto gcl = [&](int l) { return gb + min(l, n - 1); };
-  auto slot = [&](int l) { return smem + (l % kLargeRing) * TILE; };
+  auto slot = [&](int l) { return smem + (l % NB) * TILE; };
 
   // Activation copies.  Copy instruction i of a thread moves LDS chunk p =
   // i * THREADS + threadIdx.x of the tile: row p / 8, stored position p % 8,
   // which holds the row's logical chunk (p % 8) ^ ((row >> 1) & 7).  Rows past
   // M read row M-1.  One descriptor over the block's rows; the group is a
   // wave-uniform soffset.
+
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x8 + int64_t(m0) * K, int(min(BM, a.M - m0) * K));
-  int aoff[NA];
+  int aoff[NA1];
 #pragma unroll
-  for (int i = 0; i < NA; ++i) {
+  for (int i = 0; i < NA1; ++i) {
     const int p = threadIdx.x + i * THREADS;
     const int row = p >> 3, kc = (p & 7) ^ ((row >> 1) & 7);
     aoff[i] = (min(m0 + row, a.M - 1) - m0) * int(K) + kc * 16;
   }
-  auto a_copy = [&](int l) {
-    int8_t* dst = slot(l);
+  // the KI tiles of step s (groups KI s .. KI s + KI - 1)
+  auto a_copy = [&](int s) {
 #pragma unroll
-    for (int i = 0; i < NA; ++i) buf_load_lds16(xr, dst + (i * THREADS + wave * 64) * 16, aoff[i], gcl(l) * 128);
+    for (int q = 0; q < KI; ++q) {
+      const int l = KI * s + q;
+      int8_t* dst = slot(l);
+#pragma unroll
+      for (int i = 0; i < NA1; ++i) buf_load_lds16(xr, dst + (i * THREADS + wave * 64) * 16, aoff[i], gcl(l) * 128);
+    }
   };
 
   // Weights and group metadata: one descriptor over the (at most 2 TN)
@@ -884,7 +909,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
       woff[t][v] = sb + sl * 16;
     }
   }
-  // (formats without group metadata get an empty descriptor that is never used)
   const __amdgpu_buffer_rsrc_t mr =
       wf_group_meta(WF)
           ? make_rsrc(reinterpret_cast<const int8_t*>(a.meta) + int64_t(sfirst) * a.G4q * 64, nws * a.G4q * 64)
@@ -902,60 +926,100 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_large_kernel(GemmArgs a) {
       if constexpr (wf_group_meta(WF)) m[t] = buf_load4s(mr, moff[t], (g >> 2) * 64);
     }
   };
-  // global loads of one b_ld and of one a_copy, for the hand-written waits
+  // global loads of one b_ld, for the hand-written waits
   constexpr int kBLoads = TN * kVec + (wf_group_meta(WF) ? TN : 0);
   static_assert(NA + 2 * kBLoads <= 63 && NA + D * kBLoads <= 63, "vmcnt holds at most 63");
 
-  // Prologue: tiles 0 and 1, the weight ring, tile 2.  Tiles 0 and 1 must
-  // have landed before the barrier (step 0 reads the first fragments of both).
+  // Prologue: the tiles of steps 0 and 1, the weight ring, the tiles of step
+  // 2.  Steps 0 and 1 must have landed before the barrier (step 0 reads the
+  // first fragments of both).
   a_copy(0);
   a_copy(1);
 #pragma unroll
-  for (int dd = 0; dd < D; ++dd) b_ld(rb[dd], rm[dd], gcl(dd));
+  for (int dd = 0; dd < D; ++dd) b_ld(rb[dd], rm[dd], gcl(KI * dd + kset));
   a_copy(2);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(NA + D * kBLoads));
   lds_barrier();
   v4i af0[TM];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) af0[i] = *reinterpret_cast<const v4i*>(slot(0) + lds_off(row0 + i * 32 + c32, hh));
+  for (int i = 0; i < TM; ++i) af0[i] = *reinterpret_cast<const v4i*>(slot(kset) + lds_off(row0 + i * 32 + c32, hh));
 
-  auto step = [&](int l, int u) {
-    a_copy(l + 3);
+  // Step s: copy the tiles of step s+3 into the slots of step s-1, multiply
+  // this wave's group of step s (reading the first fragments of its group of
+  // step s+1), refill the weight slot with its group of step s+D, wait for the
+  // tiles of step s+2 and meet the other waves.  After the barrier every wave
+  // is done with step s's slots and the tiles of step s+2 are visible.
+  // A set whose group lies past the range (odd group counts) skips it.
+  auto step = [&](int s, int u) {
+    a_copy(s + 3);
     QOQ_COMPILER_FENCE();
-    large_group<TM, TN, WF>(acc, slot(l), slot(l + 1), af0, rb[u], rm[u], S, C, gb + l, row0, c32, hh);
+    const int l = KI * s + kset;
+    if (KI == 1 || l < n)
+      large_group<TM, TN, WF>(acc, slot(l), slot(l + KI), af0, rb[u], rm[u], S, C, gb + l, row0, c32, hh);
     QOQ_COMPILER_FENCE();
-    b_ld(rb[u], rm[u], gcl(l + D));
-    // tile l+2 was issued one step ago; after it come the weights of the last
-    // step, tile l+3 and the weights of this step
+    b_ld(rb[u], rm[u], gcl(KI * (s + D) + kset));
+    // the tiles of step s+2 were issued one step ago; after them come the
+    // weights of the last step, the tiles of step s+3 and this step's weights
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(NA + 2 * kBLoads));
     lds_barrier();
   };
-  int l0 = 0;
-  for (; l0 + D <= n; l0 += D) {
+  int s0 = 0;
+  for (; s0 + D <= nsteps; s0 += D) {
 #pragma unroll
-    for (int u = 0; u < D; ++u) step(l0 + u, u);
+    for (int u = 0; u < D; ++u) step(s0 + u, u);
   }
-  // the last n % D groups are already in the weight ring
-  const int rem = n - l0;
+  // the last nsteps % D steps' weights are already in the ring
+  const int rem = nsteps - s0;
 #pragma unroll
   for (int u = 0; u < D; ++u)
-    if (u < rem) step(l0 + u, u);
+    if (u < rem) step(s0 + u, u);
 
-  // Epilogue: lane holds column lane%32 and rows 8*(r/4) + 4*(lane/32) + r%4.
-  // Every scale is fetched before the first store: stores count on the same
-  // in-order counter as global loads, so a load issued after a store waits
-  // for it.  The block's row scales go through LDS, once the trailing
-  // (clamped) copies have landed.
+  // the trailing (clamped) copies land before the LDS is reused
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   lds_barrier();
+  if constexpr (KI > 1) {
+    // exact sum of the K sets' partials: set k > 0 parks its accumulators as
+    // 16-byte records [set-1][wave][i][t][4][lane]; set 0 adds them
+    v4i* red = reinterpret_cast<v4i*>(smem);
+    if (kset > 0) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            red[(((((kset - 1) * WM * WN + wl) * TM + i) * TN + t) * 4 + q) * 64 + lane] =
+                v4i{acc[i][t][4 * q], acc[i][t][4 * q + 1], acc[i][t][4 * q + 2], acc[i][t][4 * q + 3]};
+    }
+    __syncthreads();
+    if (kset == 0) {
+#pragma unroll
+      for (int k2 = 1; k2 < KI; ++k2)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int t = 0; t < TN; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const v4i v = red[(((((k2 - 1) * WM * WN + wl) * TM + i) * TN + t) * 4 + q) * 64 + lane];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[i][t][4 * q + e] += v[e];
+            }
+    }
+  }
+  // Epilogue (set 0): lane holds column lane%32 and rows 8*(r/4) + 4*(lane/32)
+  // + r%4.  Every scale is fetched before the first store: stores count on
+  // the same in-order counter as global loads, so a load issued after a store
+  // waits for it.  The block's row scales go through LDS, past the partials.
   float sc[TN];
 #pragma unroll
   for (int t = 0; t < TN; ++t) sc[t] = I32OUT ? 0.0f : col_scale(a, n0 + 32 * t + c32);
-  float* sxs = reinterpret_cast<float*>(smem);
+  float* sxs = reinterpret_cast<float*>(smem + (KI > 1 ? (KI - 1) * WM * WN * TM * TN * 4096 : 0));
   if constexpr (!I32OUT) {
     for (int r = threadIdx.x; r < BM; r += THREADS) sxs[r] = row_scale(a, m0 + r);
     __syncthreads();
   }
+  if (kset != 0) return;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -1114,14 +1178,6 @@ hipError_t launch_skinny_upto(int tn, const GemmArgs& a, hipStream_t st) {
   return launch_skinny<TM, T, QOQ_SKS4, skinny_pf(WF), QOQ_SAD, WF, I32>(a, st);
 }
 
-template <int TM, int WF, bool I32>
-hipError_t dispatch_skinny_tn(const GemmArgs& a, hipStream_t st) {
-  constexpr int kHi = skinny_tn_max(TM);
-  const int ny = (a.M + TM * 16 - 1) / (TM * 16);
-  const int tn = TM == 4 ? pick_skinny_tn_rows(a.n_strips, ny, kHi) : pick_skinny_tn(a.n_strips, ny, kHi);
-  return launch_skinny_upto<TM, WF, I32, kHi>(tn, a, st);
-}
-
 // Dynamic LDS of the strip kernel: the activations, or the K-part partial
 // sums, whichever is larger.
 inline size_t strip_lds_bytes(int G, int R, int spb, int ks, bool group_meta) {
@@ -1148,23 +1204,24 @@ hipError_t launch_strip(const GemmArgs& a, int spb, int ks, size_t lds, hipStrea
 
 // Up to 16 rows: the strip kernel when the activations fit in LDS, else the
 // K-split skinny kernel.  Strips per block as for the skinny kernel (rounds of
-// 256 blocks); the K split fills a block up to 8 waves.
-template <int WF, bool I32>
-hipError_t dispatch_skinny_strip(const GemmArgs& a, hipStream_t st) {
-  const int R = a.M < 16 ? a.M : 16;
-  const int spb = pick_skinny_tn(a.n_strips, 1, 8);
-  int ks = 8 / spb;
-  if (ks < 1) ks = 1;
-  const size_t lds = strip_lds_bytes(a.G, R, spb, ks, wf_group_meta(WF));
-  if (lds <= kStripMaxLds) return launch_strip<WF, I32>(a, spb, ks, lds, st);
-  return dispatch_skinny_tn<1, WF, I32>(a, st);
+// 256 blocks); the K split fills a block up to 8 waves.  Returns false when
+// the activations do not fit.
+inline bool plan_strip(int64_t M, int n_strips, int G, bool group_meta, int* spb, int* ks, size_t* lds) {
+  const int R = M < 16 ? int(M) : 16;
+  *spb = pick_skinny_tn(n_strips, 1, 8);
+  *ks = 8 / *spb;
+  if (*ks < 1) *ks = 1;
+  *lds = strip_lds_bytes(G, R, *spb, *ks, group_meta);
+  return *lds <= kStripMaxLds;
 }
 
-
 // Large-M plans.  Tile 0: the big tile (128 x 512); tile 1: the small one
-// (64 x 256), for problems with fewer than 192 big tiles.
+// (64 x 256), for problems with fewer than 192 big tiles; tile 2: the K-set
+// tile (128 x 128), in place of the small one when every block runs at least
+// QOQ_KSET_MIN_GROUPS groups (the sets' final reduction and the shorter runs
+// per set cost more than they save below that).
 struct LargePlan {
-  int tile;    // 0 or 1
+  int tile;    // 0, 1 or 2
   int ksplit;  // K splits
 };
 
@@ -1193,6 +1250,7 @@ inline LargePlan plan_large(int64_t M, int64_t N, int64_t K) {
   };
   for (int64_t ks = 2; G / ks >= 4; ks *= 2)
     if (cost_ns(ks) < cost_ns(p.ksplit)) p.ksplit = int(ks);
+  if (p.tile == 1 && G / p.ksplit >= QOQ_KSET_MIN_GROUPS) p.tile = 2;
   return p;
 }
 
@@ -1216,39 +1274,73 @@ inline bool skinny_mid(int64_t M, int64_t N) {
   return blocks <= 256;
 }
 
-inline size_t workspace_bytes_of(int64_t M, int64_t N, int64_t K) {
-  if (M <= kSkinnyMaxM || skinny_mid(M, N)) return 0;
+// The launch plan of one GEMM call.  kernel: the kernel family; tile: strips
+// per block (strip and skinny kernels) or the large-M tile (0 big, 1 small,
+// 2 K-set); ksplit: K parts per block (strip kernel) or K splits across
+// blocks (large kernel).
+enum GemmKernel { kPlanStrip = 0, kPlanSkinny16 = 1, kPlanSkinny32 = 2, kPlanSkinny64 = 3, kPlanLarge = 4 };
+struct GemmPlan {
+  int kernel, tile, ksplit;
+};
+
+inline GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool group_meta) {
+  const int n_strips = int(round_up(N, kStrip) / kStrip);
+  const int G = int(K / kGroup);
+  if (M <= 16) {
+    int spb, ks;
+    size_t lds;
+    if (plan_strip(M, n_strips, G, group_meta, &spb, &ks, &lds)) return {kPlanStrip, spb, ks};
+    return {kPlanSkinny16, pick_skinny_tn(n_strips, int((M + 15) / 16), skinny_tn_max(1)), 1};
+  }
+  if (M <= 32) return {kPlanSkinny32, pick_skinny_tn(n_strips, int((M + 31) / 32), skinny_tn_max(2)), 1};
+  if (M <= kSkinnyMaxM || skinny_mid(M, N))
+    return {kPlanSkinny64, pick_skinny_tn_rows(n_strips, int((M + 63) / 64), skinny_tn_max(4)), 1};
   const LargePlan p = plan_large(M, N, K);
-  return p.ksplit > 1 ? size_t(p.ksplit) * size_t(M) * size_t(round_up(N, kStrip)) * sizeof(int) : 0;
+  return {kPlanLarge, p.tile, p.ksplit};
 }
 
-template <int WM, int WN, int TM, int TN, int D, int WF, bool I32>
+inline size_t workspace_bytes_of(int64_t M, int64_t N, int64_t K) {
+  const GemmPlan p = plan_gemm(M, N, K, false);
+  return p.kernel == kPlanLarge && p.ksplit > 1
+             ? size_t(p.ksplit) * size_t(M) * size_t(round_up(N, kStrip)) * sizeof(int)
+             : 0;
+}
+
+template <int WM, int WN, int TM, int TN, int D, int KI, int WF, bool I32>
 hipError_t launch_large(const GemmArgs& a, hipStream_t st) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
-  constexpr size_t lds = large_lds_bytes(BM);
-  auto* fn = gemm_large_kernel<WM, WN, TM, TN, D, WF, I32>;
+  constexpr size_t lds = large_lds_bytes(BM) * KI;
+  auto* fn = gemm_large_kernel<WM, WN, TM, TN, D, KI, WF, I32>;
   if (lds > 64 * 1024) {
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (attr != hipSuccess) return attr;
   }
   const dim3 grid((a.n_strips * 16 + BN - 1) / BN, (a.M + BM - 1) / BM, a.ksplit);
-  hipLaunchKernelGGL(fn, grid, dim3(64 * WM * WN), lds, st, a);
+  hipLaunchKernelGGL(fn, grid, dim3(64 * WM * WN * KI), lds, st, a);
   return hipGetLastError();
 }
 
 template <int WF, bool I32>
 hipError_t launch_large_tile(int tile, const GemmArgs& a, hipStream_t st) {
-  if (tile == 0) return launch_large<QOQ_LWM, QOQ_LWN, QOQ_LTM, QOQ_LTN, QOQ_LD, WF, I32>(a, st);
-  return launch_large<QOQ_SWM, QOQ_SWN, QOQ_STM, QOQ_STN, QOQ_SD, WF, I32>(a, st);
+  if (tile == 0) return launch_large<QOQ_LWM, QOQ_LWN, QOQ_LTM, QOQ_LTN, QOQ_LD, 1, WF, I32>(a, st);
+  if (tile == 1) return launch_large<QOQ_SWM, QOQ_SWN, QOQ_STM, QOQ_STN, QOQ_SD, 1, WF, I32>(a, st);
+  return launch_large<QOQ_KWM, QOQ_KWN, QOQ_KTM, QOQ_KTN, QOQ_SD, QOQ_KKI, WF, I32>(a, st);
 }
 
 template <int WF, bool I32>
 hipError_t dispatch(const GemmArgs& a0, void* ws, hipStream_t st) {
-  if (a0.M <= 16) return dispatch_skinny_strip<WF, I32>(a0, st);
-  if (a0.M <= 32) return dispatch_skinny_tn<2, WF, I32>(a0, st);
-  if (a0.M <= kSkinnyMaxM || skinny_mid(a0.M, a0.N)) return dispatch_skinny_tn<4, WF, I32>(a0, st);
-  const LargePlan p = plan_large(a0.M, a0.N, int64_t(a0.G) * kGroup);
+  const GemmPlan p = plan_gemm(a0.M, a0.N, int64_t(a0.G) * kGroup, wf_group_meta(WF));
+  switch (p.kernel) {
+    case kPlanStrip: {
+      const size_t lds = strip_lds_bytes(a0.G, a0.M < 16 ? a0.M : 16, p.tile, p.ksplit, wf_group_meta(WF));
+      return launch_strip<WF, I32>(a0, p.tile, p.ksplit, lds, st);
+    }
+    case kPlanSkinny16: return launch_skinny_upto<1, WF, I32, skinny_tn_max(1)>(p.tile, a0, st);
+    case kPlanSkinny32: return launch_skinny_upto<2, WF, I32, skinny_tn_max(2)>(p.tile, a0, st);
+    case kPlanSkinny64: return launch_skinny_upto<4, WF, I32, skinny_tn_max(4)>(p.tile, a0, st);
+    default: break;
+  }
   if (p.ksplit == 1) return launch_large_tile<WF, I32>(p.tile, a0, st);
   // split K: INT32 partials into the workspace, then reduce + epilogue
   GemmArgs a = a0;

@@ -36,6 +36,20 @@ extern "C" int qoq_w4a8_gemm_i32(const int8_t* x8, const void* qweight, const vo
                            workspace, workspace_bytes, true, st);
 }
 
+extern "C" int qoq_w4a8_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t* kernel,
+                                  int32_t* tile, int32_t* ksplit) {
+  clear_error();
+  if (!kernel || !tile || !ksplit) return fail(QOQ_ERR_INVALID_ARG, "qoq_w4a8_gemm_plan: null pointer argument");
+  if (int st = check_weight_shape(N, K, group_size)) return st;
+  if (M < 1 || M > 0x7fffffffLL - 4096)
+    return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "qoq_w4a8_gemm_plan: M=%lld out of range", (long long)M);
+  const GemmPlan p = plan_gemm(M, N, K, group_size != 0);
+  *kernel = p.kernel;
+  *tile = p.tile;
+  *ksplit = p.ksplit;
+  return QOQ_OK;
+}
+
 // ---------------------------------------------------------------------------
 // Allocation-free variant of qoq_w4a8_gemm.  The split-K INT32 partials live
 // in this file-scope device array instead of a caller workspace.  Each GPU
