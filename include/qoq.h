@@ -226,8 +226,9 @@ QOQ_API int qoq_w4a8_gemm_i32(const int8_t* x8, const void* qweight, const void*
  * 1 / 2 / 3 skinny kernel with 16- / 32- / 64-row tiles, 4 large-M kernel.
  * tile: strips per workgroup (kernels 0-3) or the large-M block tile (0:
  * 128 x 512, 1: 64 x 256, 2: 128 x 128 with K split inside the block).
- * ksplit: K parts per workgroup (kernel 0) or K splits across workgroups with
- * a reduction (kernel 4), else 1.  Same argument checks as qoq_w4a8_gemm.
+ * ksplit: K parts per workgroup (kernels 0-3: waves that split the K groups
+ * and sum their partials in LDS) or K splits across workgroups with a
+ * reduction (kernel 4).  Same argument checks as qoq_w4a8_gemm.
  */
 QOQ_API int qoq_w4a8_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t* kernel,
                        int32_t* tile, int32_t* ksplit);

@@ -1,8 +1,9 @@
 """Launch plans of the W4A8 GEMM (host query, no GPU): every parity shape
 reaches the plan pinned for it in gemm_cases.py, and together the shapes
 reach every kernel variant -- the strip kernel with one and several strips
-per block and with K parts, the skinny kernel with 16-, 32- and 64-row tiles,
-and the three large-M tiles with and without a K split."""
+per block and with K parts, the skinny kernel with 16-, 32- and 64-row tiles
+and 4 or 8 K parts per block, and the three large-M tiles with and without a
+K split."""
 
 import pytest
 
@@ -18,12 +19,15 @@ def test_parity_shape_plans(M, K, N, gs, plan):
 def test_parity_shapes_reach_every_kernel_variant():
     plans = {c[-1] for c in SMALL}
     kinds = {(k, t if k == "large" else None, s > 1) for k, t, s in plans}
-    want = {("strip", None, True), ("strip", None, False), ("skinny16", None, False),
-            ("skinny32", None, False), ("skinny64", None, False)}
+    want = {("strip", None, True), ("strip", None, False), ("skinny16", None, True),
+            ("skinny32", None, True), ("skinny64", None, True)}
     want |= {("large", t, False) for t in (0, 1, 2)} | {("large", t, True) for t in (1, 2)}
     assert want <= kinds, sorted(want - kinds)
-    # the skinny kernel with several strips per block, and both weight formats on the large tiles
+    # the skinny kernel with several strips per block, with 4 and with 8 K
+    # parts per block, and both weight formats on the large tiles
     assert any(k == "skinny64" and t > 1 for k, t, _ in plans)
+    assert {s for k, _, s in plans if k.startswith("skinny")} == {4, 8}
+    assert any(k == "skinny64" and t > 1 and s == 8 for k, t, s in plans)
     for t in (0, 1, 2):
         assert {c[3] for c in SMALL if c[-1][0] == "large" and c[-1][1] == t} == {0, 128}
 
@@ -36,7 +40,7 @@ def test_headline_and_decode_plans():
     assert q.qoq_w4a8_gemm_plan(1024, 28672, 4096) == ("large", 0, 1)
     assert q.qoq_w4a8_gemm_plan(1, 28672, 8192) == ("strip", 7, 1)
     assert q.qoq_w4a8_gemm_plan(16, 28672, 8192) == ("strip", 7, 1)
-    assert q.qoq_w4a8_gemm_plan(64, 28672, 8192) == ("skinny64", 7, 1)
+    assert q.qoq_w4a8_gemm_plan(64, 28672, 8192) == ("skinny64", 7, 8)
 
 
 def test_plan_query_rejects_bad_shapes():

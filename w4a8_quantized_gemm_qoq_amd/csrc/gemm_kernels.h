@@ -135,6 +135,16 @@ __device__ __forceinline__ uint32_t buf_load4s(__amdgpu_buffer_rsrc_t r, int vof
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
 
+// s_waitcnt immediates (gfx9 encoding): wait until at most n vector-memory
+// operations of this wave are outstanding, leaving the other counters free.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Direct global -> LDS copy of 16 bytes per lane: lane i writes lds + 16 i.
+// (Kept in a device function: the builtin is not meaningful to the host pass.)
+__device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, int8_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
 // Packed 16-bit lanes, written as vector arithmetic (selected as v_pk_mad_u16
 // and friends) so that the scheduler sees ordinary VALU instructions.
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -284,21 +294,58 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int row, int col, i
 // ---------------------------------------------------------------------------
 // skinny: M <= 64 (decode), and up to 256 rows when one round of blocks
 // covers the problem.  A block is KS waves that split the K groups of the
-// same TN strips between them, so every wave streams different weight bytes.
-// Each wave passes its activations (whole 128-byte rows, shared by all blocks
-// and mostly served from L2) through a wave-private LDS buffer into the MFMA
-// operand layout, and streams its weights through a PF-deep register ring of
-// 128-bit loads so that enough bytes are in flight to cover HBM latency.  The
-// KS partial INT32 accumulators are summed exactly through LDS at the end.
-template <int TM, int TN, int KS, int PF, int AD, int WF, bool I32OUT>
+// same TN strips between them, so every wave streams different weight bytes
+// (8 waves, two per SIMD, when every wave still gets at least 8 groups: one
+// wave's dequantization then runs while the other's MFMAs do).  Each wave
+// streams its weights through a PF-deep register ring of 128-bit loads and
+// its activations (whole 128-byte rows, shared by all blocks and mostly
+// served from L2) through a PF-deep ring of its own in LDS, filled by direct
+// global -> LDS copies, so that enough bytes are in flight to cover HBM
+// latency.  The KS partial INT32 accumulators are summed exactly through LDS
+// at the end, and the FP16 results leave through an LDS tile in 16-byte row
+// segments.
+
+// The A fragments of one K half from a wave's activation ring: row tile i
+// sits 2048 bytes after tile i-1 (the chunk swizzle depends only on the row
+// within its 16-row tile).  Read in inline assembly: the compiler cannot tell
+// which ring slot a direct-to-LDS copy fills and would otherwise wait for
+// every copy in flight before each read.  The caller's hand-counted vmcnt
+// wait covers the slot read here, and the block waits for its own reads, so
+// no output register is left in flight.
+template <int TM>
+__device__ __forceinline__ void read_a_frags(v4i (&af)[TM], const int8_t* p) {
+  const auto* lp = (const __attribute__((address_space(3))) int8_t*)p;
+  const uint32_t ad = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lp));
+  if constexpr (TM == 1) {
+    asm volatile("ds_read_b128 %0, %1\n s_waitcnt lgkmcnt(0)" : "=&v"(af[0]) : "v"(ad));
+  } else if constexpr (TM == 2) {
+    asm volatile("ds_read_b128 %0, %2\n ds_read_b128 %1, %2 offset:2048\n s_waitcnt lgkmcnt(0)"
+                 : "=&v"(af[0]), "=&v"(af[1])
+                 : "v"(ad));
+  } else {
+    static_assert(TM == 4, "row tiles per skinny block: 1, 2 or 4");
+    asm volatile(
+        "ds_read_b128 %0, %4\n ds_read_b128 %1, %4 offset:2048\n ds_read_b128 %2, %4 offset:4096\n"
+        " ds_read_b128 %3, %4 offset:6144\n s_waitcnt lgkmcnt(0)"
+        : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3])
+        : "v"(ad));
+  }
+}
+
+template <int TM, int TN, int KS, int PF, int WF, bool I32OUT>
 __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
-  static_assert(PF % AD == 0 && PF % 2 == 0, "the activation ring and the LDS ping-pong must tile the weight ring");
-  // LDS: while multiplying, each wave stages its own activations in two
-  // buffers of TM*16 rows x 128 B; afterwards the same memory holds the
-  // partial sums of every wave, [KS][TN][TM][64 lanes] records of 4 INT32.
-  constexpr int kStageBytes = 2 * TM * 16 * 128;
-  constexpr int kRedBytes = KS > 1 ? KS * TN * TM * 4 * 64 * 4 : 0;
-  constexpr int kSmemBytes = KS * kStageBytes > kRedBytes ? KS * kStageBytes : kRedBytes;
+  static_assert(KS == 4 || KS == 8, "K parts per skinny block: 4 or 8");
+  // LDS: while multiplying, wave w's activation ring (PF slots of TM*16 rows
+  // x 128 B); afterwards the partial sums, [KS/2 or KS][TN][TM][64 lanes]
+  // records of 4 INT32 (with 8 waves the upper four first hand theirs to the
+  // lower four), followed by the FP16 output tile [TM*16][TN*16].
+  constexpr int kSlot = TM * 16 * 128;
+  constexpr int kRingBytes = KS * PF * kSlot;
+  constexpr int kRedWaves = KS > 4 ? KS / 2 : KS;
+  constexpr int kRedBytes = kRedWaves * TN * TM * 1024;
+  constexpr int kTileCols = TN * 16;
+  constexpr int kTileBytes = I32OUT ? 0 : TM * 16 * kTileCols * 2;
+  constexpr int kSmemBytes = kRingBytes > kRedBytes + kTileBytes ? kRingBytes : kRedBytes + kTileBytes;
   __shared__ __align__(16) int8_t smem[kSmemBytes];
   // wave-uniform by construction; readfirstlane lets the compiler keep
   // everything derived from it (K range, group indices) in SGPRs
@@ -314,22 +361,18 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
     }
     __syncthreads();
   }
-  int8_t* stage = smem + wave * kStageBytes;
+  int8_t* ring = smem + wave * (PF * kSlot);
   const int c16 = lane & 15, j = lane >> 4;
   const int sbase = blockIdx.x * TN;
   const int m0 = blockIdx.y * TM * 16;
   const int64_t K = int64_t(a.G) * 128;
   const int g0 = (a.G * wave) / KS, g1 = (a.G * (wave + 1)) / KS;
 
-  int strip[TN];
-#pragma unroll
-  for (int t = 0; t < TN; ++t) strip[t] = min(sbase + t, a.n_strips - 1);
-
   constexpr int kVec = wf_vec(WF);
   uint32_t S[TN] = {}, C[TN] = {};
   if constexpr (WF == kWfPerChannel) {
 #pragma unroll
-    for (int t = 0; t < TN; ++t) meta_perchannel(a.meta8[strip[t] * 16 + c16], S[t], C[t]);
+    for (int t = 0; t < TN; ++t) meta_perchannel(a.meta8[min(sbase + t, a.n_strips - 1) * 16 + c16], S[t], C[t]);
   }
 
   v4i acc[TM][TN];
@@ -340,7 +383,6 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
 
   u32x4 bq[PF][TN][kVec];
   uint32_t mq[PF][TN];
-  u32x4 aq[AD][TM][2];
 
   // The block's strips are contiguous in the packed weights.  Every load's
   // per-lane offset is the same loop-invariant lane * 16; the group moves the
@@ -372,55 +414,40 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
       for (int t = 0; t < TN; ++t) m[t] = buf_load4s(mr, c16 * 4, min(t, nvalid - 1) * a.G4q * 64);
     }
   };
-  // Activations are read in whole 128-byte rows: one load covers 8 rows x one
-  // group (lane l: row l/8, chunk l%8), so every cache line it touches is
-  // used in full (loads in the MFMA operand layout would touch 16 half-used
-  // lines each).  The descriptor covers the block's valid rows; rows past M
-  // and groups past this wave's range read zeros without touching memory.
-  // As for the weights, the group moves the descriptor's base (a group past
-  // the range gets an empty descriptor); rows past M have a per-lane offset
-  // beyond the descriptor.
-  const int ar8 = lane >> 3, aq8 = lane & 7;
+  // Activations: copy (i, hh) of a group moves 8 whole 128-byte rows (every
+  // cache line it touches is used in full), lane l filling LDS row r = 16 i +
+  // 8 hh + l/8 at stored position l % 8, which holds the row's logical chunk
+  // (l % 8) ^ ((r >> 1) & 7): the swizzle of lds_off, so the MFMA-layout
+  // reads are conflict-free.  Rows past M read row M-1 (never stored); a
+  // group past the range gets an empty descriptor and touches no memory.
   const int8_t* xbase = a.x8 + int64_t(m0) * K;
   const int xbytes = int(min(TM * 16, a.M - m0) * K);
-  int arow[TM][2];
+  int aoff[TM][2];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const int rl = 16 * i + 8 * hh + ar8;
-      arow[i][hh] = m0 + rl < a.M ? int(rl * K) + 16 * aq8 : kDeadOffset;
+      const int r = 16 * i + 8 * hh + (lane >> 3);
+      const int kc = (lane & 7) ^ ((r >> 1) & 7);
+      aoff[i][hh] = (min(m0 + r, a.M - 1) - m0) * int(K) + kc * 16;
     }
-  auto load_a = [&](int g, u32x4 (&ar)[TM][2]) {
+  auto load_a = [&](int g, int slot) {
     const bool live = g < g1;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(xbase + (live ? g : 0) * 128, live ? xbytes : 0);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) ar[i][hh] = buf_load16<0>(xr, arow[i][hh]);
+      for (int hh = 0; hh < 2; ++hh) buf_load_lds16(xr, ring + slot * kSlot + (2 * i + hh) * 1024, aoff[i][hh], 0);
   };
-  // Into this wave's LDS buffer (chunk-XOR swizzled, conflict-free both
-  // ways), to be read back in the MFMA A layout: lane (c16, j) takes row c16
-  // of tile i, K chunk j (+4 for the second 64-wide step).  A wave reads only
-  // what it wrote, and LDS operations of one wave complete in order, so no
-  // barrier is involved.
-  auto stage_a = [&](const u32x4 (&ar)[TM][2], int buf) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-        *reinterpret_cast<u32x4*>(stage + buf * (TM * 16 * 128) + lds_off(16 * i + 8 * hh + ar8, aq8)) = ar[i][hh];
-  };
+  // vector-memory operations of one group (weights, metadata, activation
+  // copies); a wait down to kAhead outstanding leaves the last PF - 1 groups
+  // in flight (at most 63 can be counted)
+  constexpr int kLoads = TN * kVec + (wf_group_meta(WF) ? TN : 0) + 2 * TM;
+  constexpr int kAhead = (PF - 1) * kLoads < 63 ? (PF - 1) * kLoads : 63;
 
-  // Multiply group g: its activations come out of LDS buffer (g - g0) % 2,
-  // read here so that the fragments are live only while they are used.
-  auto compute = [&](int g, const u32x4 (&bc)[TN][kVec], const uint32_t (&mc)[TN]) {
-    v4i af[TM][2];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        af[i][h] = *reinterpret_cast<const v4i*>(stage + ((g - g0) & 1) * (TM * 16 * 128) + lds_off(16 * i + c16, j + 4 * h));
+  // Multiply group g from ring slot `slot`: per K half, the TM A fragments,
+  // then per strip the dequantized B operand feeding TM MFMAs.
+  auto compute = [&](int g, int slot, const u32x4 (&bc)[TN][kVec], const uint32_t (&mc)[TN]) {
     if constexpr (wf_group_meta(WF)) {
 #pragma unroll
       for (int t = 0; t < TN; ++t) {
@@ -431,129 +458,136 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      v4i af[TM];
+      read_a_frags<TM>(af, ring + slot * kSlot + lds_off(c16, j + 4 * h));
 #pragma unroll
       for (int t = 0; t < TN; ++t) {
         const v4i bf = b_op16<WF>(bc[t], h, S[t], C[t]);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) acc[i][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i][h], bf, acc[i][t], 0, 0, 0);
+        for (int i = 0; i < TM; ++i) acc[i][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf, acc[i][t], 0, 0, 0);
       }
     }
   };
-
-  // Epilogue scales, loaded once the prologue's loads are in flight so that
-  // their latency hides behind the main loop (global loads retire in order,
-  // so no wait of the loop is held up by them): row scales of the lane's
-  // rows and column scales of the strips this wave stores.
-  // The raw FP16 bits are kept (addresses clamped into range, so there is no
-  // select on the loaded values) and converted only in the epilogue.
-  constexpr int kScN = KS > 1 ? (TN + KS - 1) / KS : TN;
-  unsigned short sxh[TM][4] = {}, sch[kScN] = {};
-  auto load_scales = [&]() {
-    if constexpr (!I32OUT) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sxh[i][r] = a.sx[min(m0 + i * 16 + 4 * j + r, a.M - 1)];
-#pragma unroll
-      for (int u = 0; u < kScN; ++u) {
-        const int t = min(KS > 1 ? wave + u * KS : u, TN - 1);
-        sch[u] = a.scale[min((sbase + t) * 16 + c16, a.N - 1)];
-      }
-    }
-  };
-  auto fp16 = [](unsigned short h) { return __half2float(__ushort_as_half(h)); };
 
   const int ng = g1 - g0;
-  if (ng <= 0) load_scales();
   if (ng > 0) {
-    // prologue: activations of the first AD groups, then weights of the first
-    // PF (loads retire in order: the first multiply waits only for what was
-    // issued before its operands); group g0 goes into LDS right away.
 #pragma unroll
-    for (int p = 0; p < AD; ++p) load_a(g0 + p, aq[p]);
-#pragma unroll
-    for (int p = 0; p < PF; ++p) load_b(g0 + p, bq[p], mq[p]);
-    stage_a(aq[0], 0);
-    load_a(g0 + AD, aq[0]);
-    QOQ_COMPILER_FENCE();
-    load_scales();
-
-    // full rounds of PF groups.  Loads are unconditional (past the range they
-    // read zeros for free) so a round is straight-line code.  Step l: multiply
-    // group g0+l (weights from ring slot l % PF, activations already in
-    // registers from LDS buffer l % 2); then pass group l+1 through the other
-    // LDS buffer and refill both rings, the weights PF groups ahead and the
-    // activations AD + 1 ahead.  Loads retire in issue order, so the
-    // activation lookahead also bounds how far ahead the weights effectively
-    // run.
-    int it = 0;
-    for (; it + PF <= ng; it += PF) {
+    for (int p = 0; p < PF; ++p) {
+      load_b(g0 + p, bq[p], mq[p]);
+      load_a(g0 + p, p);
+    }
+    // Rounds of PF groups; ring slot u holds group g0 + it + u.  Step u waits
+    // until the operands of its group have landed (everything issued before
+    // the last PF - 1 groups' loads), multiplies it, and refills the slot with
+    // the group PF ahead.  Past the range the loads are empty and free.  The
+    // refill follows the slot's last read: the fragments were consumed by the
+    // MFMAs before the fence.
+    for (int it = 0; it < ng; it += PF) {
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
         const int g = g0 + it + u;
-        compute(g, bq[u], mq[u]);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kAhead));
         QOQ_COMPILER_FENCE();
-        stage_a(aq[(u + 1) % AD], (u + 1) & 1);
+        if (g < g1) compute(g, u, bq[u], mq[u]);
+        QOQ_COMPILER_FENCE();
         load_b(g + PF, bq[u], mq[u]);
-        load_a(g + 1 + AD, aq[(u + 1) % AD]);
+        load_a(g + PF, u);
         QOQ_COMPILER_FENCE();
-      }
-    }
-    // remaining ng % PF groups: weights are in bq[0 .. rem), the activations
-    // of the next ones in the activation ring
-    const int rem = ng - it;
-#pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      if (u < rem) {
-        const int g = g0 + it + u;
-        compute(g, bq[u], mq[u]);
-        if (u + 1 < rem) {
-          stage_a(aq[(u + 1) % AD], (u + 1) & 1);
-          if (u + 1 + AD < rem) load_a(g + 1 + AD, aq[(u + 1) % AD]);
-        }
       }
     }
   }
+  // the trailing (empty) copies land before the LDS is reused
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
-  // Exact cross-wave reduction of the K-split partial sums, and the epilogue.
-  // Once every wave is done with its activation buffers, every wave parks its
-  // partials in the same LDS; after a second barrier wave w sums and stores
-  // strips w, w+KS, ... (lane holds rows 4*(lane/16)+r of each 16x16
-  // tile, column lane%16).  The scales were loaded before the main loop.
-  if constexpr (KS > 1) {
-    __syncthreads();  // every wave is done with its activation buffers
-    // [wave][strip][row tile][lane] 16-byte records: one 128-bit LDS write
-    // per accumulator tile and one 128-bit read per partial
-    v4i* red4 = reinterpret_cast<v4i*>(smem);
+  // Epilogue scales, fetched now so that their latency overlaps the
+  // reduction (held through the loop they would cost registers): row scales
+  // of the lane's rows and column scales of the strips this wave stores.
+  // The raw FP16 bits are kept (addresses clamped into range) and converted
+  // where they are used.
+  constexpr int kScN = (TN + KS - 1) / KS;
+  unsigned short sxh[TM][4] = {}, sch[kScN] = {};
+  if constexpr (!I32OUT) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sxh[i][r] = a.sx[min(m0 + i * 16 + 4 * j + r, a.M - 1)];
+#pragma unroll
+    for (int u = 0; u < kScN; ++u) sch[u] = a.scale[min((sbase + min(wave + u * KS, TN - 1)) * 16 + c16, a.N - 1)];
+  }
+  auto fp16 = [](unsigned short h) { return __half2float(__ushort_as_half(h)); };
+
+  // Exact cross-wave reduction of the K-part sums ([wave][strip][row tile]
+  // [lane] 16-byte records: one 128-bit LDS access per accumulator tile),
+  // then wave w finishes strips w, w+KS, ... (lane holds rows 4*(lane/16)+r
+  // of each 16x16 tile, column lane%16).
+  __syncthreads();  // every wave is done with its ring
+  v4i* red4 = reinterpret_cast<v4i*>(smem);
+  if constexpr (KS > kRedWaves) {
+    if (wave >= kRedWaves) {
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+#pragma unroll
+        for (int i = 0; i < TM; ++i) red4[(((wave - kRedWaves) * TN + t) * TM + i) * 64 + lane] = acc[i][t];
+    }
+    __syncthreads();
+    if (wave < kRedWaves) {
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+#pragma unroll
+        for (int i = 0; i < TM; ++i) acc[i][t] += red4[((wave * TN + t) * TM + i) * 64 + lane];
+    }
+    __syncthreads();
+  }
+  if (wave < kRedWaves) {
 #pragma unroll
     for (int t = 0; t < TN; ++t)
 #pragma unroll
       for (int i = 0; i < TM; ++i) red4[((wave * TN + t) * TM + i) * 64 + lane] = acc[i][t];
-    __syncthreads();
+  }
+  __syncthreads();
+  __half* tile = reinterpret_cast<__half*>(smem + kRedBytes);
 #pragma unroll
-    for (int u = 0; u < (TN + KS - 1) / KS; ++u) {
-      const int t = wave + u * KS;
-      if (t < TN && sbase + t < a.n_strips) {
+  for (int u = 0; u < kScN; ++u) {
+    const int t = wave + u * KS;
+    if (t < TN && sbase + t < a.n_strips) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          v4i v = red4[(t * TM + i) * 64 + lane];
+      for (int i = 0; i < TM; ++i) {
+        v4i v = red4[(t * TM + i) * 64 + lane];
 #pragma unroll
-          for (int w = 1; w < KS; ++w) v += red4[((w * TN + t) * TM + i) * 64 + lane];
+        for (int w = 1; w < kRedWaves; ++w) v += red4[((w * TN + t) * TM + i) * 64 + lane];
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            store_out<I32OUT>(a, m0 + i * 16 + 4 * j + r, (sbase + t) * 16 + c16, v[r], fp16(sxh[i][r]), fp16(sch[u]));
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (I32OUT) {
+            store_out<true>(a, m0 + i * 16 + 4 * j + r, (sbase + t) * 16 + c16, v[r], 0.0f, 0.0f);
+          } else {
+            const float y = static_cast<float>(v[r]) * fp16(sxh[i][r]) * fp16(sch[u]);
+            tile[(i * 16 + 4 * j + r) * kTileCols + t * 16 + c16] = __float2half_rn(y);
+          }
         }
       }
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int t = 0; t < TN; ++t)
-          if (sbase + t < a.n_strips)
-            store_out<I32OUT>(a, m0 + i * 16 + 4 * j + r, (sbase + t) * 16 + c16, acc[i][t][r], fp16(sxh[i][r]), fp16(sch[t]));
+  }
+  if constexpr (!I32OUT) {
+    // the block's FP16 rows, 16 bytes at a time where the output rows are
+    // 16-byte aligned (element by element otherwise and at a ragged end)
+    __syncthreads();
+    const int rows = min(TM * 16, a.M - m0);
+    const int col0 = sbase * 16;
+    const int cols = min(kTileCols, a.N - col0);
+    const bool vec = ((reinterpret_cast<uintptr_t>(a.out) | uintptr_t(a.ldo * 2)) & 15) == 0;
+    constexpr int kSeg = kTileCols / 8;
+    for (int e = threadIdx.x; e < TM * 16 * kSeg; e += 64 * KS) {
+      const int row = e / kSeg, c = (e - row * kSeg) * 8;
+      if (row < rows && c < cols) {
+        __half* dst = static_cast<__half*>(a.out) + int64_t(m0 + row) * a.ldo + col0 + c;
+        const __half* src = tile + row * kTileCols + c;
+        if (vec && c + 8 <= cols) {
+          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+        } else {
+          for (int q = 0; q < 8 && c + q < cols; ++q) dst[q] = src[q];
+        }
+      }
+    }
   }
 }
 
@@ -575,9 +609,6 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
 __device__ __forceinline__ int round_up_lds(int bytes) { return (bytes + 1023) & ~1023; }
 __device__ __forceinline__ int strip_lds_off(int lrow, int q) { return lrow * 128 + ((q ^ ((lrow >> 1) & 7)) << 4); }
 
-// s_waitcnt immediates (gfx9 encoding): wait until at most n vector-memory
-// operations of this wave are outstanding, leaving the other counters free.
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <int PF, int WF, bool I32OUT>
 __global__ __launch_bounds__(512) void gemm_strip_kernel(GemmArgs a, int spb, int ks) {
@@ -732,11 +763,6 @@ struct ATile {
   static_assert(kChunks % THREADS == 0, "A tile must split evenly over the block");
 };
 
-// Direct global -> LDS copy of 16 bytes per lane: lane i writes lds + 16 i.
-// (Kept in a device function: the builtin is not meaningful to the host pass.)
-__device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, int8_t* lds, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
-}
 
 // Barrier for LDS traffic only: this wave's LDS operations are complete
 // (lgkmcnt 0) and every wave has arrived.  Global loads stay in flight.
@@ -1100,22 +1126,25 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const int* __restric
 // there are too few strips to give every CU several waves.  For 32 or 64 rows
 // the activation operand is larger than the weights it multiplies, so a wave
 // covers TN strips with one activation load and the K range is split over 4
-// waves.
+// or 8 waves.
 #ifndef QOQ_S1PF
 #define QOQ_S1PF 4
 #endif
-#ifndef QOQ_SKS4
-#define QOQ_SKS4 4
-#endif
-#ifndef QOQ_SPF
-#define QOQ_SPF 4
-#endif
 constexpr int kStripWavesTarget = 1024;  // 4 waves per CU
 
-template <int TM, int TN, int KS, int PF, int AD, int WF, bool I32>
+// K parts (waves) per skinny block: 8 for the UINT4 formats when every part
+// keeps at least 8 groups, else 4 (INT8 weights need twice the registers per
+// group in flight, which two waves per SIMD cannot hold).  Ring depth: 2
+// groups with 8 waves, 4 with 4 (2 for INT8 blocks, twice as large): the same
+// bytes in flight per SIMD.
+constexpr int kSkinnyKs8MinGroups = 64;
+constexpr int skinny_ks(bool uint4, int G) { return uint4 && G >= kSkinnyKs8MinGroups ? 8 : 4; }
+constexpr int skinny_pf(int wf, int ks) { return ks == 8 ? 2 : 4 / wf_vec(wf); }
+
+template <int TM, int TN, int KS, int WF, bool I32>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
   const dim3 grid((a.n_strips + TN - 1) / TN, (a.M + TM * 16 - 1) / (TM * 16));
-  hipLaunchKernelGGL((gemm_skinny_kernel<TM, TN, KS, PF, AD, WF, I32>), grid, dim3(64 * KS), 0, st, a);
+  hipLaunchKernelGGL((gemm_skinny_kernel<TM, TN, KS, skinny_pf(WF, KS), WF, I32>), grid, dim3(64 * KS), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1159,23 +1188,20 @@ inline int pick_skinny_tn_rows(int n_strips, int ny, int hi) {
   return best;
 }
 
-#ifndef QOQ_SAD
-#define QOQ_SAD 2
-#endif
 // Most strips per skinny block: 8, or 7 with 64-row tiles (eight would not
 // fit the register file beside four row tiles of accumulators).
 constexpr int skinny_tn_max(int tm) { return tm >= 4 ? 7 : 8; }
-// Weight-ring depth of the skinny kernel: the same bytes in flight for every
-// format (INT8 blocks are twice as large, so half as many groups).
-constexpr int skinny_pf(int wf) { return QOQ_SPF / wf_vec(wf); }
 
-// launch_skinny with TN = tn, instantiated for 1 <= TN <= T only
+// launch_skinny with TN = tn and KS = ks, instantiated for 1 <= TN <= T only
 template <int TM, int WF, bool I32, int T>
-hipError_t launch_skinny_upto(int tn, const GemmArgs& a, hipStream_t st) {
+hipError_t launch_skinny_upto(int tn, int ks, const GemmArgs& a, hipStream_t st) {
   if constexpr (T > 1) {
-    if (tn < T) return launch_skinny_upto<TM, WF, I32, T - 1>(tn, a, st);
+    if (tn < T) return launch_skinny_upto<TM, WF, I32, T - 1>(tn, ks, a, st);
   }
-  return launch_skinny<TM, T, QOQ_SKS4, skinny_pf(WF), QOQ_SAD, WF, I32>(a, st);
+  if constexpr (WF != kWfW8) {
+    if (ks == 8) return launch_skinny<TM, T, 8, WF, I32>(a, st);
+  }
+  return launch_skinny<TM, T, 4, WF, I32>(a, st);
 }
 
 // Dynamic LDS of the strip kernel: the activations, or the K-part partial
@@ -1276,25 +1302,27 @@ inline bool skinny_mid(int64_t M, int64_t N) {
 
 // The launch plan of one GEMM call.  kernel: the kernel family; tile: strips
 // per block (strip and skinny kernels) or the large-M tile (0 big, 1 small,
-// 2 K-set); ksplit: K parts per block (strip kernel) or K splits across
-// blocks (large kernel).
+// 2 K-set); ksplit: K parts per block (strip and skinny kernels) or K splits
+// across blocks (large kernel).
 enum GemmKernel { kPlanStrip = 0, kPlanSkinny16 = 1, kPlanSkinny32 = 2, kPlanSkinny64 = 3, kPlanLarge = 4 };
 struct GemmPlan {
   int kernel, tile, ksplit;
 };
 
-inline GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool group_meta) {
+// group_meta: per-group metadata (g128); uint4: UINT4 weights (else INT8).
+inline GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool group_meta, bool uint4 = true) {
   const int n_strips = int(round_up(N, kStrip) / kStrip);
   const int G = int(K / kGroup);
+  const int ks = skinny_ks(uint4, G);
   if (M <= 16) {
-    int spb, ks;
+    int spb, sks;
     size_t lds;
-    if (plan_strip(M, n_strips, G, group_meta, &spb, &ks, &lds)) return {kPlanStrip, spb, ks};
-    return {kPlanSkinny16, pick_skinny_tn(n_strips, int((M + 15) / 16), skinny_tn_max(1)), 1};
+    if (plan_strip(M, n_strips, G, group_meta, &spb, &sks, &lds)) return {kPlanStrip, spb, sks};
+    return {kPlanSkinny16, pick_skinny_tn(n_strips, int((M + 15) / 16), skinny_tn_max(1)), ks};
   }
-  if (M <= 32) return {kPlanSkinny32, pick_skinny_tn(n_strips, int((M + 31) / 32), skinny_tn_max(2)), 1};
+  if (M <= 32) return {kPlanSkinny32, pick_skinny_tn(n_strips, int((M + 31) / 32), skinny_tn_max(2)), ks};
   if (M <= kSkinnyMaxM || skinny_mid(M, N))
-    return {kPlanSkinny64, pick_skinny_tn_rows(n_strips, int((M + 63) / 64), skinny_tn_max(4)), 1};
+    return {kPlanSkinny64, pick_skinny_tn_rows(n_strips, int((M + 63) / 64), skinny_tn_max(4)), ks};
   const LargePlan p = plan_large(M, N, K);
   return {kPlanLarge, p.tile, p.ksplit};
 }
@@ -1330,15 +1358,15 @@ hipError_t launch_large_tile(int tile, const GemmArgs& a, hipStream_t st) {
 
 template <int WF, bool I32>
 hipError_t dispatch(const GemmArgs& a0, void* ws, hipStream_t st) {
-  const GemmPlan p = plan_gemm(a0.M, a0.N, int64_t(a0.G) * kGroup, wf_group_meta(WF));
+  const GemmPlan p = plan_gemm(a0.M, a0.N, int64_t(a0.G) * kGroup, wf_group_meta(WF), WF != kWfW8);
   switch (p.kernel) {
     case kPlanStrip: {
       const size_t lds = strip_lds_bytes(a0.G, a0.M < 16 ? a0.M : 16, p.tile, p.ksplit, wf_group_meta(WF));
       return launch_strip<WF, I32>(a0, p.tile, p.ksplit, lds, st);
     }
-    case kPlanSkinny16: return launch_skinny_upto<1, WF, I32, skinny_tn_max(1)>(p.tile, a0, st);
-    case kPlanSkinny32: return launch_skinny_upto<2, WF, I32, skinny_tn_max(2)>(p.tile, a0, st);
-    case kPlanSkinny64: return launch_skinny_upto<4, WF, I32, skinny_tn_max(4)>(p.tile, a0, st);
+    case kPlanSkinny16: return launch_skinny_upto<1, WF, I32, skinny_tn_max(1)>(p.tile, p.ksplit, a0, st);
+    case kPlanSkinny32: return launch_skinny_upto<2, WF, I32, skinny_tn_max(2)>(p.tile, p.ksplit, a0, st);
+    case kPlanSkinny64: return launch_skinny_upto<4, WF, I32, skinny_tn_max(4)>(p.tile, p.ksplit, a0, st);
     default: break;
   }
   if (p.ksplit == 1) return launch_large_tile<WF, I32>(p.tile, a0, st);
