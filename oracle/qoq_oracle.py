@@ -66,6 +66,9 @@ __all__ = [
     "dequant_level1_saturating",
     "rmsnorm_fp16",
     "rmsnorm_quant_per_token",
+    "silu_fp16",
+    "swiglu_fp16",
+    "swiglu_quant_per_token",
     "kv4_quant_per_head",
     "kv4_dequant",
     "kv4_decode_attention",
@@ -428,6 +431,54 @@ def rmsnorm_quant_per_token(X, gamma, eps):
     Returns (x8 int8 [M,K], s_x float16 [M]).
     """
     return quant_act_per_token(rmsnorm_fp16(X, gamma, eps))
+
+
+def silu_fp16(G):
+    """SiLU of FP16 values, rounded once to FP16.
+
+    [PL §5, runtime and precision mapping]: activation quantization also runs
+    inside the activation-function kernel that produces a layer's input.  In
+    the Llama-family FFN the down projection's input is SiLU(gate) * up.  The
+    pages give no arithmetic for it; the reading taken here rounds each FP16
+    step once:  silu(g) = g / (1 + e^-g)  evaluated in FP64 and rounded to
+    FP16.  For every finite FP16 g the exact value lies at least 4.8e-12
+    (relative) from the nearest FP16 rounding boundary, far beyond the FP64
+    evaluation's error, so the result is the correctly rounded FP16 value
+    (checked against 60-digit decimal arithmetic in the tests).
+
+    Returns float16, the shape of G.
+    """
+    g = np.asarray(G, dtype=np.float16).astype(np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        s = g / (1.0 + np.exp(-g))
+    return fp16_rne(s)
+
+
+def swiglu_fp16(G, U):
+    """h = fp16(silu_fp16(g) * u): the product of two FP16 values is exact in
+    FP64 and is rounded once to FP16 (round half to even).
+
+    Returns float16 [M, K].
+    """
+    s = silu_fp16(G).astype(np.float64)
+    u = np.asarray(U, dtype=np.float16).astype(np.float64)
+    if s.shape != u.shape:
+        raise ValueError("gate and up must have the same shape")
+    return fp16_rne(s * u)
+
+
+def swiglu_quant_per_token(G, U):
+    """Fused producer of the down projection's input: h = SiLU(gate) * up
+    (``swiglu_fp16``), then the per-token INT8 quantization of those FP16
+    values (``quant_act_per_token``).  The activations must stay finite.
+
+    Returns (x8 int8 [M,K], s_x float16 [M], h float16 [M,K]).
+    """
+    h = swiglu_fp16(G, U)
+    if not np.all(np.isfinite(h)):
+        raise ValueError("SiLU(gate) * up overflows FP16")
+    x8, s_x = quant_act_per_token(h)
+    return x8, s_x, h
 
 
 # ------------------------------------------------------------------ KV4 (f3)

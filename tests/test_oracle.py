@@ -6,6 +6,9 @@ index, the wrong rounding mode, a transposed operand).
 CPU only.
 """
 
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
 import numpy as np
 import pytest
 
@@ -428,6 +431,85 @@ def test_rmsnorm_zero_row_and_bad_args():
         O.rmsnorm_fp16(X, np.ones(128, np.float16), 0.0)
     with pytest.raises(ValueError):
         O.rmsnorm_fp16(X, np.ones(64, np.float16), 1e-5)
+
+
+def _fp16_nearest_exact(val, candidates):
+    """The FP16 value among candidates nearest to the exact value val
+    (a Decimal or a Fraction), ties to the even mantissa."""
+    v = Fraction(val)
+    return min(candidates, key=lambda c: (abs(Fraction(float(c)) - v), int(np.array(c, np.float16).view(np.uint16)) & 1))
+
+
+def _fp16_neighbours(x):
+    c = np.float16(x)
+    with np.errstate(over="ignore"):
+        cands = [c, np.nextafter(c, np.float16(np.inf)), np.nextafter(c, np.float16(-np.inf))]
+    return [v for v in cands if np.isfinite(v)]
+
+
+def test_silu_fp16_every_finite_half_against_decimal():
+    # silu(g) = g / (1 + e^-g) to 50 significant digits (Decimal's exp is
+    # correctly rounded), then the nearest FP16: must equal the oracle's
+    # FP64 evaluation for every finite FP16 input
+    getcontext().prec = 50
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    g = bits.view(np.float16)
+    g = g[np.isfinite(g)]
+    got = O.silu_fp16(g)
+    bad = 0
+    for gv, out in zip(g.tolist(), got.tolist()):
+        d = Decimal(gv)
+        if d < -200:      # |silu| < 2^-200: rounds to -0 (the oracle's e^-g overflows to inf)
+            want = -0.0
+        else:
+            ex = Decimal(float(d)).__neg__().exp()
+            val = d / (1 + ex)
+            want = float(_fp16_nearest_exact(val, _fp16_neighbours(float(val))))
+            if want == 0:
+                want = -0.0 if val < 0 or d.is_signed() else 0.0
+        bad += np.float16(want).view(np.uint16) != np.float16(out).view(np.uint16)
+    assert bad == 0
+    # sign and size: 0 <= silu(g) <= g above zero, g <= silu(g) <= 0 below
+    g64, s64 = g.astype(np.float64), got.astype(np.float64)
+    assert np.all((s64 >= np.minimum(g64, 0)) & (s64 <= np.maximum(g64, 0)))
+
+
+def test_swiglu_product_rounds_once_half_to_even():
+    # h = fp16(s * u) with s = silu_fp16(g): against exact rational products
+    rng = np.random.default_rng(8)
+    G = rng.standard_normal(4000).astype(np.float16) * np.float16(3)
+    U = (rng.standard_normal(4000) * 7).astype(np.float16)
+    h = O.swiglu_fp16(G, U)
+    s = O.silu_fp16(G)
+    for sv, uv, hv in zip(s.tolist(), U.tolist(), h.tolist()):
+        exact = Fraction(sv) * Fraction(uv)
+        assert hv == float(_fp16_nearest_exact(exact, _fp16_neighbours(float(exact))))
+
+
+def test_swiglu_quant_hand_worked_rows():
+    fx = read_fixture("swiglu_rows.txt")
+    for r in range(2):
+        G = np.array([fx[f"g{r}"]], np.float16)
+        U = np.array([fx[f"u{r}"]], np.float16)
+        x8, sx, h = O.swiglu_quant_per_token(G, U)
+        assert h[0].astype(np.float64).tolist() == fx[f"h{r}"]
+        assert float(sx[0]) == fx[f"s{r}"][0]
+        assert x8[0].tolist() == [int(v) for v in fx[f"q{r}"]]
+    with pytest.raises(ValueError):   # 300 * 300 overflows FP16
+        O.swiglu_quant_per_token(np.full((1, 4), 300, np.float16), np.full((1, 4), 300, np.float16))
+
+
+def test_swiglu_with_large_gate_reduces_to_plain_quantizer_of_up_times_gate():
+    # for g >= 24 (an FP16 value), silu(g) rounds to g itself (g e^-g is far
+    # below half an ulp), so h = fp16(g * u) and the fused producer equals
+    # the plain quantizer of that product
+    rng = np.random.default_rng(5)
+    G = np.full((3, 256), 32.0, np.float16)
+    U = rng.standard_normal((3, 256)).astype(np.float16)
+    assert np.array_equal(O.silu_fp16(G), G)
+    x8, sx, h = O.swiglu_quant_per_token(G, U)
+    ref8, refs = O.quant_act_per_token((G.astype(np.float64) * U.astype(np.float64)).astype(np.float16))
+    assert np.array_equal(x8, ref8) and np.array_equal(sx, refs)
 
 
 # ------------------------------------------------------------------ KV4 (f3)
