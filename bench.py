@@ -64,6 +64,12 @@ def producer_bytes(w) -> int:
     return 2 * w.M * w.K + 2 * w.K + w.M * w.K + 2 * w.M
 
 
+def swiglu_bytes(w) -> int:
+    """Fused SiLU(gate) * up + quantization: two FP16 [M, K] inputs in, INT8
+    rows and FP16 scales out."""
+    return 4 * w.M * w.K + w.M * w.K + 2 * w.M
+
+
 def bound_of(w) -> str:
     t_hbm = algo_bytes(w) / (PEAK_HBM_GBS * 1e9)
     t_mfma = w.ops / (PEAK_INT8_TOPS * 1e12)
@@ -335,6 +341,9 @@ def measure_gemm(torch, q, w, X, W, reps: int, comparators: bool = False):
     t_q = time_kernel(torch, lambda i: q.qoq_quant_act_per_token(x, x8, sx), reps)
     gamma = torch.from_numpy(synthetic_gamma(w.K)).to(dev)
     t_n = time_kernel(torch, lambda i: q.qoq_rmsnorm_quant_per_token(x, gamma, 1e-5, x8, sx), reps)
+    up = torch.flip(x, dims=(1,)).contiguous()   # a second FP16 operand of the same shape
+    t_s = time_kernel(torch, lambda i: q.qoq_swiglu_quant_per_token(x, up, x8, sx), reps)
+    del up
     t_g = time_kernel(torch, lambda i: q.qoq_w4a8_gemm(x8, sx, ws[i % copies], y=y), reps)
     b = algo_bytes(w)
     bnd = bound_of(w)
@@ -346,7 +355,8 @@ def measure_gemm(torch, q, w, X, W, reps: int, comparators: bool = False):
          "frac": round(frac, 4), "traffic": stored_traffic(w.name), "weight_copies": copies,
          "act_quant_us": round(t_q, 3),
          "act_quant_gbs": round(act_bytes(w) / t_q / 1e3, 1),
-         "rmsnorm_quant_us": round(t_n, 3), "rmsnorm_quant_gbs": round(producer_bytes(w) / t_n / 1e3, 1)}
+         "rmsnorm_quant_us": round(t_n, 3), "rmsnorm_quant_gbs": round(producer_bytes(w) / t_n / 1e3, 1),
+         "swiglu_quant_us": round(t_s, 3), "swiglu_quant_gbs": round(swiglu_bytes(w) / t_s / 1e3, 1)}
     if comparators:
         r.update(measure_comparators(torch, q, w, W, x8, sx, y, ws, t_g, reps))
     del ws

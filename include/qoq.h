@@ -189,6 +189,27 @@ QOQ_API int qoq_quant_act_per_token(const void* x_fp16, int64_t M, int64_t K, in
 QOQ_API int qoq_rmsnorm_quant_per_token(const void* x_fp16, const void* gamma_fp16, float eps, int64_t M, int64_t K,
                                 int64_t ldx, int8_t* x8, void* sx_fp16, void* stream);
 
+/*
+ * Fused producer (device) of a gated FFN's down-projection input: h = SiLU(gate)
+ * * up per element, then the per-token INT8 quantization of h, in one kernel
+ * that reads gate and up once and writes x8 and s_x (and h if asked).  [PL §5,
+ * runtime and precision mapping: the quantizer also runs inside the
+ * activation-function kernel that produces a layer's input].  Per element,
+ * each step rounded once (round half to even):
+ *   s = fp16(g / (1 + e^-g))  (the correctly rounded FP16 SiLU),
+ *   h = fp16(s * u)           (the product of two halves is exact in FP32),
+ * then s_x[m] and x8[m,:] from the row of h exactly as qoq_quant_act_per_token.
+ * gate_fp16, up_fp16: device [M][ldg] and [M][ldu] FP16 (ldg, ldu >= K; the
+ * two halves of a fused gate-up output are gate = base, up = base + K with
+ * ldg = ldu = 2K).  x8: device [M][K] int8.  sx_fp16: device [M].  h_fp16:
+ * device [M][ldh] FP16 (ldh >= K) that receives h, or NULL.  Vector path when
+ * K and the leading dimensions are multiples of 8 and the FP16 pointers are
+ * 16-byte aligned (else a scalar path).  Non-finite inputs or an FP16
+ * overflow of h are undefined behaviour.
+ */
+QOQ_API int qoq_swiglu_quant_per_token(const void* gate_fp16, const void* up_fp16, int64_t M, int64_t K, int64_t ldg,
+                               int64_t ldu, int8_t* x8, void* sx_fp16, void* h_fp16, int64_t ldh, void* stream);
+
 /* Device workspace (bytes) qoq_w4a8_gemm / qoq_w4a8_gemm_i32 need for this
  * shape; 0 means the workspace arguments may be NULL / 0. */
 QOQ_API size_t qoq_w4a8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_size);

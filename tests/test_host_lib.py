@@ -26,7 +26,7 @@ def header_symbols():
 def test_library_exports_every_header_symbol():
     lib = q.load_library()
     syms = header_symbols()
-    assert len(syms) == 27, syms
+    assert len(syms) == 28, syms
     assert sorted(_native.EXPORTS) == syms
     for s in syms:
         assert hasattr(lib, s), s

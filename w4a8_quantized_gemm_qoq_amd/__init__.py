@@ -23,6 +23,7 @@ from ._native import (  # noqa: F401
     qoq_rmsnorm_quant_per_token,
     qoq_scale_columns,
     qoq_smoothing_factors,
+    qoq_swiglu_quant_per_token,
     qoq_unpack_weights,
     qoq_w4a8_forward,
     qoq_w4a8_gemm,

@@ -28,6 +28,7 @@ EXPORTS = [
     "qoq_unpack_weights",
     "qoq_quant_act_per_token",
     "qoq_rmsnorm_quant_per_token",
+    "qoq_swiglu_quant_per_token",
     "qoq_w4a8_gemm_workspace_size",
     "qoq_w4a8_gemm",
     "qoq_w4a8_gemm_i32",
@@ -110,6 +111,7 @@ def load_library():
         "qoq_unpack_weights": (ctypes.c_int, [vp, vp, vp, i64, i64, i32, vp, vp, vp, vp]),
         "qoq_quant_act_per_token": (ctypes.c_int, [vp, i64, i64, i64, vp, vp, vp]),
         "qoq_rmsnorm_quant_per_token": (ctypes.c_int, [vp, vp, ctypes.c_float, i64, i64, i64, vp, vp, vp]),
+        "qoq_swiglu_quant_per_token": (ctypes.c_int, [vp, vp, i64, i64, i64, i64, vp, vp, vp, i64, vp]),
         "qoq_w4a8_gemm_workspace_size": (sz, [i64, i64, i64, i32]),
         "qoq_w4a8_gemm": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]),
         "qoq_w4a8_gemm_i32": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]),
@@ -292,6 +294,41 @@ def qoq_rmsnorm_quant_per_token(x, gamma, eps: float, x8=None, sx=None, stream=N
     _check(lib.qoq_rmsnorm_quant_per_token(_t_ptr(x), _t_ptr(gamma), float(eps), M, K, x.stride(0), _t_ptr(x8),
                                            _t_ptr(sx), _stream(stream)), "qoq_rmsnorm_quant_per_token")
     return x8, sx
+
+
+def qoq_swiglu_quant_per_token(gate, up, x8=None, sx=None, h=None, want_h=False, stream=None):
+    """Fused SiLU(gate) * up + per-token INT8 quantization on the GPU.
+
+    gate and up: FP16 [M, K] with unit column stride (row strides may exceed
+    K, e.g. the two halves of one [M, 2K] gate-up output).  Returns (x8, sx),
+    or (x8, sx, h) with the FP16 activations when want_h or h is given."""
+    import torch
+    _require_cuda(gate, up)
+    for name, t in (("gate", gate), ("up", up)):
+        if t.dtype != torch.float16 or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{name} must be a 2-D FP16 tensor with unit column stride")
+    if gate.shape != up.shape:
+        raise ValueError("gate and up must have the same shape")
+    M, K = gate.shape
+    if x8 is None:
+        x8 = torch.empty((M, K), dtype=torch.int8, device=gate.device)
+    if sx is None:
+        sx = torch.empty((M,), dtype=torch.float16, device=gate.device)
+    if h is None and want_h:
+        h = torch.empty((M, K), dtype=torch.float16, device=gate.device)
+    _require_cuda(x8, sx, h)
+    if not (x8.is_contiguous() and x8.shape == (M, K) and x8.dtype == torch.int8):
+        raise ValueError("x8 must be a contiguous int8 [M, K] tensor")
+    if not (sx.is_contiguous() and sx.numel() == M and sx.dtype == torch.float16):
+        raise ValueError("sx must be a contiguous float16 [M] tensor")
+    if h is not None and not (h.dtype == torch.float16 and h.shape == (M, K) and h.stride(1) == 1):
+        raise ValueError("h must be a float16 [M, K] tensor with unit column stride")
+    lib = load_library()
+    _check(lib.qoq_swiglu_quant_per_token(_t_ptr(gate), _t_ptr(up), M, K, gate.stride(0), up.stride(0), _t_ptr(x8),
+                                          _t_ptr(sx), _t_ptr(h),
+                                          h.stride(0) if h is not None else 0, _stream(stream)),
+           "qoq_swiglu_quant_per_token")
+    return (x8, sx, h) if h is not None else (x8, sx)
 
 
 def _check_gemm_inputs(x8, w: PackedWeight):

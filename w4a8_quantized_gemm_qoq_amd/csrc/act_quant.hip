@@ -410,6 +410,142 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_scalar_kernel(const un
     x8[m * K + k] = s != 0.0f ? static_cast<int8_t>(quant1(norm1(row[k], gamma[k], r), s, y)) : int8_t(0);
 }
 
+// ---------------------------------------------------------------------------
+// Fused producer of the down projection's input: h = SiLU(gate) * up, then the
+// per-token quantization above ("QServe: W4A8KV4 Quantization and System
+// Co-design for Efficient LLM Serving", paperlayer.ai summary, §5 runtime and
+// precision mapping: the quantizer also runs inside the activation-function
+// kernel that produces a layer's input).  Per element, each step rounded once:
+//   s = fp16(g / (1 + e^-g))   the correctly rounded FP16 SiLU
+//   h = fp16(s * u)            the product of two halves is exact in FP32
+// then s_x and x8 from the row of h as for the plain quantizer.  Inputs must
+// be finite and their products must not overflow FP16.
+
+// FP16 SiLU, correctly rounded.  Evaluated in FP32 (e^-g by the library's
+// expf, one hardware reciprocal: within a few ulps).  Where that value lies
+// within 8 FP32 ulps of an FP16 rounding boundary (its 13 bits below the FP16
+// precision within 8 of one half; about 0.2% of inputs), or in the FP16
+// subnormal range, the side of the boundary is decided from an FP64
+// evaluation instead, far more accurate than the 4.8e-12 (relative) that
+// separates every finite FP16 input's exact SiLU from the nearest boundary.
+// silu(g) has the sign of g.
+__device__ __forceinline__ float half_bits_to_float(uint32_t b) {
+  return __half2float(__ushort_as_half(static_cast<unsigned short>(b)));
+}
+__device__ __forceinline__ uint32_t silu_half(uint32_t gbits) {
+  const float g = half_bits_to_float(gbits);
+  const float a = fabsf(g * __builtin_amdgcn_rcpf(1.0f + expf(-g)));
+  const uint32_t ab = __float_as_uint(a);
+  const uint32_t c = __half_as_ushort(__float2half_rn(a));  // |s| candidate (RNE)
+  uint32_t r = c;
+  if (ab < 0x38800000u || (ab & 0x1fffu) - 0x0ff8u <= 16u) {
+    // midpoints to the neighbouring halves (exact in FP32), against FP64
+    const float fc = half_bits_to_float(c);
+    const float lo = c > 0 ? 0.5f * (fc + half_bits_to_float(c - 1)) : -1.0f;
+    const float hi = c < 0x7bffu ? 0.5f * (fc + half_bits_to_float(c + 1)) : INFINITY;
+    const double gd = static_cast<double>(g);
+    const double ad = fabs(gd / (1.0 + exp(-gd)));
+    r = ad > static_cast<double>(hi) ? c + 1 : (ad < static_cast<double>(lo) ? c - 1 : c);
+  }
+  return r | (gbits & 0x8000u);
+}
+__device__ __forceinline__ uint32_t swiglu1(uint32_t gbits, uint32_t ubits) {
+  const float sv = half_bits_to_float(silu_half(gbits));
+  return __half_as_ushort(__float2half_rn(sv * half_bits_to_float(ubits)));
+}
+__device__ __forceinline__ uint32_t swiglu2(uint32_t g2, uint32_t u2) {
+  return swiglu1(g2 & 0xffffu, u2 & 0xffffu) | (swiglu1(g2 >> 16, u2 >> 16) << 16);
+}
+__device__ __forceinline__ uint4 swiglu8(uint4 g, uint4 u) {
+  return make_uint4(swiglu2(g.x, u.x), swiglu2(g.y, u.y), swiglu2(g.z, u.z), swiglu2(g.w, u.w));
+}
+
+// Vector path: the row of h is computed once, in a loop of 8-element vectors
+// (the SiLU with its rare FP64 branch is too long to unroll over a whole
+// row), and kept in LDS until the scale is known.  h (optional) receives the
+// FP16 activations.  Dynamic LDS: 16 bytes per vector of the row.
+constexpr int kSwigluLdsMaxVec = 4000;  // 62.5 KB (within the 64 KB default): rows up to 32000 channels
+__global__ __launch_bounds__(kThreads) void swiglu_quant_lds_kernel(const uint4* __restrict__ gate, int64_t ldg_vec,
+                                                                     const uint4* __restrict__ up, int64_t ldu_vec,
+                                                                     int k_vec, uint2* __restrict__ x8,
+                                                                     unsigned short* __restrict__ sx,
+                                                                     uint4* __restrict__ h, int64_t ldh_vec) {
+  extern __shared__ uint4 hrow[];
+  __shared__ uint32_t red[kThreads / 64];
+  const int64_t m = blockIdx.x;
+  uint32_t amax = 0;
+  for (int idx = threadIdx.x; idx < k_vec; idx += kThreads) {
+    const uint4 v = swiglu8(gate[m * ldg_vec + idx], up[m * ldu_vec + idx]);
+    hrow[idx] = v;
+    amax = max(amax, max_abs_bits8(v));
+    if (h) h[m * ldh_vec + idx] = v;
+  }
+  amax = block_max(amax, red);  // each thread rereads only the entries it wrote
+  unsigned short s_bits;
+  const float s = scale_from_absmax(amax, &s_bits);
+  const float y = s != 0.0f ? 1.0f / s : 0.0f;
+  if (threadIdx.x == 0) sx[m] = s_bits;
+  uint2* out = x8 + m * k_vec;
+  for (int idx = threadIdx.x; idx < k_vec; idx += kThreads) {
+    const uint4 v = hrow[idx];
+    uint2 q = make_uint2(0u, 0u);
+    if (s != 0.0f) q = make_uint2(quant4(v.x, v.y, s, y), quant4(v.z, v.w, s, y));
+    out[idx] = q;
+  }
+}
+
+// Vector path for long rows: two passes, the second recomputing h from the
+// inputs (read again, from cache).
+__global__ __launch_bounds__(kThreads) void swiglu_quant_stream_kernel(const uint4* __restrict__ gate, int64_t ldg_vec,
+                                                                        const uint4* __restrict__ up, int64_t ldu_vec,
+                                                                        int k_vec, uint2* __restrict__ x8,
+                                                                        unsigned short* __restrict__ sx,
+                                                                        uint4* __restrict__ h, int64_t ldh_vec) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int64_t m = blockIdx.x;
+  uint32_t amax = 0;
+  for (int idx = threadIdx.x; idx < k_vec; idx += kThreads)
+    amax = max(amax, max_abs_bits8(swiglu8(gate[m * ldg_vec + idx], up[m * ldu_vec + idx])));
+  amax = block_max(amax, red);
+  unsigned short s_bits;
+  const float s = scale_from_absmax(amax, &s_bits);
+  const float y = s != 0.0f ? 1.0f / s : 0.0f;
+  if (threadIdx.x == 0) sx[m] = s_bits;
+  uint2* out = x8 + m * k_vec;
+  for (int idx = threadIdx.x; idx < k_vec; idx += kThreads) {
+    const uint4 v = swiglu8(gate[m * ldg_vec + idx], up[m * ldu_vec + idx]);
+    uint2 q = make_uint2(0u, 0u);
+    if (s != 0.0f) q = make_uint2(quant4(v.x, v.y, s, y), quant4(v.z, v.w, s, y));
+    out[idx] = q;
+    if (h) h[m * ldh_vec + idx] = v;
+  }
+}
+
+// Scalar path for any K / alignment.
+__global__ __launch_bounds__(kThreads) void swiglu_quant_scalar_kernel(const unsigned short* __restrict__ gate,
+                                                                        int64_t ldg,
+                                                                        const unsigned short* __restrict__ up,
+                                                                        int64_t ldu, int64_t K,
+                                                                        int8_t* __restrict__ x8,
+                                                                        unsigned short* __restrict__ sx,
+                                                                        unsigned short* __restrict__ h, int64_t ldh) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int64_t m = blockIdx.x;
+  uint32_t amax = 0;
+  for (int64_t k = threadIdx.x; k < K; k += kThreads)
+    amax = max(amax, swiglu1(gate[m * ldg + k], up[m * ldu + k]) & 0x7fffu);
+  amax = block_max(amax, red);
+  unsigned short s_bits;
+  const float s = scale_from_absmax(amax, &s_bits);
+  const float y = s != 0.0f ? 1.0f / s : 0.0f;
+  if (threadIdx.x == 0) sx[m] = s_bits;
+  for (int64_t k = threadIdx.x; k < K; k += kThreads) {
+    const uint32_t v = swiglu1(gate[m * ldg + k], up[m * ldu + k]);
+    x8[m * K + k] = s != 0.0f ? static_cast<int8_t>(quant1(v, s, y)) : int8_t(0);
+    if (h) h[m * ldh + k] = static_cast<unsigned short>(v);
+  }
+}
+
 }  // namespace
 }  // namespace qoq
 
@@ -494,5 +630,48 @@ extern "C" int qoq_quant_act_per_token(const void* x_fp16, int64_t M, int64_t K,
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(QOQ_ERR_HIP, "qoq_quant_act_per_token: launch failed: %s", hipGetErrorString(e));
+  return QOQ_OK;
+}
+
+extern "C" int qoq_swiglu_quant_per_token(const void* gate_fp16, const void* up_fp16, int64_t M, int64_t K,
+                                          int64_t ldg, int64_t ldu, int8_t* x8, void* sx_fp16, void* h_fp16,
+                                          int64_t ldh, void* stream) {
+  clear_error();
+  if (!gate_fp16 || !up_fp16 || !x8 || !sx_fp16)
+    return fail(QOQ_ERR_INVALID_ARG, "qoq_swiglu_quant_per_token: null pointer argument");
+  if (M < 1 || K < 1) return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "qoq_swiglu_quant_per_token: M and K must be >= 1");
+  if (ldg < K || ldu < K || (h_fp16 && ldh < K))
+    return fail(QOQ_ERR_INVALID_ARG, "qoq_swiglu_quant_per_token: a leading dimension is below K");
+  if (M > 0x7fffffff || K > 0x7fffffff)
+    return fail(QOQ_ERR_UNSUPPORTED_SHAPE, "qoq_swiglu_quant_per_token: M or K too large");
+  const auto al = [](const void* p, uintptr_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; };
+  if (!al(gate_fp16, 2) || !al(up_fp16, 2) || !al(sx_fp16, 2) || (h_fp16 && !al(h_fp16, 2)))
+    return fail(QOQ_ERR_ALIGNMENT, "qoq_swiglu_quant_per_token: FP16 pointers must be 2-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>(M)), block(kThreads);
+  const bool vec = K % 8 == 0 && ldg % 8 == 0 && ldu % 8 == 0 && al(gate_fp16, 16) && al(up_fp16, 16) &&
+                   al(x8, 8) && (!h_fp16 || (ldh % 8 == 0 && al(h_fp16, 16)));
+  auto* sx = static_cast<unsigned short*>(sx_fp16);
+  if (vec) {
+    const auto* gv = static_cast<const uint4*>(gate_fp16);
+    const auto* uv = static_cast<const uint4*>(up_fp16);
+    auto* qv = reinterpret_cast<uint2*>(x8);
+    auto* hv = static_cast<uint4*>(h_fp16);
+    const int k_vec = static_cast<int>(K / 8);
+    const int64_t lg = ldg / 8, lu = ldu / 8, lh = h_fp16 ? ldh / 8 : 0;
+    if (k_vec <= kSwigluLdsMaxVec) {
+      const size_t lds = size_t(k_vec) * sizeof(uint4);
+      hipLaunchKernelGGL(swiglu_quant_lds_kernel, grid, block, lds, st, gv, lg, uv, lu, k_vec, qv, sx, hv, lh);
+    } else {
+      hipLaunchKernelGGL(swiglu_quant_stream_kernel, grid, block, 0, st, gv, lg, uv, lu, k_vec, qv, sx, hv, lh);
+    }
+  } else {
+    hipLaunchKernelGGL(swiglu_quant_scalar_kernel, grid, block, 0, st, static_cast<const unsigned short*>(gate_fp16),
+                       ldg, static_cast<const unsigned short*>(up_fp16), ldu, K, x8, sx,
+                       static_cast<unsigned short*>(h_fp16), ldh);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(QOQ_ERR_HIP, "qoq_swiglu_quant_per_token: launch failed: %s", hipGetErrorString(e));
   return QOQ_OK;
 }
