@@ -234,7 +234,7 @@ def _copies(w, wbytes):
     return min(c, 64)
 
 
-def measure_comparators(torch, q, w, W, x8, sx, y, ws, t_g, reps: int):
+def measure_comparators(torch, q, w, W, x8, sx, y, ws, t_g, reps: int, p_host=None):
     """The two comparators on the same inputs and launch plans: the W8A8
     GEMM (INT8 weights, no dequantization) and the saturating-dequantization
     ablation of the g128 GEMM."""
@@ -251,7 +251,42 @@ def measure_comparators(torch, q, w, W, x8, sx, y, ws, t_g, reps: int):
     if w.group_size:
         t_sat = time_kernel(torch, lambda i: q.qoq_w4a8_gemm_saturating(x8, sx, ws[i % len(ws)], y=y), reps)
         r.update({"saturating_us": round(t_sat, 3), "saturating_slowdown": round(t_sat / t_g, 3)})
+    if p_host is not None:
+        r.update(measure_library_w8a8(torch, q, w, p_host, x8, t_g, reps))
     return r
+
+
+def plain_w8(q, p_host):
+    """The INT8 weights [N, K] that packed W4 weights dequantize to."""
+    import numpy as np
+    q4, s1, z, _ = q.qoq_unpack_weights(p_host)
+    G = q4.shape[1] // 128
+    if s1 is None:
+        return (q4.astype(np.int16) - z.astype(np.int16)[:, None]).astype(np.int8)
+    w = (q4.reshape(q4.shape[0], G, 128).astype(np.int16) - z.astype(np.int16)[:, :, None]) * s1.astype(np.int16)[:, :, None]
+    return w.reshape(q4.shape).astype(np.int8)
+
+
+def measure_library_w8a8(torch, q, w, p_host, x8, t_g, reps: int):
+    """The vendor library's INT8 GEMM on the same shape: hipBLASLt through
+    torch._int_mm (INT32 output, no scale epilogue: less work than the fused
+    FP16 epilogue here), on the INT8 weights the W4 codes dequantize to.  The
+    pages set their W4A8 GEMM against the vendor W8A8 GEMM; this is that
+    comparison on MI355X.  (The library refuses 16 rows or fewer.)"""
+    if w.M <= 16:
+        return {"hipblaslt_w8a8_us": None, "hipblaslt_note": "torch._int_mm needs more than 16 rows"}
+    w8 = torch.from_numpy(plain_w8(q, p_host)).to(x8.device)
+    c = _copies(w, w8.numel())
+    w8s = [w8] + [w8.clone() for _ in range(c - 1)]
+    try:
+        for b in w8s:
+            torch._int_mm(x8, b.t())
+    except RuntimeError as e:
+        return {"hipblaslt_w8a8_us": None, "hipblaslt_note": str(e).splitlines()[0][:120]}
+    t = time_kernel(torch, lambda i: torch._int_mm(x8, w8s[i % c].t()), reps)
+    del w8s, w8
+    return {"hipblaslt_w8a8_us": round(t, 3), "hipblaslt_w8a8_tops": round(w.ops / t / 1e6, 2),
+            "hipblaslt_weight_copies": c, "w4a8_over_hipblaslt_w8a8": round(t / t_g, 3)}
 
 
 KV4_SHAPES = [("llama2_7b_mha", 64, 32, 32, 1024), ("llama3_8b_gqa", 64, 32, 8, 1024),
@@ -358,7 +393,7 @@ def measure_gemm(torch, q, w, X, W, reps: int, comparators: bool = False):
          "rmsnorm_quant_us": round(t_n, 3), "rmsnorm_quant_gbs": round(producer_bytes(w) / t_n / 1e3, 1),
          "swiglu_quant_us": round(t_s, 3), "swiglu_quant_gbs": round(swiglu_bytes(w) / t_s / 1e3, 1)}
     if comparators:
-        r.update(measure_comparators(torch, q, w, W, x8, sx, y, ws, t_g, reps))
+        r.update(measure_comparators(torch, q, w, W, x8, sx, y, ws, t_g, reps, packed_host))
     del ws
     return r
 
@@ -523,8 +558,11 @@ def main():
                 "w4a8_over_w8a8": {r["workload"]: r["w4a8_over_w8a8"] for r in sweep if "w4a8_over_w8a8" in r},
                 "saturating_slowdown": {r["workload"]: r["saturating_slowdown"] for r in sweep
                                         if "saturating_slowdown" in r},
+                "w4a8_over_hipblaslt_w8a8": {r["workload"]: r["w4a8_over_hipblaslt_w8a8"] for r in sweep
+                                             if r.get("w4a8_over_hipblaslt_w8a8") is not None},
                 "note": "same kernels and plans; W8A8 = per-channel INT8 weights without dequantization; "
-                        "saturating = g128 GEMM with a clamping 16-bit-lane dequantization",
+                        "saturating = g128 GEMM with a clamping 16-bit-lane dequantization; "
+                        "hipblaslt = the vendor library's INT8 GEMM (torch._int_mm, INT32 out) on the same shape",
             }
 
     if not args.no_kv4:

@@ -82,3 +82,40 @@ def test_binding_rejects_bad_arguments():
         q.qoq_rmsnorm_quant_per_token(x, torch.ones(64, dtype=torch.float16, device="cuda"), 1e-5)
     with pytest.raises(q.QoQError):
         q.qoq_rmsnorm_quant_per_token(x, torch.ones(128, dtype=torch.float16, device="cuda"), 0.0)
+
+
+def boundary_rows(K, n, seed):
+    """Rows whose exact mean square is an FP32 rounding tie (even rows) or
+    lies 2^-48 / K above one (odd rows): [1, 1, m3 2^-12, m4 2^-12, (2^-24),
+    0, ...] with m3, m4 odd, so S = 2 + (m3^2 + m4^2) 2^-24 with m3^2 + m4^2
+    twice an odd number; for K a power of two, S / K is an odd multiple of
+    half the FP32 spacing of its binade.  The kernel's FP64 sum cannot decide
+    such rows and takes the exact 128-bit sum."""
+    rng = np.random.default_rng(seed)
+    X = np.zeros((n, K), np.float16)
+    for r in range(n):
+        m3, m4 = (2 * rng.integers(0, 1024, 2) + 1).tolist()
+        X[r, 0] = X[r, 1] = 1.0
+        X[r, 2], X[r, 3] = m3 * 2.0 ** -12, -m4 * 2.0 ** -12
+        if r % 2:
+            X[r, 4] = 2.0 ** -24
+        perm = rng.permutation(K)
+        X[r] = X[r, perm]
+        # the tie property, from the exact sum (every FP16 value is an integer times 2^-24)
+        units = (X[r].astype(np.float64) * 2.0 ** 24).astype(np.int64).tolist()
+        S = sum(v * v for v in units)                     # units of 2^-48
+        half = 2 ** 25                                    # half the FP32 spacing of [2, 4) (2^-23), units of 2^-48
+        assert (S - 2 * 2 ** 48) % half == (0 if r % 2 == 0 else 1) and ((S - 2 * 2 ** 48) // half) % 2 == 1
+    return X
+
+
+@pytest.mark.parametrize("K", [1024, 4096, 8192, 16384])
+def test_mean_square_at_fp32_rounding_boundaries(K):
+    """Rows the FP64 fast path must hand to the exact sum (ties and near-ties
+    of the FP32 mean square), through every register-path width; the oracle
+    rounds the exact S."""
+    print(f"[rmsnorm ties] K={K}", flush=True)
+    X = boundary_rows(K, 12, seed=K)
+    g = synthetic.make_gamma(K, seed=3)
+    check(X, g, 1e-5)
+    check(X, g, 2.0 ** -40)

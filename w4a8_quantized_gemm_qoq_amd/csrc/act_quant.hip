@@ -272,9 +272,54 @@ __device__ __forceinline__ double u128_to_double_rn(u128 v) {
   return ldexp(static_cast<double>(top), n);
 }
 
-__device__ __forceinline__ float rms_factor(u128 S, int64_t K, float eps) {
-  const float ms = static_cast<float>(ldexp(u128_to_double_rn(S), -48) / static_cast<double>(K));
-  return 1.0f / sqrtf(ms + eps);
+__device__ __forceinline__ float mean_square(u128 S, int64_t K) {
+  return static_cast<float>(ldexp(u128_to_double_rn(S), -48) / static_cast<double>(K));
+}
+__device__ __forceinline__ float rms_factor(float ms, float eps) { return 1.0f / sqrtf(ms + eps); }
+
+// Fast path for the mean square.  The square of an FP16 value is exact in
+// FP32 (at most 22 significant bits, between 2^-48 and 2^32), so summing the
+// squares in FP64 rounds only at the additions: with non-negative addends, a
+// sum reached through at most n additions along any path is within n * 2^-53
+// (relative) of the exact S.  A thread adds at most 64 squares and the block
+// reduction adds 8 levels, so S' is within 2^-46 of S.  Every step from S to
+// ms (FP64 rounding, division by K, FP32 rounding) is monotone, so when the
+// ends of [S'(1 - 2^-44), S'(1 + 2^-44)] give the same FP32 value, so does S
+// and that value is the exact path's result; otherwise (a row whose mean
+// square lies within about 2^-44 of an FP32 rounding boundary) the caller
+// takes the exact 128-bit sum.
+__device__ __forceinline__ double sumsq8_f64(uint4 q, double acc) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = __half2float(__ushort_as_half(static_cast<unsigned short>(w[i] & 0xffffu)));
+    const float b = __half2float(__ushort_as_half(static_cast<unsigned short>(w[i] >> 16)));
+    acc += static_cast<double>(a * a);
+    acc += static_cast<double>(b * b);
+  }
+  return acc;
+}
+
+// Block-wide FP64 sum (every thread gets the same value).
+__device__ __forceinline__ double block_sum_f64(double v, double* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  double r = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) r += red[w];
+  return r;
+}
+
+// The mean square from the FP64 sum when it is certain to equal the exact
+// path's value; NaN otherwise.
+__device__ __forceinline__ float mean_square_fast(double s, int64_t K) {
+  const double k = static_cast<double>(K);
+  const float lo = static_cast<float>(s * (1.0 - 0x1p-44) / k);
+  const float hi = static_cast<float>(s * (1.0 + 0x1p-44) / k);
+  return lo == hi ? lo : __builtin_nanf("");
 }
 
 __device__ __forceinline__ uint32_t norm1(uint32_t xbits, uint32_t gbits, float r) {
@@ -296,10 +341,11 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_reg_kernel(const uint4
                                                                       float eps, uint2* __restrict__ x8,
                                                                       unsigned short* __restrict__ sx) {
   __shared__ uint32_t red_sum[kThreads / 64][4];
+  __shared__ double red_f64[kThreads / 64];
   __shared__ uint32_t red[kThreads / 64];
   const int64_t m = blockIdx.x;
   const uint4* row = x + m * ldx_vec;
-  static_assert(VPT * 8 <= 64, "one flush per row");
+  static_assert(VPT * 8 <= 64, "one flush per row, at most 64 FP64 additions per thread");
   // gamma is fetched together with the row, so that its latency overlaps the
   // row's and the sum of squares instead of following the reduction
   uint4 v[VPT], gv[VPT];
@@ -309,11 +355,18 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_reg_kernel(const uint4
     v[i] = idx < k_vec ? row[idx] : make_uint4(0, 0, 0, 0);
     gv[i] = idx < k_vec ? gamma[idx] : make_uint4(0, 0, 0, 0);
   }
-  SumSq S;
+  double s2 = 0.0;
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) S.add8(v[i]);
-  S.flush();
-  const float r = rms_factor(block_sum_u128(S.total, red_sum), int64_t(k_vec) * 8, eps);
+  for (int i = 0; i < VPT; ++i) s2 = sumsq8_f64(v[i], s2);
+  float ms = mean_square_fast(block_sum_f64(s2, red_f64), int64_t(k_vec) * 8);
+  if (ms != ms) {  // block-uniform: every thread holds the same sum
+    SumSq S;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) S.add8(v[i]);
+    S.flush();
+    ms = mean_square(block_sum_u128(S.total, red_sum), int64_t(k_vec) * 8);
+  }
+  const float r = rms_factor(ms, eps);
   uint32_t amax = 0;
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
@@ -360,7 +413,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_stream_kernel(const ui
     }
   }
   S.flush();
-  const float r = rms_factor(block_sum_u128(S.total, red_sum), int64_t(k_vec) * 8, eps);
+  const float r = rms_factor(mean_square(block_sum_u128(S.total, red_sum), int64_t(k_vec) * 8), eps);
   uint32_t amax = 0;
   for (int idx = threadIdx.x; idx < k_vec; idx += kThreads)
     amax = max(amax, max_abs_bits8(norm8(row[idx], gamma[idx], r)));
@@ -398,7 +451,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_scalar_kernel(const un
     }
   }
   S.flush();
-  const float r = rms_factor(block_sum_u128(S.total, red_sum), K, eps);
+  const float r = rms_factor(mean_square(block_sum_u128(S.total, red_sum), K), eps);
   uint32_t amax = 0;
   for (int64_t k = threadIdx.x; k < K; k += kThreads) amax = max(amax, norm1(row[k], gamma[k], r) & 0x7fffu);
   amax = block_max(amax, red);
