@@ -475,23 +475,38 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_scalar_kernel(const un
 // be finite and their products must not overflow FP16.
 
 // FP16 SiLU, correctly rounded.  Evaluated in FP32 (e^-g by the library's
-// expf, one hardware reciprocal: within a few ulps).  Where that value lies
-// within 8 FP32 ulps of an FP16 rounding boundary (its 13 bits below the FP16
-// precision within 8 of one half; about 0.2% of inputs), or in the FP16
-// subnormal range, the side of the boundary is decided from an FP64
-// evaluation instead, far more accurate than the 4.8e-12 (relative) that
-// separates every finite FP16 input's exact SiLU from the nearest boundary.
+// expf, one hardware reciprocal): over every finite FP16 input whose SiLU is
+// at least the smallest FP16 subnormal, that value lies within 2.5 FP32 ulps
+// of the exact SiLU.  Where it lies within 4 FP32 ulps of an FP16 rounding
+// boundary -- for normal FP16 results, its 13 bits below the FP16 precision
+// within 4 of one half (0.1% of inputs); for subnormal ones, within 4 of its
+// ulps of an odd multiple of 2^-25 -- the side of the boundary is decided from
+// an FP64 evaluation instead, far more accurate than the 4.8e-12 (relative)
+// that separates every finite FP16 input's exact SiLU from the nearest
+// boundary.  The GPU tests check the result on every finite FP16 input.
 // silu(g) has the sign of g.
 __device__ __forceinline__ float half_bits_to_float(uint32_t b) {
   return __half2float(__ushort_as_half(static_cast<unsigned short>(b)));
 }
+constexpr uint32_t kSiluWindow = 4;  // FP32 ulps
 __device__ __forceinline__ uint32_t silu_half(uint32_t gbits) {
   const float g = half_bits_to_float(gbits);
   const float a = fabsf(g * __builtin_amdgcn_rcpf(1.0f + expf(-g)));
   const uint32_t ab = __float_as_uint(a);
   const uint32_t c = __half_as_ushort(__float2half_rn(a));  // |s| candidate (RNE)
+  bool near;
+  if (ab >= 0x38800000u) {  // a normal FP16 result
+    near = (ab & 0x1fffu) - (0x1000u - kSiluWindow) <= 2u * kSiluWindow;
+  } else {
+    // FP16 subnormals are multiples of 2^-24: the distance of a * 2^24 (exact)
+    // to the nearest half-integer, against the FP32 ulps of a * 2^24
+    const float r = a * 0x1p24f;
+    const float d = fabsf(r - (floorf(r) + 0.5f));
+    const float u = __uint_as_float((__float_as_uint(r) & 0x7f800000u) | 1u) - __uint_as_float(__float_as_uint(r) & 0x7f800000u);
+    near = r >= 0x1p-30f && !(d > static_cast<float>(kSiluWindow) * u);
+  }
   uint32_t r = c;
-  if (ab < 0x38800000u || (ab & 0x1fffu) - 0x0ff8u <= 16u) {
+  if (near) {
     // midpoints to the neighbouring halves (exact in FP32), against FP64
     const float fc = half_bits_to_float(c);
     const float lo = c > 0 ? 0.5f * (fc + half_bits_to_float(c - 1)) : -1.0f;
