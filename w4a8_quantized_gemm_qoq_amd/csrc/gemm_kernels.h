@@ -10,9 +10,9 @@
 //     INT8; four weights are decoded per 32-bit register operation;
 //   §4: the protective level-0 range [-119, 119] keeps the dequantized
 //     intermediates inside INT8, so no saturating arithmetic is needed;
-//   §5: subtraction after multiplication, w8 = q4*s1 - z*s1; weights stored in
-//     computation order and read with 128-bit loads; per-channel scale fused
-//     into the epilogue; FP16 output.
+//   §5: subtraction after multiplication, w8 = q4*s1 - z*s1; the packed
+//     weights laid out in the order the kernel consumes them, fetched 16 bytes
+//     per lane; the per-channel scale applied in the epilogue; FP16 output.
 //
 // In-register dequantization (per 32-bit word of 8 packed UINT4 codes):
 //   lo = v & 0x0f0f0f0f, hi = (v >> 4) & 0x0f0f0f0f   (four codes per word)
