@@ -39,7 +39,7 @@ SMALL = [
     (640, 1024, 4096, 0, ('large', 1, 1)),  # ... per-channel, 160 tiles, ragged last row tile
     (256, 512, 4096, 128, ('skinny64', 4, 4)),  # up to 256 rows in one round of skinny blocks (4 strips, K split in LDS)
     (200, 384, 4000, 0, ('skinny64', 4, 4)),  # ... per-channel, ragged M and N (252 blocks)
-    (40, 256, 32768, 128, ('skinny64', 4, 4)),  # skinny 64-row tiles at most 7 strips per block; rows past M repeat row M-1
+    (80, 256, 14336, 128, ('skinny64', 7, 4)),  # skinny 64-row tiles at most 7 strips per block; rows past M repeat row M-1
     (192, 640, 4096, 128, ('skinny64', 4, 4)),  # 3 row blocks of 4 strips (192 blocks): strip count from the activation-aware cost
     (161, 384, 2000, 0, ('skinny64', 2, 4)),  # ... per-channel, 2 strips per block, ragged last row block and last strip block
     (250, 1024, 160, 128, ('skinny64', 1, 4)),  # ... one strip per block, 4 row blocks, rows past M in the last
@@ -52,4 +52,11 @@ SMALL = [
     (1000, 8192, 4000, 0, ('large', 2, 1)),  # ... per-channel, ragged M and N
     (512, 32768, 2048, 128, ('large', 2, 4)),  # ... with K split in 4 across blocks (64 groups per split)
     (384, 32768, 2048, 0, ('large', 2, 4)),  # ... per-channel, K split in 4
+    (40, 256, 32768, 128, ('skinny64', 4, 4)),  # skinny 64-row tiles, 4 strips per block; rows past M repeat row M-1
+    (40, 1024, 20000, 128, ('ring', 5, 1)),  # ring kernel (one strip per wave, activations through an LDS ring): one batch of 8 groups
+    (33, 2048, 28000, 0, ('ring', 7, 1)),  # ... per-channel, two batches, rows past M
+    (24, 5120, 24000, 128, ('ring', 6, 1)),  # ... 32-row tiles, five batches
+    (16, 10240, 20000, 128, ('ring', 5, 1)),  # ... 16-row tiles where the strip kernel's LDS is too small, ten batches
+    (64, 1024, 32768, 128, ('ring', 8, 1)),  # ... eight strips per block (256 blocks)
+    (60, 3072, 17000, 0, ('ring', 5, 1)),  # ... per-channel, three batches, dead waves past N in the last block
 ]

@@ -362,7 +362,7 @@ def qoq_w4a8_gemm(x8, sx, w: PackedWeight, y=None, workspace=None, stream=None):
     return y
 
 
-GEMM_KERNELS = {0: "strip", 1: "skinny16", 2: "skinny32", 3: "skinny64", 4: "large"}
+GEMM_KERNELS = {0: "strip", 1: "skinny16", 2: "skinny32", 3: "skinny64", 4: "large", 5: "ring"}
 
 
 def qoq_w4a8_gemm_plan(M: int, N: int, K: int, group_size: int = GROUP) -> tuple[str, int, int]:

@@ -51,6 +51,8 @@
 #include <hip/hip_fp16.h>
 
 #include <algorithm>
+#include <type_traits>
+#include <utility>
 
 #include "qoq_internal.h"
 
@@ -138,6 +140,13 @@ __device__ __forceinline__ uint32_t buf_load4s(__amdgpu_buffer_rsrc_t r, int vof
 // s_waitcnt immediates (gfx9 encoding): wait until at most n vector-memory
 // operations of this wave are outstanding, leaving the other counters free.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Barrier for LDS traffic only: this wave's LDS operations are complete
+// (lgkmcnt 0) and every wave has arrived.  Global loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+}
 
 // Direct global -> LDS copy of 16 bytes per lane: lane i writes lds + 16 i.
 // (Kept in a device function: the builtin is not meaningful to the host pass.)
@@ -245,6 +254,17 @@ __device__ __forceinline__ v4i b_op16(const u32x4 (&q)[wf_vec(WF)], int h, uint3
 // consecutive rows reading the same K chunk over all 64 banks.
 __device__ __forceinline__ int lds_off(int row, int kc) { return row * 128 + ((kc ^ ((row >> 1) & 7)) << 4); }
 
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, each i a compile-time
+// constant (for immediates such as hand-counted waits in unrolled loops).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // Keeps prefetch loads where they are written: the empty asm with a memory
 // clobber stops IR passes from sinking loads toward their uses, and the
 // scheduling barrier stops the machine scheduler from doing the same.
@@ -312,6 +332,48 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int row, int col, i
 // every copy in flight before each read.  The caller's hand-counted vmcnt
 // wait covers the slot read here, and the block waits for its own reads, so
 // no output register is left in flight.
+// One dword from LDS, read the same way (for data that direct-to-LDS copies
+// wrote before the last barrier, while other copies are in flight).
+__device__ __forceinline__ uint32_t lds_read_u32(const uint32_t* p) {
+  const auto* lp = (const __attribute__((address_space(3))) uint32_t*)p;
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n s_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lp))));
+  return v;
+}
+
+// Both K halves' A fragments of one group (row tile i of half h at p[h] +
+// 2048 i) and, when `pm` is given, the metadata dword at pm, with a single
+// wait: one LDS round trip per group.
+template <int TM>
+__device__ __forceinline__ void read_group_frags(v4i (&af)[2][TM], uint32_t& m, const int8_t* p0, const int8_t* p1,
+                                                 const uint32_t* pm) {
+  const auto ad = [](const void* q) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) int8_t*)q));
+  };
+  const uint32_t a0 = ad(p0), a1 = ad(p1), am = ad(pm);
+  if constexpr (TM == 1) {
+    asm volatile("ds_read_b128 %0, %3\n ds_read_b128 %1, %4\n ds_read_b32 %2, %5\n s_waitcnt lgkmcnt(0)"
+                 : "=&v"(af[0][0]), "=&v"(af[1][0]), "=&v"(m)
+                 : "v"(a0), "v"(a1), "v"(am));
+  } else if constexpr (TM == 2) {
+    asm volatile(
+        "ds_read_b128 %0, %5\n ds_read_b128 %1, %5 offset:2048\n ds_read_b128 %2, %6\n"
+        " ds_read_b128 %3, %6 offset:2048\n ds_read_b32 %4, %7\n s_waitcnt lgkmcnt(0)"
+        : "=&v"(af[0][0]), "=&v"(af[0][1]), "=&v"(af[1][0]), "=&v"(af[1][1]), "=&v"(m)
+        : "v"(a0), "v"(a1), "v"(am));
+  } else {
+    static_assert(TM == 4, "row tiles per ring block: 1, 2 or 4");
+    asm volatile(
+        "ds_read_b128 %0, %9\n ds_read_b128 %1, %9 offset:2048\n ds_read_b128 %2, %9 offset:4096\n"
+        " ds_read_b128 %3, %9 offset:6144\n ds_read_b128 %4, %10\n ds_read_b128 %5, %10 offset:2048\n"
+        " ds_read_b128 %6, %10 offset:4096\n ds_read_b128 %7, %10 offset:6144\n ds_read_b32 %8, %11\n"
+        " s_waitcnt lgkmcnt(0)"
+        : "=&v"(af[0][0]), "=&v"(af[0][1]), "=&v"(af[0][2]), "=&v"(af[0][3]), "=&v"(af[1][0]), "=&v"(af[1][1]),
+          "=&v"(af[1][2]), "=&v"(af[1][3]), "=&v"(m)
+        : "v"(a0), "v"(a1), "v"(am));
+  }
+}
+
 template <int TM>
 __device__ __forceinline__ void read_a_frags(v4i (&af)[TM], const int8_t* p) {
   const auto* lp = (const __attribute__((address_space(3))) int8_t*)p;
@@ -741,6 +803,194 @@ __global__ __launch_bounds__(512) void gemm_strip_kernel(GemmArgs a, int spb, in
 }
 
 // ---------------------------------------------------------------------------
+// ring: up to 64 rows when the strips alone give about one block per CU
+// (decode with a wide N).  As in the strip kernel every wave streams one
+// 16-channel strip over the whole K range as one contiguous run and keeps one
+// accumulator tile per 16 rows, so PF groups of weights stay in flight.  The
+// block's TM*16 activation rows do not fit in LDS whole: they pass through a
+// ring of two batches of kRingBatch groups, copied by every wave of the block
+// one batch ahead (direct-to-LDS loads), with one barrier per batch.
+//
+// LDS: batch slot b (of 2): kRingBatch group tiles of R = TM*16 rows x 128 B,
+// row r of group u at row u*R + r, 16-byte chunk q stored at chunk
+// q ^ ((row >> 1) & 7) (row tiles of 16 share one swizzle, 2048 bytes apart);
+// then the metadata of the block's strips (g128), as in the strip kernel.
+constexpr int kRingBatch = 8;
+constexpr int ring_batch_bytes(int tm) { return kRingBatch * tm * 16 * 128; }
+
+template <int TM, int SPB, int PF, int WF, bool I32OUT>
+__global__ __launch_bounds__(64 * SPB) void gemm_ring_kernel(GemmArgs a) {
+  static_assert(kRingBatch % PF == 0 || PF % kRingBatch == 0, "the weight ring turns over at a batch boundary");
+  static_assert(PF * wf_vec(WF) + (PF + kRingBatch - 1) / kRingBatch * ((kRingBatch * TM * 16 * 8 / 64 + SPB - 1) / SPB) <= 63 &&
+                    kRingBatch * wf_vec(WF) <= 63,
+                "vmcnt holds at most 63");
+  constexpr int spb = SPB;  // strips (waves) per block
+  extern __shared__ __align__(16) int8_t smem[];
+  constexpr int R = TM * 16;
+  constexpr int kBatchChunks = kRingBatch * R * 8;  // 16-byte chunks per batch
+  constexpr int kBatchBytes = ring_batch_bytes(TM);
+  static_assert(kBatchChunks % 64 == 0, "whole wave-wide copies per batch");
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int sb = blockIdx.x * spb;
+  const int strip = sb + wave;
+  const bool live = strip < a.n_strips;
+  const int cstrip = min(strip, a.n_strips - 1);
+  const int c16 = lane & 15, j = lane >> 4;
+  const int G = a.G;
+  const int64_t K = int64_t(G) * 128;
+  const int nb = (G + kRingBatch - 1) / kRingBatch;
+
+  // Activation copies of batch bt into slot bt & 1.  Every wave issues the
+  // same, compile-time number of copy instructions (a wave past the batch's
+  // last 64 chunks repeats them: the same bytes to the same place), so the
+  // compiler's waits for the weight registers and the hand-counted waits
+  // below are exact for every wave.  Rows past M read row M-1 (never
+  // stored); groups past K read the last group (never multiplied).
+  constexpr int ncp = (kBatchChunks / 64 + spb - 1) / spb;
+  auto copy_batch = [&](int bt) {
+    int8_t* dst = smem + (bt & 1) * kBatchBytes;
+#pragma unroll
+    for (int k = 0; k < ncp; ++k) {
+      const int base = min((k * spb + wave) * 64, kBatchChunks - 64);
+      const int pc = base + lane;
+      const int lrow = pc >> 3;
+      const int q = (pc & 7) ^ ((lrow >> 1) & 7);
+      const int u = lrow / R, r = lrow - u * R;
+      const int g = min(bt * kRingBatch + u, G - 1);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(a.x8 + int64_t(min(r, a.M - 1)) * K + int64_t(g) * 128 + q * 16),
+                                       (__attribute__((address_space(3))) void*)(dst + base * 16), 16, 0, 0);
+    }
+  };
+  // group metadata of the block's strips, after the ring (one contiguous run
+  // of G4q * 64 bytes per strip); lanes past the end fetch a valid chunk into
+  // the region's padding
+  int8_t* meta_lds = smem + 2 * kBatchBytes;
+  if constexpr (wf_group_meta(WF)) {
+    const int m_chunks = min(spb, a.n_strips - sb) * a.G4q * 4;
+    const int m_last = ((m_chunks - 1) >> 6) << 6;
+    const int nmp = ((m_chunks + 63) / 64 + spb - 1) / spb;
+    const int8_t* msrc = reinterpret_cast<const int8_t*>(a.meta) + int64_t(sb) * a.G4q * 64;
+    for (int k = 0; k < nmp; ++k) {
+      const int base = min((k * spb + wave) * 64, m_last);
+      const int pc = min(base + lane, m_chunks - 1);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(msrc + pc * 16),
+                                       (__attribute__((address_space(3))) void*)(meta_lds + base * 16), 16, 0, 0);
+    }
+  }
+  const uint32_t* lmeta = reinterpret_cast<const uint32_t*>(meta_lds) + wave * a.G4q * 16 + c16;
+
+  constexpr int kVec = wf_vec(WF);
+  constexpr int kBlk = wf_block_bytes(WF);
+  const int strip_bytes = G * kBlk;
+  const __amdgpu_buffer_rsrc_t wrs =
+      make_rsrc(reinterpret_cast<const int8_t*>(a.qw) + int64_t(cstrip) * strip_bytes, live ? strip_bytes : 0);
+  u32x4 bq[PF][kVec];
+  auto load_b = [&](int g, u32x4 (&b)[kVec]) {
+#pragma unroll
+    for (int v = 0; v < kVec; ++v) b[v] = buf_load16<kCacheStream>(wrs, lane * 16 + v * 1024 + (g < G ? g * kBlk : kDeadOffset));
+  };
+  uint32_t S = 0, C = 0;
+  if constexpr (WF == kWfPerChannel) meta_perchannel(a.meta8[cstrip * 16 + c16], S, C);
+
+  // Prologue: batch 0, the metadata, then the first PF groups of weights;
+  // wait for everything but those weights and meet the other waves.
+  copy_batch(0);
+  QOQ_COMPILER_FENCE();
+#pragma unroll
+  for (int p = 0; p < PF; ++p) load_b(p, bq[p]);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(PF * kVec));
+  __builtin_amdgcn_s_barrier();
+  QOQ_COMPILER_FENCE();
+
+  v4i acc[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) acc[i] = v4i{0, 0, 0, 0};
+  // A fragments of one K half from group u of a slot (row tile i at +2048 i),
+  // read in inline assembly with their own wait: the compiler cannot tell
+  // which slot the copies in flight fill and would otherwise wait for all of
+  // them before every read.
+  // A fragments and metadata dword of group g (row u of a slot), one group
+  // ahead: they are read right after the previous group's multiplies are
+  // issued, so the read's round trip overlaps the matrix unit's work.  (The
+  // formats without group metadata read, and ignore, a dword of the slot.)
+  v4i fa[2][2][TM];
+  uint32_t fm[2];
+  auto read_next = [&](v4i (&af)[2][TM], uint32_t& mw, const int8_t* slot, int u, int g) {
+    read_group_frags<TM>(af, mw, slot + strip_lds_off(u * R + c16, j), slot + strip_lds_off(u * R + c16, j + 4),
+                         wf_group_meta(WF) ? lmeta + (min(g, G - 1) >> 2) * 16 : reinterpret_cast<const uint32_t*>(slot));
+  };
+  auto compute = [&](const v4i (&af)[2][TM], uint32_t mw, int g, const u32x4 (&bc)[kVec]) {
+    if constexpr (wf_group_meta(WF)) meta_g128<WF>((mw >> (8 * (g & 3))) & 0xffu, S, C);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const v4i bf = b_op16<WF>(bc, h, S, C);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[h][i], bf, acc[i], 0, 0, 0);
+    }
+  };
+  // group u of a batch uses fragment buffer u % 2 (kRingBatch is even, so
+  // every batch starts on buffer 0)
+  static_assert(kRingBatch % 2 == 0, "fragment buffers alternate within a batch");
+  read_next(fa[0], fm[0], smem, 0, 0);
+  // one batch; group u of batch bt sits in weight slot (off + u) % PF, with
+  // off a compile-time constant in the unrolled loop below
+  auto batch = [&](int bt, int off) {
+    // the next batch into the slot of batch bt - 1, which every wave is done
+    // with (for every batch, so that every path through the loop issues the
+    // same loads and the compiler's waits for the weights stay exact; after
+    // the last batch it re-reads the last group)
+    copy_batch(bt + 1);
+    QOQ_COMPILER_FENCE();
+    const int8_t* slot = smem + (bt & 1) * kBatchBytes;
+    // Each group waits until its weights have landed: younger are the next
+    // PF - 1 groups' loads and the copies of every batch begun since its
+    // load was issued (PF groups earlier): for the batch's first
+    // min(PF, kRingBatch) groups, ceil(PF / kRingBatch) batches' copies.
+    constexpr int kFirst = PF < kRingBatch ? PF : kRingBatch;
+    constexpr int kCross = (PF + kRingBatch - 1) / kRingBatch;
+    static_for<kRingBatch>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      const int g = bt * kRingBatch + u;
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm((PF - 1) * kVec + (u < kFirst ? kCross * ncp : 0)));
+      __builtin_amdgcn_sched_barrier(0);  // the weights' uses stay behind the wait
+      compute(fa[u & 1], fm[u & 1], g, bq[(off + u) % PF]);
+      QOQ_COMPILER_FENCE();
+      load_b(g + PF, bq[(off + u) % PF]);
+      if constexpr (u + 1 < kRingBatch) read_next(fa[(u + 1) & 1], fm[(u + 1) & 1], slot, u + 1, g + 1);
+      QOQ_COMPILER_FENCE();
+    });
+    // the next batch's copies were issued before this batch's weight loads
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kRingBatch * kVec));
+    lds_barrier();
+    // the next batch's first group (past the last batch: its copies of the
+    // last group, never multiplied)
+    read_next(fa[0], fm[0], smem + ((bt + 1) & 1) * kBatchBytes, 0, (bt + 1) * kRingBatch);
+  };
+  // PF > kRingBatch: the weight ring turns over every PF / kRingBatch
+  // batches.  The plan keeps G a multiple of both, so that every batch is
+  // whole: the loop has no data-dependent branch, and the compiler's waits
+  // for the weight registers stay exact.
+  constexpr int kUnrollB = PF > kRingBatch ? PF / kRingBatch : 1;
+  for (int bt = 0; bt < nb; bt += kUnrollB) {
+#pragma unroll
+    for (int v = 0; v < kUnrollB; ++v) batch(bt + v, v * kRingBatch);
+  }
+  if (!live) return;
+
+  // epilogue: lane holds rows 16 i + 4 (lane / 16) + r, column lane % 16
+  const float sc = I32OUT ? 0.0f : col_scale(a, strip * 16 + c16);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    float sxv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sxv[r] = I32OUT ? 0.0f : row_scale(a, 16 * i + 4 * j + r);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) store_out<I32OUT>(a, 16 * i + 4 * j + r, strip * 16 + c16, acc[i][r], sxv[r], sc);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // gemm_large: M > 64 (prefill, compute-bound).  Block = WM x WN waves, wave
 // tile = TM*32 rows x TN*32 columns of v_mfma_i32_32x32x32_i8.
 //
@@ -764,12 +1014,6 @@ struct ATile {
 };
 
 
-// Barrier for LDS traffic only: this wave's LDS operations are complete
-// (lgkmcnt 0) and every wave has arrived.  Global loads stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xc07f);
-  __builtin_amdgcn_s_barrier();
-}
 
 // 16-byte weight loads per lane, per 32-column tile and group: UINT4 slots
 // (c16, hh) and (c16, 2+hh) hold K steps {0, 2} and {1, 3}; INT8 slots hold
@@ -1241,6 +1485,58 @@ inline bool plan_strip(int64_t M, int n_strips, int G, bool group_meta, int* spb
   return *lds <= kStripMaxLds;
 }
 
+// Row tiles of the ring kernel for M rows (M <= 64): 1, 2 or 4.
+constexpr int ring_tm(int64_t M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
+inline size_t ring_lds_bytes(int tm, int G, int spb, bool group_meta) {
+  const size_t meta = group_meta ? size_t(round_up(int64_t(spb) * round_up(G, 4) / 4 * 64, 1024)) : 0;
+  return 2 * size_t(kRingBatch) * size_t(tm) * 16 * 128 + meta;
+}
+// Up to 64 rows, the ring kernel when one strip per wave and at least
+// QOQ_RING_MIN_SPB strips per block still give about a block per CU (wide N:
+// the decode projections) and K is a whole number of batches (and of weight
+// rings); otherwise the K-split skinny kernel, whose waves share a strip's K
+// range.
+#ifndef QOQ_RING_MIN_SPB
+#define QOQ_RING_MIN_SPB 5
+#endif
+// groups of weights in flight per wave of the ring kernel
+#ifndef QOQ_RING_PF
+#define QOQ_RING_PF 4
+#endif
+constexpr int kRingGroupStep = QOQ_RING_PF > kRingBatch ? QOQ_RING_PF : kRingBatch;
+inline bool plan_ring(int64_t M, int n_strips, int G, bool group_meta, int* spb, size_t* lds) {
+  *spb = pick_skinny_tn(n_strips, 1, 8);
+  *lds = ring_lds_bytes(ring_tm(M), G, *spb, group_meta);
+  return *spb >= QOQ_RING_MIN_SPB && G % kRingGroupStep == 0 && *lds <= kStripMaxLds;
+}
+
+template <int TM, int SPB, int WF, bool I32>
+hipError_t launch_ring_spb(const GemmArgs& a, hipStream_t st) {
+  auto* fn = gemm_ring_kernel<TM, SPB, QOQ_RING_PF, WF, I32>;
+  const size_t lds = ring_lds_bytes(TM, a.G, SPB, wf_group_meta(WF));
+  if (lds > 64 * 1024) {
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(kStripMaxLds));
+    if (attr != hipSuccess) return attr;
+  }
+  const dim3 grid((a.n_strips + SPB - 1) / SPB);
+  hipLaunchKernelGGL(fn, grid, dim3(64 * SPB), lds, st, a);
+  return hipGetLastError();
+}
+// strips per block: QOQ_RING_MIN_SPB .. 8 (the plan's range; with fewer
+// strips a block leaves a SIMD with a single wave and the skinny kernel,
+// whose waves split K, is faster)
+template <int TM, int WF, bool I32>
+hipError_t launch_ring(const GemmArgs& a, int spb, hipStream_t st) {
+  static_assert(QOQ_RING_MIN_SPB >= 5, "ring blocks of 5 to 8 strips are instantiated");
+  switch (spb) {
+    case 5: return launch_ring_spb<TM, 5, WF, I32>(a, st);
+    case 6: return launch_ring_spb<TM, 6, WF, I32>(a, st);
+    case 7: return launch_ring_spb<TM, 7, WF, I32>(a, st);
+    default: return launch_ring_spb<TM, 8, WF, I32>(a, st);
+  }
+}
+
 // Large-M plans.  Tile 0: the big tile (128 x 512); tile 1: the small one
 // (64 x 256), for problems with fewer than 192 big tiles; tile 2: the K-set
 // tile (128 x 128), in place of the small one when every block runs at least
@@ -1304,7 +1600,7 @@ inline bool skinny_mid(int64_t M, int64_t N) {
 // per block (strip and skinny kernels) or the large-M tile (0 big, 1 small,
 // 2 K-set); ksplit: K parts per block (strip and skinny kernels) or K splits
 // across blocks (large kernel).
-enum GemmKernel { kPlanStrip = 0, kPlanSkinny16 = 1, kPlanSkinny32 = 2, kPlanSkinny64 = 3, kPlanLarge = 4 };
+enum GemmKernel { kPlanStrip = 0, kPlanSkinny16 = 1, kPlanSkinny32 = 2, kPlanSkinny64 = 3, kPlanLarge = 4, kPlanRing = 5 };
 struct GemmPlan {
   int kernel, tile, ksplit;
 };
@@ -1318,8 +1614,13 @@ inline GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool group_meta, bool
     int spb, sks;
     size_t lds;
     if (plan_strip(M, n_strips, G, group_meta, &spb, &sks, &lds)) return {kPlanStrip, spb, sks};
-    return {kPlanSkinny16, pick_skinny_tn(n_strips, int((M + 15) / 16), skinny_tn_max(1)), ks};
   }
+  if (M <= kSkinnyMaxM) {
+    int spb;
+    size_t lds;
+    if (plan_ring(M, n_strips, G, group_meta, &spb, &lds)) return {kPlanRing, spb, 1};
+  }
+  if (M <= 16) return {kPlanSkinny16, pick_skinny_tn(n_strips, int((M + 15) / 16), skinny_tn_max(1)), ks};
   if (M <= 32) return {kPlanSkinny32, pick_skinny_tn(n_strips, int((M + 31) / 32), skinny_tn_max(2)), ks};
   if (M <= kSkinnyMaxM || skinny_mid(M, N))
     return {kPlanSkinny64, pick_skinny_tn_rows(n_strips, int((M + 63) / 64), skinny_tn_max(4)), ks};
@@ -1367,6 +1668,12 @@ hipError_t dispatch(const GemmArgs& a0, void* ws, hipStream_t st) {
     case kPlanSkinny16: return launch_skinny_upto<1, WF, I32, skinny_tn_max(1)>(p.tile, p.ksplit, a0, st);
     case kPlanSkinny32: return launch_skinny_upto<2, WF, I32, skinny_tn_max(2)>(p.tile, p.ksplit, a0, st);
     case kPlanSkinny64: return launch_skinny_upto<4, WF, I32, skinny_tn_max(4)>(p.tile, p.ksplit, a0, st);
+    case kPlanRing: {
+      const int tm = ring_tm(a0.M);
+      if (tm == 1) return launch_ring<1, WF, I32>(a0, p.tile, st);
+      if (tm == 2) return launch_ring<2, WF, I32>(a0, p.tile, st);
+      return launch_ring<4, WF, I32>(a0, p.tile, st);
+    }
     default: break;
   }
   if (p.ksplit == 1) return launch_large_tile<WF, I32>(p.tile, a0, st);
