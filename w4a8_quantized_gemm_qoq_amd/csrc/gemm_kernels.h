@@ -1499,6 +1499,13 @@ inline size_t ring_lds_bytes(int tm, int G, int spb, bool group_meta) {
 #ifndef QOQ_RING_MIN_SPB
 #define QOQ_RING_MIN_SPB 5
 #endif
+// Longest per-wave chain (groups x row tiles) the ring kernel takes: a wave
+// runs all G groups of its strip in sequence, against G / 8 groups of seven
+// strips in the skinny kernel; past this the skinny kernel's shorter chains
+// win (64 x 16384 x 28672: 55 us skinny, 60 us ring).
+#ifndef QOQ_RING_MAX_WORK
+#define QOQ_RING_MAX_WORK 256
+#endif
 // groups of weights in flight per wave of the ring kernel
 #ifndef QOQ_RING_PF
 #define QOQ_RING_PF 4
@@ -1507,7 +1514,8 @@ constexpr int kRingGroupStep = QOQ_RING_PF > kRingBatch ? QOQ_RING_PF : kRingBat
 inline bool plan_ring(int64_t M, int n_strips, int G, bool group_meta, int* spb, size_t* lds) {
   *spb = pick_skinny_tn(n_strips, 1, 8);
   *lds = ring_lds_bytes(ring_tm(M), G, *spb, group_meta);
-  return *spb >= QOQ_RING_MIN_SPB && G % kRingGroupStep == 0 && *lds <= kStripMaxLds;
+  return *spb >= QOQ_RING_MIN_SPB && G % kRingGroupStep == 0 && G * ring_tm(M) <= QOQ_RING_MAX_WORK &&
+         *lds <= kStripMaxLds;
 }
 
 template <int TM, int SPB, int WF, bool I32>
