@@ -398,7 +398,75 @@ def measure_gemm(torch, q, w, X, W, reps: int, comparators: bool = False):
     return r
 
 
+def _counter_rows(d: str, counter: str):
+    """(kernel name, grid, dispatch id) -> summed value of one counter, from
+    the counter_collection CSV files rocprofv3 wrote under directory d."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") != counter:
+                    continue
+                key = (row["Kernel_Name"], int(row["Grid_Size"]), int(row["Dispatch_Id"]))
+                vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+    return vals
+
+
+def write_traffic(workload: str, fetch_dir: str, write_dir: str, commands: list[str]) -> dict:
+    """profiles/traffic_<workload>.json from the FETCH_SIZE and WRITE_SIZE
+    passes of `bench.py --workload <workload> --no-sweep --copy-calib-mb N`:
+    both counters in KiB per dispatch, scaled so that the run's device copy
+    of known size reads as its size fetched and written; summed over the GEMM
+    call's kernels, each the mean over its dispatches."""
+    import synthetic
+    w = synthetic.get_workload(workload)
+    fetch, write = _counter_rows(fetch_dir, "FETCH_SIZE"), _counter_rows(write_dir, "WRITE_SIZE")
+    copy_f = [v for (k, _, _), v in fetch.items() if "copyBuffer" in k]
+    copy_w = [v for (k, _, _), v in write.items() if "copyBuffer" in k]
+    calib_kib = max(copy_w)  # the largest copy is the calibration copy (read and write N bytes)
+    fs, ws = calib_kib / max(copy_f), 1.0 * calib_kib / max(copy_w)
+    kern = {}
+    for src, name in ((fetch, "fetch_kib"), (write, "write_kib")):
+        for (k, grid, _), v in src.items():
+            if "gemm_" in k or "splitk_reduce" in k:
+                short = k.replace("void ", "", 1).replace("qoq::(anonymous namespace)::", "").split("(")[0]
+                e = kern.setdefault((short, grid),
+                                    {"fetch_kib": [], "write_kib": []})
+                e[name].append(v)
+    rows = []
+    total = 0
+    for (k, grid), e in sorted(kern.items()):
+        f = sum(e["fetch_kib"]) / max(1, len(e["fetch_kib"]))
+        wv = sum(e["write_kib"]) / max(1, len(e["write_kib"]))
+        b = int(round((f * fs + wv * ws) * 1024))
+        total += b
+        rows.append({"kernel": k, "grid": grid, "dispatches": len(e["fetch_kib"]), "fetch_kib": round(f, 1),
+                     "write_kib": round(wv, 1), "bytes": b})
+    rec = {"workload": workload, "copy_fetch_kib": round(max(copy_f), 2), "copy_write_kib": round(max(copy_w), 2),
+           "fetch_scale": round(fs, 4), "write_scale": round(ws, 4), "kernels": rows,
+           "hbm_bytes_per_launch": total, "algorithmic_bytes": algo_bytes(w),
+           "ratio": round(total / algo_bytes(w), 3), "src_hash": src_hash(), "commands": commands,
+           "note": "hbm_bytes_per_launch = FETCH_SIZE x fetch_scale + WRITE_SIZE x write_scale (KiB -> bytes) over "
+                   "the GEMM call's kernels, mean over its dispatches; the scales make the run's device copy of known "
+                   "size read as that size fetched and written.  FETCH_SIZE counts L2 misses, served by the 256 MB "
+                   "last-level cache or by HBM."}
+    with open(os.path.join(ROOT, "profiles", f"traffic_{workload}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--traffic-from":
+        # bench.py --traffic-from WORKLOAD FETCH_DIR WRITE_DIR: host only, no GPU
+        wl, fd, wd = sys.argv[2:5]
+        cmd = ("rocprofv3 --pmc {c} --output-format csv -d {d} -o pmc -- python -u bench.py --workload {w} "
+               "--no-sweep --no-cpu-baseline --no-kv4 --copy-calib-mb 1024 --steps 5 --warmup 2 --kernel-reps 5")
+        rec = write_traffic(wl, fd, wd, [cmd.format(c="FETCH_SIZE", d=fd, w=wl), cmd.format(c="WRITE_SIZE", d=wd, w=wl)])
+        print(json.dumps({k: rec[k] for k in ("workload", "fetch_scale", "hbm_bytes_per_launch", "ratio")}))
+        return
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
