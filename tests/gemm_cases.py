@@ -30,6 +30,11 @@ SMALL = [
     (16, 10112, 40, 128, ('strip', 1, 8)),  # strip kernel: activations and metadata fill all 160 KB of LDS
     (16, 10240, 40, 128, ('skinny16', 1, 8)),  # one group more exceeds LDS: K-split skinny kernel instead
     (16, 2048, 20000, 128, ('strip', 5, 1)),  # strip kernel, 5 strips per block: second activation copy after the barrier
+    (8, 1024, 3000, 128, ('strip', 1, 8)),  # strip kernel, 8 rows: groups padded to 16 LDS rows, group-major copies, K in 8 parts
+    (15, 2048, 5000, 0, ('strip', 2, 4)),  # ... per-channel, 15 rows, 2 strips x 4 K parts
+    (13, 4096, 28672, 128, ('strip', 7, 1)),  # ... 13 rows, 7 strips per block (the decode layout), rows 13-15 repeat row 12
+    (9, 10112, 100, 128, ('strip', 1, 8)),  # ... 9 rows padded to 16: activations and metadata fill all 160 KB of LDS
+    (8, 10240, 100, 128, ('skinny16', 1, 8)),  # ... one group more exceeds LDS once padded: K-split skinny kernel instead
     (7, 1664, 17000, 0, ('strip', 5, 1)),  # ... per-channel, odd row count, copies running into padding
     (512, 256, 24576, 128, ('large', 0, 1)),  # big 128x512 tiles (192 of them), 2 groups
     (520, 384, 24400, 0, ('large', 0, 1)),  # ... per-channel, ragged M and N, 3 groups

@@ -669,6 +669,8 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
 // L = g*R + r stored at chunk q ^ ((L >> 1) & 7) (16 rows reading the same
 // chunk hit all 64 banks).
 __device__ __forceinline__ int round_up_lds(int bytes) { return (bytes + 1023) & ~1023; }
+// LDS rows per group of the strip kernel's activations for R token rows.
+__host__ __device__ constexpr int strip_rows_per_group(int r) { return r >= 8 ? 16 : r; }
 __device__ __forceinline__ int strip_lds_off(int lrow, int q) { return lrow * 128 + ((q ^ ((lrow >> 1) & 7)) << 4); }
 
 
@@ -692,16 +694,36 @@ __global__ __launch_bounds__(512) void gemm_strip_kernel(GemmArgs a, int spb, in
   uint32_t S = 0, C = 0;
   if constexpr (WF == kWfPerChannel) meta_perchannel(a.meta8[cstrip * 16 + c16], S, C);
 
-  // activations -> LDS.  Lane l of a wave-wide copy fills LDS chunk base + l;
-  // lanes past the end fetch a valid chunk into the allocation's padding.
-  const int n_chunks = a.G * R * 8;
-  for (int base = wave * 64; base < n_chunks; base += nwaves * 64) {
-    const int pc = min(base + lane, n_chunks - 1);
-    const int lrow = pc >> 3;
-    const int q = (pc & 7) ^ ((lrow >> 1) & 7);
-    const int g = lrow / R, r = lrow - g * R;
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(a.x8 + int64_t(r) * K + int64_t(g) * 128 + q * 16),
-                                     (__attribute__((address_space(3))) void*)(smem + base * 16), 16, 0, 0);
+  // activations -> LDS, RP rows per group.  Lane l of a wave-wide copy fills
+  // LDS chunk base + l.  From 8 rows on, groups take 16 rows (rows R..15
+  // repeat row R-1, never stored) and every copy moves 8 rows of one group:
+  // the lane's offset is loop-invariant and the group a wave-uniform
+  // soffset, so the copies cost no vector ALU work before the weight stream
+  // starts.  Fewer rows pack the groups densely (lanes past the end fetch a
+  // valid chunk into the allocation's padding).
+  const int RP = strip_rows_per_group(R);
+  const int n_chunks = a.G * RP * 8;
+  if (RP == 16) {
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x8, R * int(K));
+    int coff[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int lrow = (lane >> 3) + 8 * h;
+      coff[h] = min(lrow, R - 1) * int(K) + (((lane & 7) ^ ((lrow >> 1) & 7)) << 4);
+    }
+    for (int c = wave; c < 2 * a.G; c += nwaves) {
+      const int g = c >> 1;
+      buf_load_lds16(xr, smem + (g * 16 + 8 * (c & 1)) * 128, (c & 1) ? coff[1] : coff[0], g * 128);
+    }
+  } else {
+    for (int base = wave * 64; base < n_chunks; base += nwaves * 64) {
+      const int pc = min(base + lane, n_chunks - 1);
+      const int lrow = pc >> 3;
+      const int q = (pc & 7) ^ ((lrow >> 1) & 7);
+      const int g = lrow / R, r = lrow - g * R;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(a.x8 + int64_t(r) * K + int64_t(g) * 128 + q * 16),
+                                       (__attribute__((address_space(3))) void*)(smem + base * 16), 16, 0, 0);
+    }
   }
   // group metadata of the block's strips -> LDS, after the activations (the
   // strips' metadata is one contiguous run of G4q * 64 bytes per strip)
@@ -744,7 +766,7 @@ __global__ __launch_bounds__(512) void gemm_strip_kernel(GemmArgs a, int spb, in
   v4i acc = {0, 0, 0, 0};
   auto compute = [&](int g, const u32x4 (&bc)[kVec]) {
     if constexpr (wf_group_meta(WF)) meta_g128<WF>((lmeta[(g >> 2) * 16] >> (8 * (g & 3))) & 0xffu, S, C);
-    const int lrow = g * R + ra;
+    const int lrow = g * RP + ra;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const v4i af = *reinterpret_cast<const v4i*>(smem + strip_lds_off(lrow, j + 4 * h));
@@ -846,20 +868,30 @@ __global__ __launch_bounds__(64 * SPB) void gemm_ring_kernel(GemmArgs a) {
   // last 64 chunks repeats them: the same bytes to the same place), so the
   // compiler's waits for the weight registers and the hand-counted waits
   // below are exact for every wave.  Rows past M read row M-1 (never
-  // stored); groups past K read the last group (never multiplied).
+  // stored).  One descriptor over the M activation rows: the per-lane offsets
+  // of the ncp copies are loop-invariant and the batch is a wave-uniform
+  // soffset, so the copies cost no vector ALU work (the plan keeps G a
+  // multiple of kRingBatch, so every batch is whole; the copy issued after
+  // the last batch re-reads it, never multiplied).
   constexpr int ncp = (kBatchChunks / 64 + spb - 1) / spb;
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x8, int(int64_t(a.M) * K));
+  int coff[ncp];
+#pragma unroll
+  for (int k = 0; k < ncp; ++k) {
+    const int base = min((k * spb + wave) * 64, kBatchChunks - 64);
+    const int pc = base + lane;
+    const int lrow = pc >> 3;
+    const int q = (pc & 7) ^ ((lrow >> 1) & 7);
+    const int u = lrow / R, r = lrow - u * R;
+    coff[k] = min(r, a.M - 1) * int(K) + u * 128 + q * 16;
+  }
   auto copy_batch = [&](int bt) {
     int8_t* dst = smem + (bt & 1) * kBatchBytes;
+    const int soff = min(bt, nb - 1) * (kRingBatch * 128);
 #pragma unroll
     for (int k = 0; k < ncp; ++k) {
       const int base = min((k * spb + wave) * 64, kBatchChunks - 64);
-      const int pc = base + lane;
-      const int lrow = pc >> 3;
-      const int q = (pc & 7) ^ ((lrow >> 1) & 7);
-      const int u = lrow / R, r = lrow - u * R;
-      const int g = min(bt * kRingBatch + u, G - 1);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(a.x8 + int64_t(min(r, a.M - 1)) * K + int64_t(g) * 128 + q * 16),
-                                       (__attribute__((address_space(3))) void*)(dst + base * 16), 16, 0, 0);
+      buf_load_lds16(xrs, dst + base * 16, coff[k], soff);
     }
   };
   // group metadata of the block's strips, after the ring (one contiguous run
@@ -1451,7 +1483,7 @@ hipError_t launch_skinny_upto(int tn, int ks, const GemmArgs& a, hipStream_t st)
 // Dynamic LDS of the strip kernel: the activations, or the K-part partial
 // sums, whichever is larger.
 inline size_t strip_lds_bytes(int G, int R, int spb, int ks, bool group_meta) {
-  const size_t act = size_t(round_up(int64_t(G) * R * 8 * 16, 1024));
+  const size_t act = size_t(round_up(int64_t(G) * strip_rows_per_group(R) * 8 * 16, 1024));
   const size_t meta = group_meta ? size_t(round_up(int64_t(spb) * round_up(G, 4) / 4 * 64, 1024)) : 0;
   const size_t red = size_t(spb) * size_t(ks - 1) * 1024;
   return act + meta > red ? act + meta : red;
