@@ -34,7 +34,10 @@ SMALL = [
     (15, 2048, 5000, 0, ('strip', 2, 4)),  # ... per-channel, 15 rows, 2 strips x 4 K parts
     (13, 4096, 28672, 128, ('strip', 7, 1)),  # ... 13 rows, 7 strips per block (the decode layout), rows 13-15 repeat row 12
     (9, 10112, 100, 128, ('strip', 1, 8)),  # ... 9 rows padded to 16: activations and metadata fill all 160 KB of LDS
-    (8, 10240, 100, 128, ('skinny16', 1, 8)),  # ... one group more exceeds LDS once padded: K-split skinny kernel instead
+    (8, 10240, 100, 128, ('strip', 1, 8)),  # ... one group more: 8 rows keep the dense layout (padded would exceed LDS)
+    (8, 14336, 4096, 0, ('strip', 1, 8)),  # ... dense 8-row groups at K = 14336 (the 8B down projection), per-channel
+    (15, 10752, 100, 128, ('strip', 1, 8)),  # ... 15 dense rows fill the LDS
+    (15, 10880, 100, 128, ('skinny16', 1, 8)),  # ... one group more: neither layout fits, K-split skinny kernel instead
     (7, 1664, 17000, 0, ('strip', 5, 1)),  # ... per-channel, odd row count, copies running into padding
     (512, 256, 24576, 128, ('large', 0, 1)),  # big 128x512 tiles (192 of them), 2 groups
     (520, 384, 24400, 0, ('large', 0, 1)),  # ... per-channel, ragged M and N, 3 groups

@@ -669,13 +669,11 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
 // L = g*R + r stored at chunk q ^ ((L >> 1) & 7) (16 rows reading the same
 // chunk hit all 64 banks).
 __device__ __forceinline__ int round_up_lds(int bytes) { return (bytes + 1023) & ~1023; }
-// LDS rows per group of the strip kernel's activations for R token rows.
-__host__ __device__ constexpr int strip_rows_per_group(int r) { return r >= 8 ? 16 : r; }
 __device__ __forceinline__ int strip_lds_off(int lrow, int q) { return lrow * 128 + ((q ^ ((lrow >> 1) & 7)) << 4); }
 
 
 template <int PF, int WF, bool I32OUT>
-__global__ __launch_bounds__(512) void gemm_strip_kernel(GemmArgs a, int spb, int ks) {
+__global__ __launch_bounds__(512) void gemm_strip_kernel(GemmArgs a, int spb, int ks, int rp) {
   extern __shared__ __align__(16) int8_t smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -694,14 +692,14 @@ __global__ __launch_bounds__(512) void gemm_strip_kernel(GemmArgs a, int spb, in
   uint32_t S = 0, C = 0;
   if constexpr (WF == kWfPerChannel) meta_perchannel(a.meta8[cstrip * 16 + c16], S, C);
 
-  // activations -> LDS, RP rows per group.  Lane l of a wave-wide copy fills
-  // LDS chunk base + l.  From 8 rows on, groups take 16 rows (rows R..15
-  // repeat row R-1, never stored) and every copy moves 8 rows of one group:
-  // the lane's offset is loop-invariant and the group a wave-uniform
+  // activations -> LDS, RP = rp rows per group (16 or R, from the launch).
+  // Lane l of a wave-wide copy fills LDS chunk base + l.  With 16 rows a group
+  // (rows R..15 repeat row R-1, never stored) every copy moves 8 rows of one
+  // group: the lane's offset is loop-invariant and the group a wave-uniform
   // soffset, so the copies cost no vector ALU work before the weight stream
-  // starts.  Fewer rows pack the groups densely (lanes past the end fetch a
+  // starts.  Groups of R rows are packed densely (lanes past the end fetch a
   // valid chunk into the allocation's padding).
-  const int RP = strip_rows_per_group(R);
+  const int RP = rp;
   const int n_chunks = a.G * RP * 8;
   if (RP == 16) {
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x8, R * int(K));
@@ -1482,13 +1480,21 @@ hipError_t launch_skinny_upto(int tn, int ks, const GemmArgs& a, hipStream_t st)
 
 // Dynamic LDS of the strip kernel: the activations, or the K-part partial
 // sums, whichever is larger.
-inline size_t strip_lds_bytes(int G, int R, int spb, int ks, bool group_meta) {
-  const size_t act = size_t(round_up(int64_t(G) * strip_rows_per_group(R) * 8 * 16, 1024));
+constexpr size_t kStripMaxLds = 160 * 1024;
+inline size_t strip_lds_bytes_rows(int G, int rp, int spb, int ks, bool group_meta) {
+  const size_t act = size_t(round_up(int64_t(G) * rp * 8 * 16, 1024));
   const size_t meta = group_meta ? size_t(round_up(int64_t(spb) * round_up(G, 4) / 4 * 64, 1024)) : 0;
   const size_t red = size_t(spb) * size_t(ks - 1) * 1024;
   return act + meta > red ? act + meta : red;
 }
-constexpr size_t kStripMaxLds = 160 * 1024;
+// LDS rows per group of the strip kernel's activations for R token rows: 16
+// (group-major copies) from 8 rows on when that fits, else R (dense).
+inline int strip_rows(int G, int R, int spb, int ks, bool group_meta) {
+  return R >= 8 && strip_lds_bytes_rows(G, 16, spb, ks, group_meta) <= kStripMaxLds ? 16 : R;
+}
+inline size_t strip_lds_bytes(int G, int R, int spb, int ks, bool group_meta) {
+  return strip_lds_bytes_rows(G, strip_rows(G, R, spb, ks, group_meta), spb, ks, group_meta);
+}
 
 template <int WF, bool I32>
 hipError_t launch_strip(const GemmArgs& a, int spb, int ks, size_t lds, hipStream_t st) {
@@ -1500,7 +1506,8 @@ hipError_t launch_strip(const GemmArgs& a, int spb, int ks, size_t lds, hipStrea
     if (attr != hipSuccess) return attr;
   }
   const dim3 grid((a.n_strips + spb - 1) / spb);
-  hipLaunchKernelGGL(fn, grid, dim3(64 * spb * ks), lds, st, a, spb, ks);
+  const int rp = strip_rows(a.G, a.M < 16 ? a.M : 16, spb, ks, wf_group_meta(WF));
+  hipLaunchKernelGGL(fn, grid, dim3(64 * spb * ks), lds, st, a, spb, ks, rp);
   return hipGetLastError();
 }
 
