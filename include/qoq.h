@@ -245,13 +245,15 @@ QOQ_API int qoq_w4a8_gemm_i32(const int8_t* x8, const void* qweight, const void*
  * Launch plan qoq_w4a8_gemm takes for a shape (host, no GPU work), for tests
  * and tuning.  kernel: 0 strip kernel (up to 16 rows, activations in LDS),
  * 1 / 2 / 3 skinny kernel with 16- / 32- / 64-row tiles, 4 large-M kernel,
- * 5 ring kernel (up to 64 rows, one strip per wave over the whole K range,
- * activations through an LDS ring of 8-group batches; wide N, K a multiple
- * of 1024).  tile: strips per workgroup (kernels 0-3 and 5) or the large-M
- * block tile (0: 128 x 512, 1: 64 x 256, 2: 128 x 128 with K split inside
- * the block).  ksplit: K parts per workgroup (kernels 0-3: waves that split
- * the K groups and sum their partials in LDS; 1 for kernel 5) or K splits
- * across workgroups with a reduction (kernel 4).  Same argument checks as
+ * 5 ring kernel (up to 64 rows, a strip's K range streamed by one wave, or,
+ * up to 32 rows and from 64 groups on, by two waves taking one half each;
+ * activations through an LDS ring of group batches; wide N, K a multiple of
+ * 1024).  tile: strips
+ * per workgroup (kernels 0-3 and 5) or the large-M block tile (0: 128 x 512,
+ * 1: 64 x 256, 2: 128 x 128 with K split inside the block).  ksplit: K parts
+ * per workgroup (kernels 0-3: waves that split the K groups and sum their
+ * partials in LDS; kernel 5: 1 or 2 waves a strip) or K splits across
+ * workgroups with a reduction (kernel 4).  Same argument checks as
  * qoq_w4a8_gemm.
  */
 QOQ_API int qoq_w4a8_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t* kernel,

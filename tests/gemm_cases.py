@@ -64,7 +64,13 @@ SMALL = [
     (40, 1024, 20000, 128, ('ring', 5, 1)),  # ring kernel (one strip per wave, activations through an LDS ring): one batch of 8 groups
     (33, 2048, 28000, 0, ('ring', 7, 1)),  # ... per-channel, two batches, rows past M
     (24, 5120, 24000, 128, ('ring', 6, 1)),  # ... 32-row tiles, five batches
-    (16, 10240, 20000, 128, ('ring', 5, 1)),  # ... 16-row tiles where the strip kernel's LDS is too small, ten batches
+    (16, 10240, 20000, 128, ('ring', 5, 2)),  # ... 16-row tiles where the strip kernel's LDS is too small: two waves a strip (K halves)
     (64, 1024, 32768, 128, ('ring', 8, 1)),  # ... eight strips per block (256 blocks)
     (60, 3072, 17000, 0, ('ring', 5, 1)),  # ... per-channel, three batches, dead waves past N in the last block
+    (48, 8192, 20000, 0, ('ring', 5, 1)),  # ring kernel, 64-row tiles at 64 groups: one wave a strip, per-channel
+    (64, 8192, 17000, 128, ('ring', 5, 1)),  # ... 64 rows, 8 batches, dead waves past N in the last block
+    (20, 8192, 24000, 128, ('ring', 6, 2)),  # ring kernel, K halves over two waves a strip (64 groups on, up to 32 rows)
+    (24, 8192, 20000, 0, ('ring', 5, 2)),  # ... per-channel, 32-row tiles, rows past M
+    (12, 16384, 20000, 0, ('ring', 5, 2)),  # ... per-channel, 16-row tiles (neither strip layout fits LDS)
+    (30, 8192, 32768, 128, ('ring', 8, 2)),  # ... 8 strips a block (16 waves)
 ]

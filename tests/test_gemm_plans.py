@@ -1,9 +1,9 @@
 """Launch plans of the W4A8 GEMM (host query, no GPU): every parity shape
 reaches the plan pinned for it in gemm_cases.py, and together the shapes
 reach every kernel variant -- the strip kernel with one and several strips
-per block and with K parts, the ring kernel, the skinny kernel with 16-, 32-
-and 64-row tiles and 4 or 8 K parts per block, and the three large-M tiles
-with and without a K split."""
+per block and with K parts, the ring kernel with one and two waves a strip,
+the skinny kernel with 16-, 32- and 64-row tiles and 4 or 8 K parts per
+block, and the three large-M tiles with and without a K split."""
 
 import pytest
 
@@ -20,7 +20,7 @@ def test_parity_shapes_reach_every_kernel_variant():
     plans = {c[-1] for c in SMALL}
     kinds = {(k, t if k == "large" else None, s > 1) for k, t, s in plans}
     want = {("strip", None, True), ("strip", None, False), ("skinny16", None, True),
-            ("skinny32", None, True), ("skinny64", None, True), ("ring", None, False)}
+            ("skinny32", None, True), ("skinny64", None, True), ("ring", None, False), ("ring", None, True)}
     want |= {("large", t, False) for t in (0, 1, 2)} | {("large", t, True) for t in (1, 2)}
     assert want <= kinds, sorted(want - kinds)
     # the skinny kernel with several strips per block, with 4 and with 8 K
@@ -33,9 +33,12 @@ def test_parity_shapes_reach_every_kernel_variant():
     # the ring kernel with 16-, 32- and 64-row tiles, both weight formats, and
     # one, several and a partial last batch of groups
     ring = [c for c in SMALL if c[-1][0] == "ring"]
-    assert {(m + 15) // 16 if m <= 16 else (2 if m <= 32 else 4) for m, *_ in ring} == {1, 2, 4}
-    assert {c[3] for c in ring} == {0, 128}
-    assert {k // 1024 for _, k, *_ in ring} >= {1, 2, 3, 5, 10}
+    tiles = lambda cs: {(m + 15) // 16 if m <= 16 else (2 if m <= 32 else 4) for m, *_ in cs}
+    ring1 = [c for c in ring if c[-1][2] == 1]
+    ring2 = [c for c in ring if c[-1][2] == 2]
+    assert tiles(ring1) == {2, 4} and tiles(ring2) == {1, 2}
+    assert {c[3] for c in ring1} == {0, 128} and {c[3] for c in ring2} == {0, 128}
+    assert {k // 1024 for _, k, *_ in ring1} >= {1, 2, 3, 5}
     assert {t for *_, (k, t, _) in ring} == {5, 6, 7, 8}
 
 

@@ -1020,6 +1020,171 @@ __global__ __launch_bounds__(64 * SPB) void gemm_ring_kernel(GemmArgs a) {
   }
 }
 
+// ring2: the ring kernel with each strip's K range split over two waves
+// (2 SPB waves a block, halves h = 0, 1 of the groups), so a CU holds twice
+// the waves to hide each one's latency.  Both halves' activations pass
+// through their own LDS ring of two batches of kRing2Batch groups (the block
+// copies batch bt + 1 of both halves during batch bt, one barrier a batch);
+// the halves' INT32 accumulators are added exactly through LDS at the end.
+constexpr int kRing2Batch = 4;
+constexpr int ring2_batch_bytes(int tm) { return 2 * kRing2Batch * tm * 16 * 128; }  // both halves
+
+template <int TM, int SPB, int PF, int WF, bool I32OUT>
+__global__ __launch_bounds__(128 * SPB) void gemm_ring2_kernel(GemmArgs a) {
+  static_assert(PF == kRing2Batch, "one weight ring turn per batch");
+  constexpr int NW = 2 * SPB;                             // waves
+  constexpr int R = TM * 16;
+  constexpr int kHalfChunks = kRing2Batch * R * 8;        // 16-byte chunks per batch and half
+  constexpr int kBatchChunks = 2 * kHalfChunks;
+  constexpr int kBatchBytes = ring2_batch_bytes(TM);
+  constexpr int ncp = (kBatchChunks / 64 + NW - 1) / NW;  // copies per wave per batch
+  static_assert(PF * wf_vec(WF) + ncp <= 63 && kRing2Batch * wf_vec(WF) <= 63, "vmcnt holds at most 63");
+  extern __shared__ __align__(16) int8_t smem[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int ws = wave % SPB, hk = wave / SPB;             // strip of the block, K half
+  const int sb = blockIdx.x * SPB;
+  const int strip = sb + ws;
+  const bool live = strip < a.n_strips;
+  const int cstrip = min(strip, a.n_strips - 1);
+  const int c16 = lane & 15, j = lane >> 4;
+  const int G = a.G, Gh = G / 2;                          // the plan keeps G a multiple of 2 kRing2Batch
+  const int64_t K = int64_t(G) * 128;
+  const int nb = Gh / kRing2Batch;
+
+  // Copies: chunk pc of a batch belongs to half pc / kHalfChunks, group u and
+  // row r of it; every wave issues ncp copies (a wave past the last chunks
+  // repeats them).  One descriptor over the M rows, loop-invariant lane
+  // offsets, the batch a wave-uniform soffset; rows past M read row M-1.
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x8, int(int64_t(a.M) * K));
+  int coff[ncp];
+#pragma unroll
+  for (int k = 0; k < ncp; ++k) {
+    const int base = min((k * NW + wave) * 64, kBatchChunks - 64);
+    const int pc = base + lane;
+    const int half = pc / kHalfChunks, ph = pc - half * kHalfChunks;
+    const int lrow = ph >> 3;
+    const int q = (ph & 7) ^ ((lrow >> 1) & 7);
+    const int u = lrow / R, r = lrow - u * R;
+    coff[k] = min(r, a.M - 1) * int(K) + (half * Gh + u) * 128 + q * 16;
+  }
+  auto copy_batch = [&](int bt) {
+    int8_t* dst = smem + (bt & 1) * kBatchBytes;
+    const int soff = min(bt, nb - 1) * (kRing2Batch * 128);
+#pragma unroll
+    for (int k = 0; k < ncp; ++k) {
+      const int base = min((k * NW + wave) * 64, kBatchChunks - 64);
+      buf_load_lds16(xrs, dst + base * 16, coff[k], soff);
+    }
+  };
+  int8_t* meta_lds = smem + 2 * kBatchBytes;
+  if constexpr (wf_group_meta(WF)) {
+    const int m_chunks = min(SPB, a.n_strips - sb) * a.G4q * 4;
+    const int m_last = ((m_chunks - 1) >> 6) << 6;
+    const int nmp = ((m_chunks + 63) / 64 + NW - 1) / NW;
+    const int8_t* msrc = reinterpret_cast<const int8_t*>(a.meta) + int64_t(sb) * a.G4q * 64;
+    for (int k = 0; k < nmp; ++k) {
+      const int base = min((k * NW + wave) * 64, m_last);
+      const int pc = min(base + lane, m_chunks - 1);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(msrc + pc * 16),
+                                       (__attribute__((address_space(3))) void*)(meta_lds + base * 16), 16, 0, 0);
+    }
+  }
+  const uint32_t* lmeta = reinterpret_cast<const uint32_t*>(meta_lds) + ws * a.G4q * 16 + c16;
+
+  constexpr int kVec = wf_vec(WF);
+  constexpr int kBlk = wf_block_bytes(WF);
+  const int strip_bytes = G * kBlk;
+  const int g0 = hk * Gh;  // first group of this wave's half
+  const __amdgpu_buffer_rsrc_t wrs =
+      make_rsrc(reinterpret_cast<const int8_t*>(a.qw) + int64_t(cstrip) * strip_bytes, live ? strip_bytes : 0);
+  u32x4 bq[PF][kVec];
+  auto load_b = [&](int g, u32x4 (&b)[kVec]) {  // g: group within the half
+#pragma unroll
+    for (int v = 0; v < kVec; ++v)
+      b[v] = buf_load16<kCacheStream>(wrs, lane * 16 + v * 1024 + (g < Gh ? (g0 + g) * kBlk : kDeadOffset));
+  };
+  uint32_t S = 0, C = 0;
+  if constexpr (WF == kWfPerChannel) meta_perchannel(a.meta8[cstrip * 16 + c16], S, C);
+
+  copy_batch(0);
+  QOQ_COMPILER_FENCE();
+#pragma unroll
+  for (int p = 0; p < PF; ++p) load_b(p, bq[p]);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(PF * kVec));
+  __builtin_amdgcn_s_barrier();
+  QOQ_COMPILER_FENCE();
+
+  v4i acc[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) acc[i] = v4i{0, 0, 0, 0};
+  v4i fa[2][2][TM];
+  uint32_t fm[2];
+  const int hoff = hk * (kHalfChunks * 16);  // this half's tiles within a batch slot
+  auto read_next = [&](v4i (&af)[2][TM], uint32_t& mw, const int8_t* slot, int u, int g) {
+    read_group_frags<TM>(af, mw, slot + hoff + strip_lds_off(u * R + c16, j), slot + hoff + strip_lds_off(u * R + c16, j + 4),
+                         wf_group_meta(WF) ? lmeta + ((g0 + min(g, Gh - 1)) >> 2) * 16 : reinterpret_cast<const uint32_t*>(slot));
+  };
+  auto compute = [&](const v4i (&af)[2][TM], uint32_t mw, int g, const u32x4 (&bc)[kVec]) {
+    if constexpr (wf_group_meta(WF)) meta_g128<WF>((mw >> (8 * ((g0 + g) & 3))) & 0xffu, S, C);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const v4i bf = b_op16<WF>(bc, h, S, C);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[h][i], bf, acc[i], 0, 0, 0);
+    }
+  };
+  static_assert(kRing2Batch % 2 == 0, "fragment buffers alternate within a batch");
+  read_next(fa[0], fm[0], smem, 0, 0);
+  for (int bt = 0; bt < nb; ++bt) {
+    copy_batch(bt + 1);
+    QOQ_COMPILER_FENCE();
+    const int8_t* slot = smem + (bt & 1) * kBatchBytes;
+    // each group waits for its weights: younger are the next PF - 1 groups'
+    // loads and this batch's copies (the weights of a batch's groups were
+    // loaded during the batch before)
+    static_for<kRing2Batch>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      const int g = bt * kRing2Batch + u;
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm((PF - 1) * kVec + ncp));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(fa[u & 1], fm[u & 1], g, bq[u]);
+      QOQ_COMPILER_FENCE();
+      load_b(g + PF, bq[u]);
+      if constexpr (u + 1 < kRing2Batch) read_next(fa[(u + 1) & 1], fm[(u + 1) & 1], slot, u + 1, g + 1);
+      QOQ_COMPILER_FENCE();
+    });
+    // the next batch's copies were issued before this batch's weight loads
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kRing2Batch * kVec));
+    lds_barrier();
+    read_next(fa[0], fm[0], smem + ((bt + 1) & 1) * kBatchBytes, 0, (bt + 1) * kRing2Batch);
+  }
+
+  // the trailing copies land, then half 1 parks its accumulators (16-byte
+  // records [strip][i][lane]) and half 0 adds them
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+  v4i* red = reinterpret_cast<v4i*>(smem);
+  if (hk == 1) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) red[(ws * TM + i) * 64 + lane] = acc[i];
+  }
+  __syncthreads();
+  if (hk == 1 || !live) return;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) acc[i] += red[(ws * TM + i) * 64 + lane];
+
+  const float sc = I32OUT ? 0.0f : col_scale(a, strip * 16 + c16);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    float sxv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sxv[r] = I32OUT ? 0.0f : row_scale(a, 16 * i + 4 * j + r);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) store_out<I32OUT>(a, 16 * i + 4 * j + r, strip * 16 + c16, acc[i][r], sxv[r], sc);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // gemm_large: M > 64 (prefill, compute-bound).  Block = WM x WN waves, wave
 // tile = TM*32 rows x TN*32 columns of v_mfma_i32_32x32x32_i8.
@@ -1550,15 +1715,37 @@ inline size_t ring_lds_bytes(int tm, int G, int spb, bool group_meta) {
 #define QOQ_RING_PF 4
 #endif
 constexpr int kRingGroupStep = QOQ_RING_PF > kRingBatch ? QOQ_RING_PF : kRingBatch;
-inline bool plan_ring(int64_t M, int n_strips, int G, bool group_meta, int* spb, size_t* lds) {
+// From QOQ_RING2_MIN_G groups on, and for row tiles of up to 32 rows, the
+// ring kernel splits each strip's K range over two waves (gemm_ring2_kernel,
+// reported as 2 K parts): twice the waves a CU for the same work.  Shorter K
+// keeps one wave a strip (a half would run a single batch), and so do 64-row
+// tiles (even against one wave a strip across boxes).
+#ifndef QOQ_RING2_MIN_G
+#define QOQ_RING2_MIN_G 64
+#endif
+inline size_t ring2_lds_bytes(int tm, int G, int spb, bool group_meta) {
+  const size_t meta = group_meta ? size_t(round_up(int64_t(spb) * round_up(G, 4) / 4 * 64, 1024)) : 0;
+  return 2 * size_t(ring2_batch_bytes(tm)) + meta;
+}
+inline bool plan_ring(int64_t M, int n_strips, int G, bool group_meta, int* spb, int* ks, size_t* lds) {
   *spb = pick_skinny_tn(n_strips, 1, 8);
-  *lds = ring_lds_bytes(ring_tm(M), G, *spb, group_meta);
+  *ks = G >= QOQ_RING2_MIN_G && G % (2 * kRing2Batch) == 0 && ring_tm(M) <= 2 ? 2 : 1;
+  *lds = *ks == 2 ? ring2_lds_bytes(ring_tm(M), G, *spb, group_meta) : ring_lds_bytes(ring_tm(M), G, *spb, group_meta);
   return *spb >= QOQ_RING_MIN_SPB && G % kRingGroupStep == 0 && G * ring_tm(M) <= QOQ_RING_MAX_WORK &&
          *lds <= kStripMaxLds;
 }
 
 template <int TM, int SPB, int WF, bool I32>
-hipError_t launch_ring_spb(const GemmArgs& a, hipStream_t st) {
+hipError_t launch_ring_spb(const GemmArgs& a, int ks, hipStream_t st) {
+  if (ks == 2) {
+    auto* f2 = gemm_ring2_kernel<TM, SPB, kRing2Batch, WF, I32>;
+    static const hipError_t attr2 = hipFuncSetAttribute(reinterpret_cast<const void*>(f2),
+                                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(kStripMaxLds));
+    if (attr2 != hipSuccess) return attr2;
+    hipLaunchKernelGGL(f2, dim3((a.n_strips + SPB - 1) / SPB), dim3(128 * SPB),
+                       ring2_lds_bytes(TM, a.G, SPB, wf_group_meta(WF)), st, a);
+    return hipGetLastError();
+  }
   auto* fn = gemm_ring_kernel<TM, SPB, QOQ_RING_PF, WF, I32>;
   const size_t lds = ring_lds_bytes(TM, a.G, SPB, wf_group_meta(WF));
   if (lds > 64 * 1024) {
@@ -1574,13 +1761,13 @@ hipError_t launch_ring_spb(const GemmArgs& a, hipStream_t st) {
 // strips a block leaves a SIMD with a single wave and the skinny kernel,
 // whose waves split K, is faster)
 template <int TM, int WF, bool I32>
-hipError_t launch_ring(const GemmArgs& a, int spb, hipStream_t st) {
+hipError_t launch_ring(const GemmArgs& a, int spb, int ks, hipStream_t st) {
   static_assert(QOQ_RING_MIN_SPB >= 5, "ring blocks of 5 to 8 strips are instantiated");
   switch (spb) {
-    case 5: return launch_ring_spb<TM, 5, WF, I32>(a, st);
-    case 6: return launch_ring_spb<TM, 6, WF, I32>(a, st);
-    case 7: return launch_ring_spb<TM, 7, WF, I32>(a, st);
-    default: return launch_ring_spb<TM, 8, WF, I32>(a, st);
+    case 5: return launch_ring_spb<TM, 5, WF, I32>(a, ks, st);
+    case 6: return launch_ring_spb<TM, 6, WF, I32>(a, ks, st);
+    case 7: return launch_ring_spb<TM, 7, WF, I32>(a, ks, st);
+    default: return launch_ring_spb<TM, 8, WF, I32>(a, ks, st);
   }
 }
 
@@ -1663,9 +1850,9 @@ inline GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool group_meta, bool
     if (plan_strip(M, n_strips, G, group_meta, &spb, &sks, &lds)) return {kPlanStrip, spb, sks};
   }
   if (M <= kSkinnyMaxM) {
-    int spb;
+    int spb, rks;
     size_t lds;
-    if (plan_ring(M, n_strips, G, group_meta, &spb, &lds)) return {kPlanRing, spb, 1};
+    if (plan_ring(M, n_strips, G, group_meta, &spb, &rks, &lds)) return {kPlanRing, spb, rks};
   }
   if (M <= 16) return {kPlanSkinny16, pick_skinny_tn(n_strips, int((M + 15) / 16), skinny_tn_max(1)), ks};
   if (M <= 32) return {kPlanSkinny32, pick_skinny_tn(n_strips, int((M + 31) / 32), skinny_tn_max(2)), ks};
@@ -1717,9 +1904,9 @@ hipError_t dispatch(const GemmArgs& a0, void* ws, hipStream_t st) {
     case kPlanSkinny64: return launch_skinny_upto<4, WF, I32, skinny_tn_max(4)>(p.tile, p.ksplit, a0, st);
     case kPlanRing: {
       const int tm = ring_tm(a0.M);
-      if (tm == 1) return launch_ring<1, WF, I32>(a0, p.tile, st);
-      if (tm == 2) return launch_ring<2, WF, I32>(a0, p.tile, st);
-      return launch_ring<4, WF, I32>(a0, p.tile, st);
+      if (tm == 1) return launch_ring<1, WF, I32>(a0, p.tile, p.ksplit, st);
+      if (tm == 2) return launch_ring<2, WF, I32>(a0, p.tile, p.ksplit, st);
+      return launch_ring<4, WF, I32>(a0, p.tile, p.ksplit, st);
     }
     default: break;
   }
