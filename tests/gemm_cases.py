@@ -73,4 +73,6 @@ SMALL = [
     (24, 8192, 20000, 0, ('ring', 5, 2)),  # ... per-channel, 32-row tiles, rows past M
     (12, 16384, 20000, 0, ('ring', 5, 2)),  # ... per-channel, 16-row tiles (neither strip layout fits LDS)
     (30, 8192, 32768, 128, ('ring', 8, 2)),  # ... 8 strips a block (16 waves)
+    (20, 8192, 17000, 0, ('ring', 5, 2)),  # ... per-channel, ragged N: the last block has 3 live strips (4 dead waves)
+    (16, 12288, 17000, 128, ('ring', 5, 2)),  # ... 16-row tiles, 96 groups, ragged N
 ]
