@@ -18,7 +18,9 @@ torch = pytest.importorskip("torch")
                                    (300, 2048, 96),     # large kernel, K split over blocks + reduction
                                    (520, 512, 24576),   # big 128x512 tiles
                                    (1024, 8320, 4096),  # K-set 128x128 tile, odd group count
-                                   (16, 2048, 20000)])  # strip kernel
+                                   (16, 2048, 20000),   # strip kernel (16-row groups)
+                                   (40, 1024, 20000),   # ring kernel, one wave a strip
+                                   (20, 8192, 24000)])  # ring kernel, two waves a strip
 def test_quant_gemm_graph_replays(M, K, N):
     X = synthetic.make_x(M, K, "frac", seed=M)
     W = synthetic.make_w(N, K, seed=N)
