@@ -1233,7 +1233,7 @@ __device__ __forceinline__ v4i b_op32(const u32x4 (&b)[wf_large_vec(WF)], int s,
 // are those of step 0 of the next group (tile `lds_next`), left in af0.
 // Weight slot 0 of a column tile holds K steps 0 and 2 (low / high half),
 // slot 1 holds steps 1 and 3.
-template <int TM, int TN, int WF>
+template <int TM, int TN, int WF, bool STAGE>
 __device__ __forceinline__ void large_group(v16i (&acc)[TM][TN], const int8_t* lds, const int8_t* lds_next,
                                             v4i (&af0)[TM], const u32x4 (&b)[TN][wf_large_vec(WF)],
                                             const uint32_t (&m)[TN], uint32_t (&S)[TN], uint32_t (&C)[TN], int g,
@@ -1255,7 +1255,9 @@ __device__ __forceinline__ void large_group(v16i (&acc)[TM][TN], const int8_t* l
     for (int t = 0; t < TN; ++t) {
       const v4i bf = b_op32<WF>(b[t], s, S[t], C[t]);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur[i], bf, acc[i][t], 0, 0, 0);
+      for (int i = 0; i < TM; ++i)
+        acc[i][t] = STAGE ? __builtin_amdgcn_mfma_i32_32x32x32_i8(bf, cur[i], acc[i][t], 0, 0, 0)
+                          : __builtin_amdgcn_mfma_i32_32x32x32_i8(cur[i], bf, acc[i][t], 0, 0, 0);
     }
   }
 }
@@ -1268,8 +1270,9 @@ constexpr size_t large_lds_bytes(int bm) { return size_t(kLargeRing) * size_t(bm
 // of a step in turn (set k multiplies group KI s + k of step s), so each wave
 // can hold a taller tile (fewer dequantizations per MFMA) at the same number
 // of blocks; the sets' INT32 partials are added exactly through LDS at the end.
-template <int WM, int WN, int TM, int TN, int D, int KI, int WF, bool I32OUT>
+template <int WM, int WN, int TM, int TN, int D, int KI, int WF, bool I32OUT, bool STAGE>
 __global__ __launch_bounds__(64 * WM * WN * KI) void gemm_large_kernel(GemmArgs a) {
+  static_assert(!STAGE || !I32OUT, "the staged epilogue writes FP16");
   constexpr int THREADS = 64 * WM * WN * KI;
   constexpr int BM = WM * TM * 32;
   constexpr int BN = WN * TN * 32;
@@ -1420,7 +1423,7 @@ __global__ __launch_bounds__(64 * WM * WN * KI) void gemm_large_kernel(GemmArgs 
     QOQ_COMPILER_FENCE();
     const int l = KI * s + kset;
     if (KI == 1 || l < n)
-      large_group<TM, TN, WF>(acc, slot(l), slot(l + KI), af0, rb[u], rm[u], S, C, gb + l, row0, c32, hh);
+      large_group<TM, TN, WF, STAGE>(acc, slot(l), slot(l + KI), af0, rb[u], rm[u], S, C, gb + l, row0, c32, hh);
     QOQ_COMPILER_FENCE();
     b_ld(rb[u], rm[u], gcl(KI * (s + D) + kset));
     // the tiles of step s+2 were issued one step ago; after them come the
@@ -1472,27 +1475,93 @@ __global__ __launch_bounds__(64 * WM * WN * KI) void gemm_large_kernel(GemmArgs 
             }
     }
   }
-  // Epilogue (set 0): lane holds column lane%32 and rows 8*(r/4) + 4*(lane/32)
-  // + r%4.  Every scale is fetched before the first store: stores count on
-  // the same in-order counter as global loads, so a load issued after a store
-  // waits for it.  The block's row scales go through LDS, past the partials.
-  float sc[TN];
-#pragma unroll
-  for (int t = 0; t < TN; ++t) sc[t] = I32OUT ? 0.0f : col_scale(a, n0 + 32 * t + c32);
-  float* sxs = reinterpret_cast<float*>(smem + (KI > 1 ? (KI - 1) * WM * WN * TM * TN * 4096 : 0));
-  if constexpr (!I32OUT) {
+  if constexpr (STAGE) {
+    // Staged epilogue (set 0; FP16 output rows 16-byte aligned, which the
+    // launch checks).  The weights were the MFMA's first operand, so tile
+    // (i, t) holds the transposed product: lane (c32, hh) holds token row
+    // row0 + 32 i + c32 and, in values 4 q .. 4 q + 3, the four consecutive
+    // columns 32 t + 8 q + 4 hh .. + 3 of the wave's columns.  The FP16
+    // results of 32 rows at a time go through a wave-private LDS tile
+    // (16-byte chunks XOR-swizzled by row, as the activation tiles) and leave
+    // as whole 16-byte row segments: at 64 columns a wave, one store covers 8
+    // rows of full 128-byte lines, against 2 rows of 64 bytes for the 2-byte
+    // stores of the plain epilogue.  Row and column scales go through LDS,
+    // past the partials, before the first store.
+    constexpr int WTN = TN * 32;        // columns of a wave
+    constexpr int CPR = WTN / 8;        // 16-byte chunks per staged row
+    const int nb0 = n0 - wn * TN * 32;  // first column of the block
+    float* sxs = reinterpret_cast<float*>(smem + (KI > 1 ? (KI - 1) * WM * WN * TM * TN * 4096 : 0));
+    float* scs = sxs + BM;
+    int8_t* stg = reinterpret_cast<int8_t*>(scs + BN) + wl * (32 * WTN * 2);
     for (int r = threadIdx.x; r < BM; r += THREADS) sxs[r] = row_scale(a, m0 + r);
+    for (int c = threadIdx.x; c < BN; c += THREADS) scs[c] = col_scale(a, nb0 + c);
     __syncthreads();
-  }
-  if (kset != 0) return;
+    if (kset != 0) return;
+    float4 cs[TN][4];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+    for (int t = 0; t < TN; ++t)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int lr = row0 + i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      const float sxr = I32OUT ? 0.0f : sxs[lr];
+      for (int qq = 0; qq < 4; ++qq) cs[t][qq] = *reinterpret_cast<const float4*>(scs + wn * WTN + 32 * t + 8 * qq + 4 * hh);
 #pragma unroll
-      for (int t = 0; t < TN; ++t) store_out<I32OUT>(a, m0 + lr, n0 + 32 * t + c32, acc[i][t][r], sxr, sc[t]);
+    for (int i = 0; i < TM; ++i) {
+      const float sxr = sxs[row0 + i * 32 + c32];
+      const int sw = (c32 >> 1) & (CPR - 1);
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const float sv[4] = {cs[t][qq].x, cs[t][qq].y, cs[t][qq].z, cs[t][qq].w};
+          unsigned short h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            h[e] = __half_as_ushort(__float2half_rn(static_cast<float>(acc[i][t][4 * qq + e]) * sxr * sv[e]));
+          *reinterpret_cast<uint2*>(stg + c32 * (CPR * 16) + (((4 * t + qq) ^ sw) << 4) + hh * 8) =
+              make_uint2(uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16));
+        }
+      // read back whole chunks (this wave's LDS operations run in order; the
+      // next tile's writes come after these reads)
+#pragma unroll
+      for (int k = 0; k < CPR / 2; ++k) {
+        const int f = k * 64 + lane;
+        const int rr = f / CPR, c = f % CPR;
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + rr * (CPR * 16) + ((c ^ ((rr >> 1) & (CPR - 1))) << 4));
+        const int row = m0 + row0 + i * 32 + rr;
+        const int col = n0 + 8 * c;
+        if (row >= a.M) continue;
+        unsigned short* o = static_cast<unsigned short*>(a.out) + int64_t(row) * a.ldo + col;
+        if (col + 7 < a.N) {
+          *reinterpret_cast<uint4*>(o) = v;
+        } else {  // the row's last, partial chunk
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (col + e < a.N) o[e] = static_cast<unsigned short>(w[e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+  } else {
+    // Epilogue (set 0): lane holds column lane%32 and rows 8*(r/4) + 4*(lane/32)
+    // + r%4.  Every scale is fetched before the first store: stores count on
+    // the same in-order counter as global loads, so a load issued after a store
+    // waits for it.  The block's row scales go through LDS, past the partials.
+    float sc[TN];
+  #pragma unroll
+    for (int t = 0; t < TN; ++t) sc[t] = I32OUT ? 0.0f : col_scale(a, n0 + 32 * t + c32);
+    float* sxs = reinterpret_cast<float*>(smem + (KI > 1 ? (KI - 1) * WM * WN * TM * TN * 4096 : 0));
+    if constexpr (!I32OUT) {
+      for (int r = threadIdx.x; r < BM; r += THREADS) sxs[r] = row_scale(a, m0 + r);
+      __syncthreads();
+    }
+    if (kset != 0) return;
+  #pragma unroll
+    for (int i = 0; i < TM; ++i) {
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lr = row0 + i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const float sxr = I32OUT ? 0.0f : sxs[lr];
+  #pragma unroll
+        for (int t = 0; t < TN; ++t) store_out<I32OUT>(a, m0 + lr, n0 + 32 * t + c32, acc[i][t][r], sxr, sc[t]);
+      }
     }
   }
 }
@@ -1873,11 +1942,25 @@ template <int WM, int WN, int TM, int TN, int D, int KI, int WF, bool I32>
 hipError_t launch_large(const GemmArgs& a, hipStream_t st) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   constexpr size_t lds = large_lds_bytes(BM) * KI;
-  auto* fn = gemm_large_kernel<WM, WN, TM, TN, D, KI, WF, I32>;
+  // the staged FP16 epilogue: the K sets' partials, the block's row and
+  // column scales, then one 32-row tile per wave of a set
+  static_assert(size_t(KI > 1 ? (KI - 1) * WM * WN * TM * TN * 4096 : 0) + size_t(BM + BN) * 4 +
+                        size_t(WM * WN) * 32 * TN * 32 * 2 <= lds,
+                "the staged epilogue fits the ring");
+  // FP16 rows 16-byte aligned: the staged epilogue (whole 16-byte row
+  // segments); otherwise, and for INT32 output, the plain one
+  const bool stage = !I32 && reinterpret_cast<uintptr_t>(a.out) % 16 == 0 && (a.ldo * 2) % 16 == 0;
+  auto* fn = stage ? gemm_large_kernel<WM, WN, TM, TN, D, KI, WF, I32, !I32>
+                   : gemm_large_kernel<WM, WN, TM, TN, D, KI, WF, I32, false>;
   if (lds > 64 * 1024) {
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (attr != hipSuccess) return attr;
+    static const hipError_t attr0 = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(gemm_large_kernel<WM, WN, TM, TN, D, KI, WF, I32, false>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    static const hipError_t attr1 = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(gemm_large_kernel<WM, WN, TM, TN, D, KI, WF, I32, !I32>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (attr0 != hipSuccess) return attr0;
+    if (attr1 != hipSuccess) return attr1;
   }
   const dim3 grid((a.n_strips * 16 + BN - 1) / BN, (a.M + BM - 1) / BM, a.ksplit);
   hipLaunchKernelGGL(fn, grid, dim3(64 * WM * WN * KI), lds, st, a);
