@@ -259,6 +259,25 @@ def test_device_entry_points_validate_before_launch():
     assert lib.qoq_w4a8_gemm_workspace_size(4, 16, 128, 128) == 0
 
 
+@pytest.mark.parametrize("M", [0, -1])
+def test_device_entry_points_reject_row_counts_below_one(M):
+    # M >= 1 is part of every device call's contract; an empty or negative
+    # batch is an unsupported shape (status 2), reported before any launch
+    lib = q.load_library()
+    d = 4096
+    assert lib.qoq_quant_act_per_token(d, M, 128, 128, d, d, None) == 2
+    assert lib.qoq_w4a8_gemm(d, d, d, d, d, d, M, 16, 128, 16, 128, None, 0, None) == 2
+    assert lib.qoq_w4a8_gemm_i32(d, d, d, d, M, 16, 128, 16, 128, None, 0, None) == 2
+    assert lib.qoq_w4a8_gemm_noalloc(d, d, d, d, d, d, M, 16, 128, 16, 128, None) == 2
+    assert lib.qoq_rmsnorm_quant_per_token(d, d, 1e-5, M, 128, 128, d, d, None) == 2
+    assert lib.qoq_w8a8_gemm(d, d, d, d, d, M, 16, 128, 16, None, 0, None) == 2
+    assert lib.qoq_w8a8_gemm_i32(d, d, d, M, 16, 128, 16, None, 0, None) == 2
+    assert lib.qoq_w4a8_gemm_saturating(d, d, d, d, d, d, M, 16, 128, 16, None, 0, None) == 2
+    assert lib.qoq_w4a8_gemm_saturating_i32(d, d, d, d, M, 16, 128, 16, None, 0, None) == 2
+    with pytest.raises(q.QoQError):
+        q.qoq_w4a8_gemm_plan(M, 16, 128)
+
+
 # ------------------------------------------------------------ comparators (f1)
 
 def _documented_w8_blocks(w8, N, K):
