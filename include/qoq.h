@@ -328,7 +328,7 @@ QOQ_API int qoq_scale_columns(const uint16_t* in_fp16, int64_t rows, int64_t K, 
  * per-channel weights: s = fp16((max - min) / 15) (FP32 subtract and divide,
  * round half even), z = clamp(rint(-min / s), 0, 15),
  * q = clamp(rint(x / s) + z, 0, 15); s == 0 gives z = 0 and zero codes.
- * codes: device [n_rows][64]; scale_fp16, zero: device [n_rows].
+ * codes: device [n_rows][64]; scale_fp16, zero: device [n_rows].  n_rows >= 1.
  */
 QOQ_API int qoq_kv4_quant(const void* x_fp16, int64_t n_rows, int32_t head_dim, int64_t ldx, uint8_t* codes,
                   void* scale_fp16, uint8_t* zero, void* stream);
@@ -346,7 +346,8 @@ QOQ_API int qoq_kv4_quant(const void* x_fp16, int64_t n_rows, int32_t head_dim, 
  * softmax and the weighted sum of values are FP32.  L = 0 gives o = 0.
  * q_fp16: device [B][H][128]; the k and v arrays: cache rows
  * [B][Hkv][T_max]; lengths: device int32 [B]; o_fp16: device [B][H][128].
- * 1 <= T_max <= 32768; q and the code arrays 16-byte aligned.  Accuracy:
+ * B, H, Hkv >= 1 with H a multiple of Hkv; 1 <= T_max <= 32768 (other
+ * sizes: QOQ_ERR_UNSUPPORTED_SHAPE); q and the code arrays 16-byte aligned.  Accuracy:
  * each output within one FP16 ulp plus 2^-12 max_t |v_t| of the exact
  * attention over the dequantized cache.
  */

@@ -363,6 +363,11 @@ def test_kv4_entry_points_validate_before_launch():
     assert lib.qoq_kv4_decode_attention(*args, 2, 4, 2, 16, 128, float("nan"), d, None) == 1
     assert lib.qoq_kv4_decode_attention(d + 8, *args[1:], 2, 4, 2, 16, 128, 0.1, d, None) == 3
     assert lib.qoq_kv4_decode_attention(None, *args[1:], 2, 4, 2, 16, 128, 0.1, d, None) == 1
+    # empty or negative sizes: unsupported shapes, and no workspace
+    assert lib.qoq_kv4_quant(d, 0, 128, 128, d, d, d, None) == 2
+    for B, H, Hkv, T in [(0, 4, 2, 16), (-1, 4, 2, 16), (2, 0, 2, 16), (2, 4, 0, 16), (2, 4, 2, 0)]:
+        assert lib.qoq_kv4_decode_attention(*args, B, H, Hkv, T, 128, 0.1, d, None) == 2
+        assert lib.qoq_kv4_decode_attention_workspace_size(B, H, Hkv, T) == 0
     # the token-split entry: same checks, plus its workspace
     assert lib.qoq_kv4_decode_attention_split(*args, 2, 4, 3, 16, 128, 0.1, d, d, 1 << 20, None) == 2
     need = lib.qoq_kv4_decode_attention_workspace_size(1, 32, 8, 4096)
